@@ -1,0 +1,307 @@
+/*
+ * CPU oracle for the LLM.int8() mixed-precision decomposition matmul.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product (the HIP
+ * library) never calls it, links it or shares code with it.
+ *
+ * Plain, slow, single-threaded C.  Each step is the plain definition written
+ * out, in the order the pages give it.  Page titles used in the citations:
+ *   [GENTLE] "A Gentle Introduction to 8-bit Matrix Multiplication for
+ *            transformers at scale" (Chinese translation).
+ *   [HF-INT8] "Hugging Face 将 LLM.int8() 8 位矩阵乘法集成到 Transformers 和
+ *            Accelerate 中".
+ *   [ABSTRACT] "LLM.int8() : Multiplication matricielle a 8 bits pour les
+ *            Transformers a grande echelle".
+ *
+ * Readings taken where the pages leave a step open:
+ *   - outlier test is |x| >= threshold, column-wise over every row of the call
+ *     ([GENTLE] "inside the MatMul": magnitude 6 or greater; "LLM.int8()
+ *     summary": outliers are extracted by column from the hidden states);
+ *   - the activation row scale SCA covers only the non-outlier columns, and
+ *     outlier entries of CA are 0;
+ *   - scale = 127.0f / absmax as one IEEE fp32 division, q = round-half-even
+ *     of (x * scale) as one fp32 multiply, clamped to [-127, 127]
+ *     ([GENTLE] "absmax quantization" worked example);
+ *   - an all-zero vector (absmax 0) quantizes to zeros with scale 0;
+ *   - weights are scaled per output channel (row n of W [N,K]); the recovered
+ *     weight is CB[n,k] * SCB[n] / 127 ([GENTLE] "Usage" printouts);
+ *   - the int8 product is dequantized by SCA[m] * SCB[n] / 127^2 (outer
+ *     product of the two absmax vectors, [GENTLE] "absmax quantization");
+ *   - the outlier product uses the recovered weights; Y = int8 part +
+ *     outlier part + bias.  Y is evaluated in double precision.
+ *
+ * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
+ * (SSE arithmetic on x86-64, so every float operation is one IEEE binary32
+ * operation, round-to-nearest-even).
+ *
+ * Defining ORACLE_MUTANT=n plants one known mistake (n >= 1); the test suite
+ * builds such copies on the CPU to show that its pins catch each mistake.
+ * The normal build defines nothing and contains none of them.
+ */
+#include <fenv.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+#define OK 0
+#define ERR_ARG 1
+#define ERR_NONFINITE 2
+#define ERR_OVERFLOW 3
+
+/* ---- 16-bit -> fp32 widening, exact, by bit manipulation ---------------- */
+
+static float f16_to_f32(uint16_t h) {
+    uint32_t sign = h >> 15, e = (h >> 10) & 0x1f, m = h & 0x3ff;
+    float mag;
+    if (e == 0)
+        mag = ldexpf((float)m, -24);                 /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        mag = m ? NAN : INFINITY;
+    else
+        mag = ldexpf((float)(m | 0x400), (int)e - 25); /* (1024+m) * 2^(e-25) */
+    return sign ? -mag : mag;
+}
+
+static float bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float widen(uint16_t v, int dtype) { return dtype == 0 ? f16_to_f32(v) : bf16_to_f32(v); }
+
+int oracle_widen(const uint16_t* src, int dtype, int64_t n, float* dst) {
+    if ((dtype != 0 && dtype != 1) || n < 0) return ERR_ARG;
+    for (int64_t i = 0; i < n; ++i) dst[i] = widen(src[i], dtype);
+    return OK;
+}
+
+/* ---- absmax quantization of one value ([GENTLE] "absmax quantization") -- */
+
+static float absmax_scale(float absmax) {
+    return 127.0f / absmax; /* one IEEE fp32 division */
+}
+
+static int8_t quantize_value(float x, float scale) {
+    float product = x * scale; /* one fp32 multiply */
+#if ORACLE_MUTANT == 4
+    float r = (product < 0) ? -floorf(-product + 0.5f) : floorf(product + 0.5f); /* half away */
+#else
+    float r = nearbyintf(product); /* round half to even (default mode) */
+#endif
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
+/* ---- weight quantization: per output row n ------------------------------ */
+/* SCB[n] = max_k |W[n,k]|; CB[n,k] = q(W[n,k], 127/SCB[n]).                   */
+/* [GENTLE] "absmax quantization" (vector-wise: absmax per column of B = W^T,  */
+/* i.e. per row of W) and "Usage" (weight.CB int8 [out,in], weight.SCB).       */
+
+int oracle_quantize_weight(const uint16_t* W, int dtype, int64_t N, int64_t K,
+                           int8_t* CB, float* SCB) {
+    if ((dtype != 0 && dtype != 1) || N < 0 || K < 0) return ERR_ARG;
+    if (fegetround() != FE_TONEAREST) return ERR_ARG;
+#if ORACLE_MUTANT == 3
+    /* mistake: one scale per input column instead of per output row */
+    for (int64_t k = 0; k < K; ++k) {
+        float amax = 0.0f;
+        for (int64_t n = 0; n < N; ++n) {
+            float a = fabsf(widen(W[n * K + k], dtype));
+            if (a > amax) amax = a;
+        }
+        for (int64_t n = 0; n < N; ++n)
+            CB[n * K + k] = amax == 0.0f ? 0 : quantize_value(widen(W[n * K + k], dtype), absmax_scale(amax));
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(widen(W[n * K + k], dtype));
+            if (a > amax) amax = a;
+        }
+        SCB[n] = amax;
+    }
+    return OK;
+#endif
+    for (int64_t n = 0; n < N; ++n) {
+        const uint16_t* row = W + n * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float w = widen(row[k], dtype);
+            if (!isfinite(w)) return ERR_NONFINITE;
+            float a = fabsf(w);
+            if (a > amax) amax = a;
+        }
+        SCB[n] = amax;
+        if (amax == 0.0f) {
+            memset(CB + n * K, 0, (size_t)K);
+            continue;
+        }
+        float s = absmax_scale(amax);
+        for (int64_t k = 0; k < K; ++k) CB[n * K + k] = quantize_value(widen(row[k], dtype), s);
+    }
+    return OK;
+}
+
+/* ---- activation quantization -------------------------------------------- */
+/* 1. outlier columns: O = { k : max_m |X[m,k]| >= t }, ascending              */
+/*    ([GENTLE] "LLM.int8() summary" step 1; "inside the MatMul": 6 or more). */
+/* 2. SCA[m] = max over k not in O of |X[m,k]|; CA[m,k] = q(X[m,k],127/SCA[m]) */
+/*    for k not in O, 0 for k in O (row-wise quantization of the hidden       */
+/*    states, [GENTLE] "inside the MatMul"; [HF-INT8] core idea).             */
+/* 3. XO[m,j] = X[m, idx[j]] (the 16-bit outlier part, kept as bit patterns). */
+/* XO has room for M * K values and holds [M, n_out] row-major.               */
+
+int oracle_quantize_act(const uint16_t* X, int dtype, int64_t M, int64_t K, float t,
+                        int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, uint16_t* XO) {
+    if ((dtype != 0 && dtype != 1) || M < 0 || K < 0 || isnan(t) || t < 0.0f) return ERR_ARG;
+    if (fegetround() != FE_TONEAREST) return ERR_ARG;
+    for (int64_t i = 0; i < M * K; ++i)
+        if (!isfinite(widen(X[i], dtype))) return ERR_NONFINITE;
+
+    unsigned char* is_out = (unsigned char*)calloc((size_t)(K > 0 ? K : 1), 1);
+    if (!is_out) return ERR_ARG;
+    int32_t count = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        float colmax = 0.0f;
+        for (int64_t m = 0; m < M; ++m) {
+            float a = fabsf(widen(X[m * K + k], dtype));
+            if (a > colmax) colmax = a;
+        }
+#if ORACLE_MUTANT == 1
+        int outlier = M > 0 && colmax > t; /* mistake: strict comparison */
+#else
+        int outlier = M > 0 && colmax >= t;
+#endif
+        is_out[k] = (unsigned char)outlier;
+        if (outlier) idx[count++] = (int32_t)k;
+    }
+    *n_out = count;
+
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = X + m * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+#if ORACLE_MUTANT == 2
+            /* mistake: the row scale also covers the outlier columns */
+#else
+            if (is_out[k]) continue;
+#endif
+            float a = fabsf(widen(row[k], dtype));
+            if (a > amax) amax = a;
+        }
+        SCA[m] = amax;
+        float s = amax == 0.0f ? 0.0f : absmax_scale(amax);
+        for (int64_t k = 0; k < K; ++k) {
+#if ORACLE_MUTANT == 8
+            int zero = amax == 0.0f; /* mistake: outlier entries not removed */
+#else
+            int zero = is_out[k] || amax == 0.0f;
+#endif
+            CA[m * K + k] = zero ? 0 : quantize_value(widen(row[k], dtype), s);
+        }
+#if ORACLE_MUTANT == 10
+        for (int32_t j = 0; j < count; ++j) XO[m * (int64_t)count + j] = row[j]; /* mistake: index */
+#else
+        for (int32_t j = 0; j < count; ++j) XO[m * (int64_t)count + j] = row[idx[j]];
+#endif
+    }
+    free(is_out);
+    return OK;
+}
+
+/* ---- int8 product of selected rows --------------------------------------- */
+/* C[r,n] = sum_k CA[rows[r],k] * CB[n,k], exact in int64, must fit int32.     */
+/* ([GENTLE] "LLM.int8() summary" step 2, non-outliers multiplied in int8.)   */
+
+int oracle_int8_rows(const int8_t* CA, const int8_t* CB, int64_t M, int64_t N, int64_t K,
+                     const int64_t* rows, int64_t n_rows, int32_t* C) {
+    if (M < 0 || N < 0 || K < 0 || n_rows < 0) return ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t m = rows[r];
+        if (m < 0 || m >= M) return ERR_ARG;
+        const int8_t* a = CA + m * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t* b = CB + n * K;
+            int64_t acc = 0;
+#if ORACLE_MUTANT == 11
+            for (int64_t k = 0; k + 1 < K; ++k) acc += (int64_t)a[k] * (int64_t)b[k]; /* mistake: drops a term */
+#else
+            for (int64_t k = 0; k < K; ++k) acc += (int64_t)a[k] * (int64_t)b[k];
+#endif
+            if (acc > INT32_MAX || acc < INT32_MIN) return ERR_OVERFLOW;
+            C[r * N + n] = (int32_t)acc;
+        }
+    }
+    return OK;
+}
+
+/* ---- recovered weights: CB[n,k] * SCB[n] / 127 ([GENTLE] "Usage") -------- */
+
+static double recovered_weight(const int8_t* CB, const float* SCB, int64_t K, int64_t n, int64_t k) {
+#if ORACLE_MUTANT == 6
+    (void)SCB;
+    return (double)CB[n * K + k]; /* mistake: scale not applied */
+#else
+    return (double)CB[n * K + k] * (double)SCB[n] / 127.0;
+#endif
+}
+
+int oracle_recover_weight(const int8_t* CB, const float* SCB, int64_t N, int64_t K, double* Wdq) {
+    if (N < 0 || K < 0) return ERR_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) Wdq[n * K + k] = recovered_weight(CB, SCB, K, n, k);
+    return OK;
+}
+
+/* ---- the output rows ------------------------------------------------------ */
+/* Y[m,n] = C[m,n] * SCA[m] * SCB[n] / 127^2                (dequantize)       */
+/*        + sum_{j < n_out} X[m, idx[j]] * CB[n,idx[j]] * SCB[n] / 127          */
+/*        + bias[n]                                                            */
+/* ([GENTLE] "LLM.int8() summary" step 3: dequantize the int8 result, add the  */
+/* 16-bit outlier result.)  Evaluated in double; C is the int8 product of the  */
+/* same rows (from oracle_int8_rows).  bias may be NULL.                       */
+
+int oracle_output_rows(const int32_t* C, const float* SCA, const float* SCB,
+                       const uint16_t* X, int dtype, const int32_t* idx, int32_t n_out,
+                       const int8_t* CB, const uint16_t* bias,
+                       int64_t M, int64_t N, int64_t K,
+                       const int64_t* rows, int64_t n_rows, double* Y) {
+    if ((dtype != 0 && dtype != 1) || M < 0 || N < 0 || K < 0 || n_rows < 0 || n_out < 0)
+        return ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t m = rows[r];
+        if (m < 0 || m >= M) return ERR_ARG;
+        for (int64_t n = 0; n < N; ++n) {
+#if ORACLE_MUTANT == 5
+            double y_int8 = (double)C[r * N + n] * (double)SCA[m] * (double)SCB[n] / 127.0;
+#else
+            double y_int8 = (double)C[r * N + n] * (double)SCA[m] * (double)SCB[n] / 16129.0;
+#endif
+            double y_out = 0.0;
+            for (int32_t j = 0; j < n_out; ++j) {
+                int64_t k = idx[j];
+                y_out += (double)widen(X[m * K + k], dtype) * recovered_weight(CB, SCB, K, n, k);
+            }
+#if ORACLE_MUTANT == 7
+            double b = 0.0; /* mistake: bias dropped */
+#else
+            double b = bias ? (double)widen(bias[n], dtype) : 0.0;
+#endif
+#if ORACLE_MUTANT == 9
+            Y[r * N + n] = y_int8 - y_out + b; /* mistake: wrong sign */
+#else
+            Y[r * N + n] = y_int8 + y_out + b;
+#endif
+        }
+    }
+    return OK;
+}
