@@ -1,0 +1,150 @@
+/*
+ * llmint8 -- the LLM.int8() mixed-precision decomposition matmul on AMD
+ * Instinct MI355X (gfx950), as a C-ABI shared library (libllmint8.so).
+ *
+ * Computes Y = X . W^T for a transformer linear layer (X [M,K] tokens x
+ * features, W [N,K] output channels x features) in three parts, following
+ * "A Gentle Introduction to 8-bit Matrix Multiplication for transformers at
+ * scale" (sections "LLM.int8() summary" and "inside the MatMul"):
+ *   1. feature columns of X holding any |x| >= threshold are outliers;
+ *   2. everything else is absmax-quantized to int8 per row of X (SCA) and per
+ *      output channel of W (CB, SCB), multiplied with int32 accumulation and
+ *      dequantized by SCA[m] * SCB[n] / 127^2;
+ *   3. the outlier columns of X are multiplied in 16-bit against the matching
+ *      recovered weights CB[n,k] * SCB[n] / 127 ("Usage" section) and added in,
+ *      with the optional bias, into a 16-bit Y.
+ *
+ * Conventions for every entry point
+ *   - Every pointer is caller-owned DEVICE memory on the current HIP device,
+ *     16-byte aligned.  Nothing is retained after return.  All matrices are
+ *     row-major and densely packed (row stride = number of columns).
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream).
+ *     The library never synchronizes and never copies to the host; the
+ *     outlier count stays in device memory.  Keep buffers alive until the
+ *     stream has passed the call.
+ *   - Arguments are validated before any HIP call.  On an error nothing is
+ *     enqueued.  No C++ exception crosses this interface.
+ *   - Calls are reentrant; calls that share output buffers or a workspace
+ *     must not overlap.
+ *   - dtype is LLMINT8_F16 or LLMINT8_BF16; X, W, bias, X_outlier and Y share it.
+ *     (The pages require fp16 inputs; bf16 follows the same rules with a bf16
+ *     outlier product and a bf16 output.)
+ *   - K must be a positive multiple of 64 and at most LLMINT8_K_MAX, which
+ *     keeps |int32 accumulator| <= K * 127^2 < 2^31.  M and N may be any
+ *     value in [0, 2^31); M == 0 or N == 0 is a valid empty call.
+ */
+#ifndef LLMINT8_H
+#define LLMINT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum llmint8_status {
+    LLMINT8_OK = 0,
+    LLMINT8_ERR_INVALID_ARGUMENT = 1, /* NULL/misaligned pointer, negative size, bad dtype,
+                                         NaN or negative threshold, workspace too small */
+    LLMINT8_ERR_UNSUPPORTED = 2,      /* K not a positive multiple of 64, K > LLMINT8_K_MAX,
+                                         size >= 2^31, device is not gfx950 */
+    LLMINT8_ERR_HIP = 3               /* a HIP call or launch failed; see llmint8_last_hip_error */
+} llmint8_status;
+
+typedef enum llmint8_dtype { LLMINT8_F16 = 0, LLMINT8_BF16 = 1 } llmint8_dtype;
+
+#define LLMINT8_K_ALIGN 64
+#define LLMINT8_K_MAX 133120 /* largest multiple of 64 with K * 127^2 < 2^31 */
+
+/*
+ * Weight quantization, once per weight ("Usage": quantization happens when the
+ * layer is moved to the GPU; vector-wise absmax per output channel, "absmax
+ * quantization").
+ *   W   [N,K] 16-bit, read only.
+ *   CB  [N,K] int8 out: CB[n,k] = rne(W[n,k] * (127 / SCB[n])) in [-127,127]
+ *       (fp32 divide, fp32 multiply, round half to even); 0 when SCB[n] == 0.
+ *   SCB [N] fp32 out: SCB[n] = max_k |W[n,k]|.
+ * The recovered weight is CB[n,k] * SCB[n] / 127.
+ */
+llmint8_status llmint8_quantize_weight(const void* W, int dtype, int64_t N, int64_t K,
+                                       int8_t* CB, float* SCB, hipStream_t stream);
+
+/* Bytes of device workspace llmint8_quantize_act needs for M x K (may be 0). */
+size_t llmint8_quantize_act_workspace_size(int64_t M, int64_t K);
+
+/*
+ * Activation quantization with outlier extraction ("LLM.int8() summary" step 1,
+ * "inside the MatMul": columns holding a magnitude of threshold or more; row-wise
+ * absmax quantization of the hidden states).  The outlier set is taken over all M
+ * rows of this call.
+ *   X           [M,K] 16-bit, read only.  Finite values only.
+ *   threshold   fp32, >= 0; +inf gives no outliers, 0 makes every column one.
+ *   CA          [M,K] int8 out: rne(X[m,k] * (127 / SCA[m])) for non-outlier k,
+ *               0 for outlier k and for rows with SCA[m] == 0.
+ *   SCA         [M] fp32 out: max over non-outlier k of |X[m,k]| (0 if none).
+ *   outlier_idx [K] int32 out: the first n_out entries are the outlier columns in
+ *               ascending order; later entries are unspecified.
+ *   n_outliers  [1] int32 out: n_out.
+ *   X_outlier   capacity M*K 16-bit out: holds XO [M, n_pad] row-major with
+ *               n_pad = round_up(n_out, 32) <= K, XO[m,j] = X[m, idx[j]] for
+ *               j < n_out and 0 for n_out <= j < n_pad.
+ *   workspace   device scratch of llmint8_quantize_act_workspace_size(M,K) bytes
+ *               (may be NULL when that is 0); contents need no initialization.
+ */
+llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t K,
+                                    float threshold, int8_t* CA, float* SCA,
+                                    int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of optional device workspace llmint8_matmul can use for M x N x K. */
+size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The decomposed product ("LLM.int8() summary" steps 2-3):
+ *   Y[m,n] = (C[m,n] * SCA[m] / 127 + sum_{j<n_out} XO[m,j] * CB[n, idx[j]]) * SCB[n] / 127
+ *            + bias[n],
+ *   C[m,n] = sum_k CA[m,k] * CB[n,k]  (exact int32),
+ * which equals C * SCA * SCB / 127^2 + XO . (recovered W[:, idx])^T + bias.
+ * Inputs are the outputs of llmint8_quantize_act (CA, SCA, outlier_idx,
+ * n_outliers, X_outlier) and llmint8_quantize_weight (CB, SCB).
+ *   bias   [N] 16-bit or NULL.
+ *   Y      [M,N] 16-bit out (round to nearest even from fp32).
+ *   C_i32  [M,N] int32 out or NULL: when given, the same kernels also store the
+ *          exact int8 accumulators (for parity checks).
+ *   workspace  optional scratch (NULL / 0 bytes is always valid; a workspace of
+ *          llmint8_matmul_workspace_size bytes lets long-K shapes split K).
+ */
+llmint8_status llmint8_matmul(int dtype, int64_t M, int64_t N, int64_t K,
+                              const int8_t* CA, const float* SCA, const int32_t* outlier_idx,
+                              const int32_t* n_outliers, const void* X_outlier,
+                              const int8_t* CB, const float* SCB, const void* bias,
+                              void* Y, int32_t* C_i32,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Same as llmint8_matmul, for measurement: the HIP events `start` and `stop`
+ * (either may be NULL) are bound to the dispatch of the main int8 GEMM kernel
+ * through hipExtLaunchKernel, so hipEventElapsedTime(start, stop) is that
+ * kernel's own device time.
+ */
+llmint8_status llmint8_matmul_profiled(int dtype, int64_t M, int64_t N, int64_t K,
+                                       const int8_t* CA, const float* SCA,
+                                       const int32_t* outlier_idx, const int32_t* n_outliers,
+                                       const void* X_outlier, const int8_t* CB, const float* SCB,
+                                       const void* bias, void* Y, int32_t* C_i32,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+/* Static English text for a status code. */
+const char* llmint8_status_string(llmint8_status s);
+
+/* The hipError_t behind the calling thread's last LLMINT8_ERR_HIP (0 if none). */
+int llmint8_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLMINT8_H */

@@ -1,0 +1,256 @@
+"""Python binding of libllmint8, the LLM.int8() decomposition matmul for MI355X.
+
+Two layers, both argument marshalling only (every step of the computation runs
+in the library's HIP kernels):
+
+* ``llmint8_quantize_weight``, ``llmint8_quantize_act``, ``llmint8_matmul``,
+  ``llmint8_matmul_profiled`` and the size/status helpers: the C functions of
+  ``include/llmint8.h`` with the same names and arguments (device pointers as
+  Python ints, ``stream`` as a ``hipStream_t`` int).  They raise
+  ``Llmint8Error`` on a non-OK status.
+* ``quantize_weight``, ``quantize_act``, ``matmul`` and ``linear``: the same
+  calls on torch tensors; torch supplies device memory and the current stream.
+
+The library must be built (``python -m int8_quantized_matmul_row_amd.build``);
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libllmint8.so")
+
+F16 = 0
+BF16 = 1
+K_ALIGN = 64
+K_MAX = 133120
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or device", 3: "HIP runtime error"}
+
+EXPORTS = (
+    "llmint8_quantize_weight",
+    "llmint8_quantize_act_workspace_size",
+    "llmint8_quantize_act",
+    "llmint8_matmul_workspace_size",
+    "llmint8_matmul",
+    "llmint8_matmul_profiled",
+    "llmint8_status_string",
+    "llmint8_last_hip_error",
+)
+
+
+class Llmint8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        msg = f"{fn}: {STATUS.get(status, 'unknown status')} (status {status}"
+        msg += f", hipError {hip_error})" if status == 3 else ")"
+        super().__init__(msg)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """Load libllmint8.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise RuntimeError(f"{LIBRARY_PATH} is missing: build it with "
+                           "`python -m int8_quantized_matmul_row_amd.build`")
+    L = ctypes.CDLL(LIBRARY_PATH)
+    L.llmint8_quantize_weight.argtypes = [_P, _INT, _I64, _I64, _P, _P, _P]
+    L.llmint8_quantize_act_workspace_size.argtypes = [_I64, _I64]
+    L.llmint8_quantize_act_workspace_size.restype = ctypes.c_size_t
+    L.llmint8_quantize_act.argtypes = [_P, _INT, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P,
+                                       _P, ctypes.c_size_t, _P]
+    L.llmint8_matmul_workspace_size.argtypes = [_I64, _I64, _I64]
+    L.llmint8_matmul_workspace_size.restype = ctypes.c_size_t
+    mm = [_INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    L.llmint8_matmul.argtypes = mm
+    L.llmint8_matmul_profiled.argtypes = mm + [_P, _P]
+    for f in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
+              "llmint8_matmul_profiled"):
+        getattr(L, f).restype = _INT
+    L.llmint8_status_string.argtypes = [_INT]
+    L.llmint8_status_string.restype = ctypes.c_char_p
+    L.llmint8_last_hip_error.argtypes = []
+    L.llmint8_last_hip_error.restype = _INT
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise Llmint8Error(fn, status, lib().llmint8_last_hip_error() if status == 3 else 0)
+
+
+# ---- the C functions, same names and arguments ----------------------------
+
+def llmint8_quantize_weight(W, dtype, N, K, CB, SCB, stream=0):
+    _check("llmint8_quantize_weight", lib().llmint8_quantize_weight(W, dtype, N, K, CB, SCB, stream))
+
+
+def llmint8_quantize_act_workspace_size(M, K) -> int:
+    return int(lib().llmint8_quantize_act_workspace_size(M, K))
+
+
+def llmint8_quantize_act(X, dtype, M, K, threshold, CA, SCA, outlier_idx, n_outliers, X_outlier,
+                         workspace, workspace_bytes, stream=0):
+    _check("llmint8_quantize_act",
+           lib().llmint8_quantize_act(X, dtype, M, K, ctypes.c_float(threshold), CA, SCA,
+                                      outlier_idx, n_outliers, X_outlier, workspace,
+                                      workspace_bytes, stream))
+
+
+def llmint8_matmul_workspace_size(M, N, K) -> int:
+    return int(lib().llmint8_matmul_workspace_size(M, N, K))
+
+
+def llmint8_matmul(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB, bias,
+                   Y, C_i32, workspace, workspace_bytes, stream=0):
+    _check("llmint8_matmul",
+           lib().llmint8_matmul(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB,
+                                SCB, bias, Y, C_i32, workspace, workspace_bytes, stream))
+
+
+def llmint8_matmul_profiled(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB,
+                            bias, Y, C_i32, workspace, workspace_bytes, stream, start, stop):
+    _check("llmint8_matmul_profiled",
+           lib().llmint8_matmul_profiled(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers,
+                                         X_outlier, CB, SCB, bias, Y, C_i32, workspace,
+                                         workspace_bytes, stream, start, stop))
+
+
+def llmint8_status_string(status: int) -> str:
+    return lib().llmint8_status_string(status).decode()
+
+
+def llmint8_last_hip_error() -> int:
+    return int(lib().llmint8_last_hip_error())
+
+
+# ---- torch tensors -----------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, name, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def quantize_weight(W, stream=None, out=None):
+    """W [N,K] fp16/bf16 -> (CB int8 [N,K], SCB fp32 [N])."""
+    torch = _torch()
+    _need(W, "W")
+    N, K = W.shape
+    CB, SCB = out if out is not None else (
+        torch.empty((N, K), dtype=torch.int8, device=W.device),
+        torch.empty((N,), dtype=torch.float32, device=W.device))
+    llmint8_quantize_weight(_ptr(W), dtype_code(W), N, K, _ptr(CB), _ptr(SCB), _stream(stream))
+    return CB, SCB
+
+
+class QuantizedAct(NamedTuple):
+    CA: object         # int8 [M,K]
+    SCA: object        # fp32 [M]
+    idx: object        # int32 [K]; first n_out valid
+    n_out: object      # int32 [1] (device)
+    XO: object         # 16-bit [M*K]; holds [M, n_pad]
+    dtype: int
+
+
+def alloc_act(M, K, dtype_t, device):
+    torch = _torch()
+    return QuantizedAct(
+        torch.empty((M, K), dtype=torch.int8, device=device),
+        torch.empty((M,), dtype=torch.float32, device=device),
+        torch.empty((K,), dtype=torch.int32, device=device),
+        torch.empty((1,), dtype=torch.int32, device=device),
+        torch.empty((max(M * K, 1),), dtype=dtype_t, device=device),
+        F16 if dtype_t == torch.float16 else BF16)
+
+
+def act_workspace(M, K, device):
+    torch = _torch()
+    n = llmint8_quantize_act_workspace_size(M, K)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+
+
+def quantize_act(X, threshold: float = 6.0, stream=None, out: Optional[QuantizedAct] = None,
+                 workspace=None):
+    """X [M,K] fp16/bf16 -> QuantizedAct (outlier columns over all M rows)."""
+    _need(X, "X")
+    M, K = X.shape
+    q = out if out is not None else alloc_act(M, K, X.dtype, X.device)
+    ws, nbytes = workspace if workspace is not None else act_workspace(M, K, X.device)
+    llmint8_quantize_act(_ptr(X), dtype_code(X), M, K, float(threshold), _ptr(q.CA), _ptr(q.SCA),
+                         _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(ws), nbytes,
+                         _stream(stream))
+    return q
+
+
+def outlier_columns(q: QuantizedAct):
+    """Host copy of the outlier column list (synchronizes)."""
+    n = int(q.n_out.item())
+    return q.idx[:n].cpu()
+
+
+def matmul(q: QuantizedAct, CB, SCB, bias=None, out=None, C_i32=None, stream=None,
+           workspace=None, events=None):
+    """Y [M,N] = dequant(CA CB^T) + outlier part + bias, in X's dtype."""
+    torch = _torch()
+    M, K = q.CA.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K:
+        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
+    dt_t = torch.float16 if q.dtype == F16 else torch.bfloat16
+    Y = out if out is not None else torch.empty((M, N), dtype=dt_t, device=q.CA.device)
+    ws, nbytes = (None, 0) if workspace is None else workspace
+    args = (q.dtype, M, N, K, _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO),
+            _ptr(CB), _ptr(SCB), _ptr(bias), _ptr(Y), _ptr(C_i32), _ptr(ws), nbytes,
+            _stream(stream))
+    if events is None:
+        llmint8_matmul(*args)
+    else:
+        llmint8_matmul_profiled(*args, events[0], events[1])
+    return Y
+
+
+def linear(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None):
+    """Y = X . W^T through LLM.int8(), W given as (CB, SCB)."""
+    q = quantize_act(X, threshold, stream=stream)
+    return matmul(q, CB, SCB, bias=bias, stream=stream)

@@ -1,0 +1,188 @@
+// C-ABI of libllmint8: argument validation, device check and dispatch.
+// The operations and their page citations are documented in include/llmint8.h.
+#include <mutex>
+#include <string.h>
+
+#include "../../include/llmint8.h"
+#include "common.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bad_ptr(const void* p) { return p == nullptr || !aligned16(p); }
+
+llmint8_status check_dtype(int dtype) {
+    return (dtype == LLMINT8_F16 || dtype == LLMINT8_BF16) ? LLMINT8_OK
+                                                             : LLMINT8_ERR_INVALID_ARGUMENT;
+}
+
+// Sizes: negative -> invalid; K must be a positive multiple of 64 <= K_MAX.
+llmint8_status check_sizes(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (M > kMaxDim || N > kMaxDim) return LLMINT8_ERR_UNSUPPORTED;
+    if (K == 0 || K % LLMINT8_K_ALIGN != 0 || K > LLMINT8_K_MAX) return LLMINT8_ERR_UNSUPPORTED;
+    return LLMINT8_OK;
+}
+
+llmint8_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return LLMINT8_ERR_HIP;
+}
+
+// The current device must be gfx950.  Cached per device id.
+std::mutex g_dev_mu;
+signed char g_dev_ok[64];  // 0 unknown, 1 ok, -1 not gfx950
+
+llmint8_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= 64) return LLMINT8_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_ok[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        g_dev_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return g_dev_ok[dev] == 1 ? LLMINT8_OK : LLMINT8_ERR_UNSUPPORTED;
+}
+
+llmint8_status matmul_impl(int dtype, int64_t M, int64_t N, int64_t K, const int8_t* CA,
+                           const float* SCA, const int32_t* outlier_idx,
+                           const int32_t* n_outliers, const void* X_outlier, const int8_t* CB,
+                           const float* SCB, const void* bias, void* Y, int32_t* C_i32,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t ev_start, hipEvent_t ev_stop) {
+    llmint8_status s = check_dtype(dtype);
+    if (s != LLMINT8_OK) return s;
+    if ((s = check_sizes(M, N, K)) != LLMINT8_OK) return s;
+    if (M == 0 || N == 0) return LLMINT8_OK;
+    if (bad_ptr(CA) || bad_ptr(SCA) || bad_ptr(outlier_idx) || bad_ptr(n_outliers) ||
+        bad_ptr(X_outlier) || bad_ptr(CB) || bad_ptr(SCB) || bad_ptr(Y))
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    if ((bias && !aligned16(bias)) || (C_i32 && !aligned16(C_i32)) ||
+        (workspace && !aligned16(workspace)))
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    if ((s = check_device()) != LLMINT8_OK) return s;
+    llmint8::MatmulArgs a;
+    a.bf16 = dtype == LLMINT8_BF16;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.CA = CA;
+    a.SCA = SCA;
+    a.idx = outlier_idx;
+    a.n_out = n_outliers;
+    a.XO = static_cast<const uint16_t*>(X_outlier);
+    a.CB = CB;
+    a.SCB = SCB;
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.Y = static_cast<uint16_t*>(Y);
+    a.C_i32 = C_i32;
+    a.ws = workspace;
+    a.ws_bytes = workspace ? workspace_bytes : 0;
+    hipError_t e = llmint8::launch_matmul(a, stream, ev_start, ev_stop);
+    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+}
+
+}  // namespace
+
+namespace llmint8 {
+
+size_t matmul_workspace(int64_t, int64_t, int64_t) { return 0; }
+
+hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
+    if (a.M <= kSmallM) return launch_gemm_small_m(a, stream, ev_start, ev_stop);
+    return launch_gemm_tiled(a, stream, ev_start, ev_stop);
+}
+
+}  // namespace llmint8
+
+extern "C" {
+
+llmint8_status llmint8_quantize_weight(const void* W, int dtype, int64_t N, int64_t K, int8_t* CB,
+                                       float* SCB, hipStream_t stream) {
+    llmint8_status s = check_dtype(dtype);
+    if (s != LLMINT8_OK) return s;
+    if ((s = check_sizes(0, N, K)) != LLMINT8_OK) return s;
+    if (N == 0) return LLMINT8_OK;
+    if (bad_ptr(W) || bad_ptr(CB) || bad_ptr(SCB)) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if ((s = check_device()) != LLMINT8_OK) return s;
+    hipError_t e = llmint8::launch_quantize_weight(W, dtype == LLMINT8_BF16, (int)N, (int)K, CB,
+                                                   SCB, stream);
+    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+}
+
+size_t llmint8_quantize_act_workspace_size(int64_t M, int64_t K) {
+    if (check_sizes(M, 0, K) != LLMINT8_OK) return 0;
+    return llmint8::quantize_act_workspace(M, K);
+}
+
+llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t K,
+                                    float threshold, int8_t* CA, float* SCA,
+                                    int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    llmint8_status s = check_dtype(dtype);
+    if (s != LLMINT8_OK) return s;
+    if ((s = check_sizes(M, 0, K)) != LLMINT8_OK) return s;
+    if (threshold != threshold || threshold < 0.0f) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (bad_ptr(n_outliers)) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (M > 0) {
+        if (bad_ptr(X) || bad_ptr(CA) || bad_ptr(SCA) || bad_ptr(outlier_idx) || bad_ptr(X_outlier))
+            return LLMINT8_ERR_INVALID_ARGUMENT;
+        const size_t need = llmint8::quantize_act_workspace(M, K);
+        if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+            return LLMINT8_ERR_INVALID_ARGUMENT;
+    }
+    if ((s = check_device()) != LLMINT8_OK) return s;
+    hipError_t e = llmint8::launch_quantize_act(X, dtype == LLMINT8_BF16, (int)M, (int)K, threshold,
+                                                CA, SCA, outlier_idx, n_outliers, X_outlier,
+                                                workspace, stream);
+    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+}
+
+size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (check_sizes(M, N, K) != LLMINT8_OK) return 0;
+    return llmint8::matmul_workspace(M, N, K);
+}
+
+llmint8_status llmint8_matmul(int dtype, int64_t M, int64_t N, int64_t K, const int8_t* CA,
+                              const float* SCA, const int32_t* outlier_idx,
+                              const int32_t* n_outliers, const void* X_outlier, const int8_t* CB,
+                              const float* SCB, const void* bias, void* Y, int32_t* C_i32,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return matmul_impl(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB, bias,
+                       Y, C_i32, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+llmint8_status llmint8_matmul_profiled(int dtype, int64_t M, int64_t N, int64_t K,
+                                       const int8_t* CA, const float* SCA,
+                                       const int32_t* outlier_idx, const int32_t* n_outliers,
+                                       const void* X_outlier, const int8_t* CB, const float* SCB,
+                                       const void* bias, void* Y, int32_t* C_i32,
+                                       void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    return matmul_impl(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB, bias,
+                       Y, C_i32, workspace, workspace_bytes, stream, start, stop);
+}
+
+const char* llmint8_status_string(llmint8_status s) {
+    switch (s) {
+        case LLMINT8_OK: return "ok";
+        case LLMINT8_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LLMINT8_ERR_UNSUPPORTED: return "unsupported shape or device";
+        case LLMINT8_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int llmint8_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+and rejects bad arguments before making any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int8_quantized_matmul_row_amd as pkg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llmint8.h")
+
+OK, INVALID, UNSUPPORTED = 0, 1, 2
+A = 0x10000  # a 16-byte aligned fake address; never dereferenced by these tests
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(llmint8_\w+)\s*\(", text, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pkg.lib()
+    names = declared_functions()
+    assert set(names) == set(pkg.EXPORTS), names
+    for name in names:
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings():
+    for s, text in pkg.STATUS.items():
+        assert pkg.llmint8_status_string(s) == text
+    assert pkg.llmint8_status_string(99) == "unknown status"
+    assert pkg.llmint8_last_hip_error() == 0
+
+
+def qw(W=A, dtype=0, N=8, K=64, CB=A, SCB=A):
+    return pkg.lib().llmint8_quantize_weight(W, dtype, N, K, CB, SCB, None)
+
+
+def test_quantize_weight_validation():
+    assert qw(dtype=2) == INVALID
+    assert qw(N=-1) == INVALID
+    assert qw(K=-64) == INVALID
+    assert qw(K=0) == UNSUPPORTED
+    assert qw(K=100) == UNSUPPORTED
+    assert qw(K=pkg.K_MAX + 64) == UNSUPPORTED
+    assert qw(N=1 << 31) == UNSUPPORTED
+    assert qw(W=None) == INVALID
+    assert qw(CB=None) == INVALID
+    assert qw(SCB=A + 4) == INVALID      # misaligned
+    assert qw(N=0, W=None, CB=None, SCB=None) == OK   # empty: nothing to do
+
+
+def qa(X=A, dtype=0, M=64, K=512, t=6.0, CA=A, SCA=A, idx=A, n=A, XO=A, ws=A, wsb=1 << 30):
+    return pkg.lib().llmint8_quantize_act(X, dtype, M, K, ctypes.c_float(t), CA, SCA, idx, n, XO,
+                                          ws, wsb, None)
+
+
+def test_quantize_act_validation():
+    assert qa(t=float("nan")) == INVALID
+    assert qa(t=-1.0) == INVALID
+    assert qa(dtype=-1) == INVALID
+    assert qa(K=96) == UNSUPPORTED
+    assert qa(M=-1) == INVALID
+    assert qa(n=None) == INVALID
+    assert qa(X=None) == INVALID
+    assert qa(XO=A + 2) == INVALID
+    need = pkg.llmint8_quantize_act_workspace_size(64, 512)
+    assert need > 0
+    assert qa(ws=None) == INVALID
+    assert qa(wsb=need - 1) == INVALID
+
+
+def test_workspace_sizes():
+    assert pkg.llmint8_quantize_act_workspace_size(8, 4096) == 0      # one-launch path
+    assert pkg.llmint8_quantize_act_workspace_size(2048, 4096) > 0
+    assert pkg.llmint8_quantize_act_workspace_size(64, 100) == 0       # unsupported K
+    assert pkg.llmint8_matmul_workspace_size(8, 4096, 4096) >= 0
+
+
+def mm(dtype=0, M=32, N=64, K=128, CA=A, SCA=A, idx=A, n=A, XO=A, CB=A, SCB=A, bias=None, Y=A,
+       C=None, ws=None, wsb=0):
+    return pkg.lib().llmint8_matmul(dtype, M, N, K, CA, SCA, idx, n, XO, CB, SCB, bias, Y, C, ws,
+                                    wsb, None)
+
+
+def test_matmul_validation():
+    assert mm(dtype=3) == INVALID
+    assert mm(K=65) == UNSUPPORTED
+    assert mm(K=0) == UNSUPPORTED
+    assert mm(N=-5) == INVALID
+    for key in ("CA", "SCA", "idx", "n", "XO", "CB", "SCB", "Y"):
+        assert mm(**{key: None}) == INVALID, key
+    assert mm(bias=A + 2) == INVALID
+    assert mm(C=A + 8) == INVALID
+    assert mm(M=0, CA=None, SCA=None, XO=None, Y=None) == OK
+    assert mm(N=0, CB=None, SCB=None, Y=None) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        pkg.quantize_weight(torch.zeros((4, 64), dtype=torch.float16))

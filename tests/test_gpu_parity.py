@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Integer stages (CB, SCB, CA, SCA, the outlier index list and count, XO, the
+int32 accumulators) must match bit for bit; Y must satisfy
+max|dY| <= 1e-2 * max|Y_ref| and, per element, |dY| <= ulp16(|Y_ref|) +
+1e-4 * max|Y_ref| (the 16-bit output rounding plus fp32 evaluation error).
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import compare, log, run_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = synth.F16, synth.BF16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import int8_quantized_matmul_row_amd as pkg
+    pkg.lib()  # fails loudly when the library is missing
+
+
+def full_check(orc, wl, threshold=None, label=None):
+    t = wl.threshold if threshold is None else threshold
+    label = label or f"{wl.name} t={t}"
+    log(f"[parity] {label} M={wl.M} N={wl.N} K={wl.K} dtype={synth.DTYPE_NAMES[wl.dtype]}")
+    g = run_gpu(wl, t)
+    ref = orc.forward(wl.X, wl.W, wl.dtype, t, bias=wl.bias)
+    err, scale = compare(wl, g, ref, label=label)
+    log(f"[parity] {label}: ok, n_out={g['n_out']} max|dY|={err:.3g} max|Y|={scale:.3g}")
+    return g, ref
+
+
+# ---- the two small named workloads, every row ------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_named_workload_full(orc, name):
+    wl = synth.make_workload(name)
+    g, ref = full_check(orc, wl)
+    if name == "tiny":
+        assert list(ref["idx"]) == [7, 500]
+
+
+# ---- ragged shapes over both kernel families -------------------------------
+RAGGED = [
+    # M, N, K, dtype, planted outlier columns, bias
+    (1, 1, 64, F16, 0, False),
+    (3, 17, 128, BF16, 1, True),
+    (8, 4100, 256, F16, 2, True),
+    (16, 33, 192, F16, 2, True),
+    (17, 40, 64, F16, 1, False),
+    (300, 520, 320, F16, 3, True),
+    (300, 520, 320, BF16, 3, True),
+    (513, 257, 1024, F16, 5, False),
+    (257, 769, 448, BF16, 40, True),
+    (40, 64, 57344, BF16, 2, False),
+    (8, 96, 133120, F16, 1, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,dt,nout,bias", RAGGED,
+                         ids=[f"{r[0]}x{r[1]}x{r[2]}-{synth.DTYPE_NAMES[r[3]]}" for r in RAGGED])
+def test_ragged_shapes(orc, M, N, K, dt, nout, bias):
+    wl = synth.make_random(M, N, K, dt, seed=M + N + K, n_outlier_cols=nout,
+                           bias_sigma=0.01 if bias else None)
+    full_check(orc, wl)
+
+
+# ---- degenerate cases the method has ----------------------------------------
+@pytest.mark.parametrize("M,N,K", [(8, 100, 256), (64, 300, 512)])
+def test_threshold_zero_every_column_outlier(orc, M, N, K):
+    wl = synth.make_random(M, N, K, F16, seed=21, n_outlier_cols=2, bias_sigma=0.01)
+    g, ref = full_check(orc, wl, threshold=0.0)
+    assert g["n_out"] == K and not g["CA"].any() and not g["SCA"].any()
+    assert not g["C_dev"].any().item()
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 100, 256), (64, 300, 512)])
+def test_threshold_inf_no_outliers(orc, M, N, K):
+    wl = synth.make_random(M, N, K, BF16, seed=22, n_outlier_cols=3)
+    g, _ = full_check(orc, wl, threshold=float("inf"))
+    assert g["n_out"] == 0
+
+
+@pytest.mark.parametrize("M", [5, 48])
+def test_threshold_boundary_and_zero_rows(orc, M):
+    wl = synth.make_random(M, 70, 128, F16, seed=23)
+    x = synth.bits_to_f32(wl.X, F16)
+    x[:, 9] = 0.5
+    x[M // 2, 9] = 6.0          # exactly the threshold: outlier column
+    x[:, 100] = 0.25
+    x[1, 100] = -5.99609375      # just below: stays int8
+    x[2] = 0.0                   # an all-zero row
+    x[3, :] = 0.0
+    x[3, 9] = 6.0                # a row whose only mass is in an outlier column
+    wl.X = synth.f32_to_f16_bits(x)
+    w = synth.bits_to_f32(wl.W, F16)
+    w[5] = 0.0                   # an all-zero weight row
+    wl.W = synth.f32_to_f16_bits(w)
+    g, ref = full_check(orc, wl, label=f"boundary M={M}")
+    assert 9 in list(ref["idx"]) and 100 not in list(ref["idx"])
+    assert g["SCA"][2] == 0 and g["SCA"][3] == 0 and g["SCB"][5] == 0
+
+
+def test_empty_batch_sets_zero_outliers():
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    dev = torch.device("cuda:0")
+    X = torch.empty((0, 128), dtype=torch.float16, device=dev)
+    q = pkg.alloc_act(0, 128, torch.float16, dev)
+    q.n_out.fill_(-7)
+    pkg.quantize_act(X, 6.0, out=q)
+    W = torch.randn((32, 128), dtype=torch.float16, device=dev)
+    CB, SCB = pkg.quantize_weight(W)
+    Y = pkg.matmul(q, CB, SCB)
+    torch.cuda.synchronize()
+    assert int(q.n_out.item()) == 0 and Y.shape == (0, 32)
+
+
+def test_deterministic_and_bias_applied(orc):
+    import torch
+    wl = synth.make_random(300, 520, 320, F16, seed=31, n_outlier_cols=3, bias_sigma=0.01)
+    a = run_gpu(wl)
+    b = run_gpu(wl, weight=a["weight"])
+    assert np.array_equal(a["Y"], b["Y"])
+    assert torch.equal(a["C_dev"], b["C_dev"])
+    nb = synth.Workload(**{**wl.__dict__, "bias": None})
+    c = run_gpu(nb, weight=a["weight"])
+    diff = synth.bits_to_f32(a["Y"], F16).astype(np.float64) - synth.bits_to_f32(c["Y"], F16)
+    bias = synth.bits_to_f32(wl.bias, F16).astype(np.float64)
+    # Y(bias) - Y(no bias) equals the bias up to two fp16 output roundings
+    assert np.abs(diff - bias[None, :]).max() <= 2 * 2.0 ** -11 * 8
+
+
+# ---- full-size workloads on sampled rows ------------------------------------
+def sampled_check(orc, wl, n_rows, threshold=None, weight_cache=None, label=None):
+    t = wl.threshold if threshold is None else threshold
+    label = label or f"{wl.name} t={t}"
+    log(f"[parity] {label} M={wl.M} N={wl.N} K={wl.K} sampled rows={n_rows}")
+    rows = sample_rows(wl.M, n_rows)
+    if weight_cache is not None and wl.name in weight_cache:
+        (CB_ref, SCB_ref), dev_w = weight_cache[wl.name]
+        g = run_gpu(wl, t, weight=dev_w)
+    else:
+        g = run_gpu(wl, t)
+        CB_ref, SCB_ref = orc.quantize_weight(wl.W, wl.dtype)
+        assert np.array_equal(g["CB"], CB_ref), f"{label}: CB"
+        assert np.array_equal(g["SCB"], SCB_ref), f"{label}: SCB"
+        if weight_cache is not None:
+            weight_cache[wl.name] = ((CB_ref, SCB_ref), g["weight"])
+    ref = orc.forward(wl.X, None, wl.dtype, t, bias=wl.bias, rows=rows,
+                      weight=(CB_ref, SCB_ref))
+    err, scale = compare(wl, g, ref, rows=rows, label=label)
+    log(f"[parity] {label}: ok, n_out={g['n_out']} max|dY|={err:.3g} max|Y|={scale:.3g}")
+    return g
+
+
+def test_prefill_full_size(orc):
+    wl = synth.make_workload("prefill")
+    sampled_check(orc, wl, 32)
+
+
+@pytest.fixture(scope="module")
+def sweep_weight():
+    return {}
+
+
+@pytest.mark.parametrize("name", ["sweep_0", "sweep_0.1", "sweep_1", "sweep_5"])
+def test_sweep_full_size(orc, name, sweep_weight):
+    wl = synth.make_workload(name, with_weight=not sweep_weight)
+    wl.name = "sweep"  # one weight for the four densities
+    sampled_check(orc, wl, 12, weight_cache=sweep_weight, label=name)
+
+
+@pytest.mark.parametrize("t", [float("inf"), 0.0])
+def test_sweep_threshold_extremes_full_size(orc, t, sweep_weight):
+    wl = synth.make_workload("sweep_0.1", with_weight=not sweep_weight)
+    wl.name = "sweep"
+    g = sampled_check(orc, wl, 8 if t == 0.0 else 12, threshold=t, weight_cache=sweep_weight,
+                      label=f"sweep_0.1 t={t}")
+    assert g["n_out"] == (0 if t != 0.0 else wl.K)
+
+
+@pytest.mark.parametrize("name", ["bloom_up", "bloom_down"])
+def test_bloom_ffn_full_size(orc, name):
+    wl = synth.make_workload(name)
+    sampled_check(orc, wl, 6)
