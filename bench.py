@@ -1,0 +1,297 @@
+"""Benchmark of the LLM.int8() decomposition matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|prefill|...]
+
+A step is one forward of the layer on resident inputs: llmint8_quantize_act
+(outlier columns, row scales, int8 activations) + llmint8_matmul (int8 MFMA
+product, dequantize, 16-bit outlier product, bias).  Weight quantization runs
+once per weight, at load time, and is reported separately.
+
+Prints one JSON line.  value = effective TOPS = 2*M*N*K / step time.  The
+dominant kernel (the matmul) is also timed on its own with HIP events bound to
+its dispatch, and placed against its roofline: HBM bandwidth for small-M
+(decode) shapes, int8 MFMA throughput otherwise.  Distinct copies of the int8
+weight are rotated, more than 512 MiB in total, so each step streams its weight
+from HBM rather than from the 256 MiB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LLM.int8 matmul effective TOPS (2MNK/s) + % of int8-MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+ROTATE_BYTES = 512 << 20     # > 2x the Infinity Cache
+KERNEL_SOURCES = {
+    "small_m": ["int8_quantized_matmul_row_amd/csrc/gemm_small_m.hip",
+                "int8_quantized_matmul_row_amd/csrc/common.h"],
+    "tiled": ["int8_quantized_matmul_row_amd/csrc/gemm_tiled.hip",
+              "int8_quantized_matmul_row_amd/csrc/common.h"],
+}
+
+
+def kernel_family(M):
+    return "small_m" if M <= 16 else "tiled"
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_matmul_bytes(M, N, K, n_out, has_bias):
+    """Bytes the matmul kernel must move: CB, SCB, CA, SCA, the 16-bit outlier
+    activations (n_pad columns) and their index list, bias, and Y."""
+    n_pad = (n_out + 31) // 32 * 32
+    return (N * K + 4 * N + M * K + 4 * M + 2 * M * n_pad + 4 * n_out
+            + (2 * N if has_bias else 0) + 2 * M * N)
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark makes itself (events)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+
+def load_traffic(config, family):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_hash(KERNEL_SOURCES[family]):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The CPU oracle (single-threaded C) on a bounded sample of the same step."""
+    import numpy as np
+    import oracle
+    orc = oracle.get()
+    CB, SCB = orc.quantize_weight(wl.W, wl.dtype)
+    M = wl.M
+    if M * wl.N * wl.K <= (1 << 28):
+        # whole forward, repeated
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            orc.forward(wl.X, None, wl.dtype, wl.threshold, bias=wl.bias, weight=(CB, SCB))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+        step_s = el / reps
+        sample = f"full {M}x{wl.N}x{wl.K} forward (quantize_act + matmul), {reps} repetitions"
+    else:
+        t0 = time.perf_counter()
+        CA, SCA, idx, XO = orc.quantize_act(wl.X, wl.dtype, wl.threshold)
+        t_act = time.perf_counter() - t0
+        per_row = 2 * wl.N * wl.K
+        n_rows = max(2, min(M, int(budget_s * 1.0e9 / per_row)))  # ~1 GOP/s single core
+        rows = np.linspace(0, M - 1, n_rows).astype(np.int64)
+        t0 = time.perf_counter()
+        C = orc.int8_rows(CA, CB, rows)
+        orc.output_rows(C, SCA, SCB, wl.X, wl.dtype, idx, CB, wl.bias, rows)
+        t_rows = time.perf_counter() - t0
+        step_s = t_act + t_rows * M / n_rows
+        sample = (f"quantize_act on all {M} rows + matmul on {n_rows} evenly spaced rows, "
+                  f"extrapolated to {M} rows")
+    return {"value": round(2 * M * wl.N * wl.K / step_s / 1e12, 6), "unit": "TOPS", "cores": 1,
+            "kind": "oracle", "sample": sample, "ms_per_step": round(step_s * 1e3, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode")
+    ap.add_argument("--threshold", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    wl = synth.make_workload(args.config)
+    if args.threshold is not None:
+        wl.threshold = args.threshold
+    M, N, K = wl.M, wl.N, wl.K
+    dt_t = torch.float16 if wl.dtype == synth.F16 else torch.bfloat16
+
+    def dev16(bits):
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(dt_t)
+
+    X = dev16(wl.X)
+    W = dev16(wl.W)
+    bias = None if wl.bias is None else dev16(wl.bias)
+
+    # ---- one-time weight quantization (S1), timed on its own ---------------
+    CB0 = torch.empty((N, K), dtype=torch.int8, device=dev)
+    SCB0 = torch.empty((N,), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        pkg.quantize_weight(W, out=(CB0, SCB0))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        pkg.quantize_weight(W, out=(CB0, SCB0))
+    e1.record()
+    torch.cuda.synchronize()
+    wq_ms = e0.elapsed_time(e1) / reps
+    wq_bytes = 2 * N * K + N * K + 4 * N
+    del W
+
+    # ---- resident buffers: rotated weight copies, activations, outputs -------
+    n_copies = max(1, -(-ROTATE_BYTES // (N * K)))
+    weights = [(CB0, SCB0)] + [(CB0.clone(), SCB0.clone()) for _ in range(n_copies - 1)]
+    q = pkg.alloc_act(M, K, dt_t, dev)
+    ws = pkg.act_workspace(M, K, dev)
+    Y = torch.empty((M, N), dtype=dt_t, device=dev)
+    stream = torch.cuda.Stream()
+    s_ptr = stream.cuda_stream
+
+    def step(i, ev=None):
+        CB, SCB = weights[i % n_copies]
+        pkg.llmint8_quantize_act(X.data_ptr(), wl.dtype, M, K, wl.threshold, q.CA.data_ptr(),
+                                 q.SCA.data_ptr(), q.idx.data_ptr(), q.n_out.data_ptr(),
+                                 q.XO.data_ptr(), ws[0].data_ptr(), ws[1], s_ptr)
+        a = (wl.dtype, M, N, K, q.CA.data_ptr(), q.SCA.data_ptr(), q.idx.data_ptr(),
+             q.n_out.data_ptr(), q.XO.data_ptr(), CB.data_ptr(), SCB.data_ptr(),
+             None if bias is None else bias.data_ptr(), Y.data_ptr(), None, None, 0, s_ptr)
+        if ev is None:
+            pkg.llmint8_matmul(*a)
+        else:
+            pkg.llmint8_matmul_profiled(*a, ev[0], ev[1])
+
+    # ---- warmup ---------------------------------------------------------------
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+    n_out = int(q.n_out.item())
+
+    # One graph holds one pass over the weight copies; the timed region replays
+    # it (a decode step is a few microseconds of GPU work, far below the cost of
+    # launching it from Python).
+    per_graph = n_copies
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(per_graph):
+                step(i)
+    reps_graph = max(1, -(-args.steps // per_graph))
+    steps = reps_graph * per_graph if graph is not None else args.steps
+
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph is not None:
+        for _ in range(2):
+            graph.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g0.record(stream)
+        if graph is not None:
+            for _ in range(reps_graph):
+                graph.replay()
+        else:
+            for i in range(steps):
+                step(i)
+        g1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = g0.elapsed_time(g1)
+
+    # The dominant kernel's own duration: the same steps again, each matmul
+    # launched with a HIP event pair bound to its dispatch on this stream.
+    n_kt = min(steps, 512)
+    evs = [(hip.event(), hip.event()) for _ in range(n_kt)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(n_kt):
+            step(i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = [hip.elapsed_ms(a, b) for a, b in evs]
+
+    ms_per_step = total_ms / steps
+    tops = 2.0 * M * N * K / (ms_per_step * 1e-3) / 1e12
+    k_ms = float(np.mean(kern_ms))
+    fam = kernel_family(M)
+    alg_bytes = algorithmic_matmul_bytes(M, N, K, n_out, bias is not None)
+    if fam == "small_m":
+        achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = 2.0 * M * N * K / (k_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
+    roof["traffic"] = load_traffic(args.config, fam)
+    roof["kernel"] = "gemm_small_m_kernel" if fam == "small_m" else "gemm_tiled_kernel"
+    roof["kernel_ms"] = round(k_ms, 5)
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["ops"] = 2 * M * N * K
+
+    result = {
+        "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: X {synth.DTYPE_NAMES[wl.dtype]} [{M}x{K}], "
+                               f"W [{N}x{K}], threshold {wl.threshold}, {n_out} outlier columns"
+                               + (", bias" if bias is not None else ""),
+                   "M": M, "N": N, "K": K, "io_dtype": synth.DTYPE_NAMES[wl.dtype],
+                   "outlier_cols": n_out, "threshold": wl.threshold,
+                   "weight_copies_rotated": n_copies, "graph": graph is not None},
+        "roofline": roof,
+        "weight_quant_once": {"ms": round(wq_ms, 4), "GB/s": round(wq_bytes / wq_ms / 1e6, 1),
+                              "frac_hbm": round(wq_bytes / wq_ms / 1e6 / HBM_PEAK_GBS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
