@@ -2,9 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|prefill|...]
 
-A step is one forward of the layer on resident inputs: llmint8_quantize_act
-(outlier columns, row scales, int8 activations) + llmint8_matmul (int8 MFMA
-product, dequantize, 16-bit outlier product, bias).  Weight quantization runs
+A step is one forward of the layer on resident inputs through llmint8_linear:
+outlier columns, row scales and int8 activations (llmint8_quantize_act's
+results), then the int8 MFMA product, dequantization, 16-bit outlier product
+and bias (llmint8_matmul's).  For a handful of tokens this is one fused kernel;
+otherwise the activation kernels then the tiled GEMM.  Weight quantization runs
 once per weight, at load time, and is reported separately.
 
 Prints one JSON line.  value = effective TOPS = 2*M*N*K / step time.  The
@@ -32,6 +34,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 ROTATE_BYTES = 512 << 20     # > 2x the Infinity Cache
 KERNEL_SOURCES = {
+    "fused": ["int8_quantized_matmul_row_amd/csrc/linear_small_m.hip",
+              "int8_quantized_matmul_row_amd/csrc/common.h"],
     "small_m": ["int8_quantized_matmul_row_amd/csrc/gemm_small_m.hip",
                 "int8_quantized_matmul_row_amd/csrc/common.h"],
     "tiled": ["int8_quantized_matmul_row_amd/csrc/gemm_tiled.hip",
@@ -39,7 +43,14 @@ KERNEL_SOURCES = {
 }
 
 
-def kernel_family(M):
+KERNEL_NAMES = {"fused": "linear_small_m_kernel", "small_m": "gemm_small_m_kernel",
+                "tiled": "gemm_tiled_kernel"}
+
+
+def kernel_family(M, K):
+    """The kernel that carries the product in llmint8_linear for this shape."""
+    if 1 <= M <= 16 and M * K <= 65536 and K <= 8192:
+        return "fused"
     return "small_m" if M <= 16 else "tiled"
 
 
@@ -51,12 +62,17 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def algorithmic_matmul_bytes(M, N, K, n_out, has_bias):
-    """Bytes the matmul kernel must move: CB, SCB, CA, SCA, the 16-bit outlier
-    activations (n_pad columns) and their index list, bias, and Y."""
+def algorithmic_bytes(family, M, N, K, n_out, has_bias):
+    """Bytes the kernel must move.  GEMM kernels: CB, SCB, CA, SCA, the 16-bit
+    outlier activations (n_pad columns) and their index list, bias, Y.  The fused
+    kernel reads X instead of CA, and also writes the activation outputs (CA,
+    SCA, index list, count, XO)."""
     n_pad = (n_out + 31) // 32 * 32
-    return (N * K + 4 * N + M * K + 4 * M + 2 * M * n_pad + 4 * n_out
-            + (2 * N if has_bias else 0) + 2 * M * N)
+    common = N * K + 4 * N + (2 * N if has_bias else 0) + 2 * M * N
+    act_out = M * K + 4 * M + 2 * M * n_pad + 4 * n_out
+    if family == "fused":
+        return common + 2 * M * K + act_out + 4
+    return common + act_out
 
 
 class Hip:
@@ -188,23 +204,21 @@ def main():
     n_copies = max(1, -(-ROTATE_BYTES // (N * K)))
     weights = [(CB0, SCB0)] + [(CB0.clone(), SCB0.clone()) for _ in range(n_copies - 1)]
     q = pkg.alloc_act(M, K, dt_t, dev)
-    ws = pkg.act_workspace(M, K, dev)
+    ws = pkg.linear_workspace(M, N, K, dev)
     Y = torch.empty((M, N), dtype=dt_t, device=dev)
     stream = torch.cuda.Stream()
     s_ptr = stream.cuda_stream
 
     def step(i, ev=None):
         CB, SCB = weights[i % n_copies]
-        pkg.llmint8_quantize_act(X.data_ptr(), wl.dtype, M, K, wl.threshold, q.CA.data_ptr(),
-                                 q.SCA.data_ptr(), q.idx.data_ptr(), q.n_out.data_ptr(),
-                                 q.XO.data_ptr(), ws[0].data_ptr(), ws[1], s_ptr)
-        a = (wl.dtype, M, N, K, q.CA.data_ptr(), q.SCA.data_ptr(), q.idx.data_ptr(),
-             q.n_out.data_ptr(), q.XO.data_ptr(), CB.data_ptr(), SCB.data_ptr(),
-             None if bias is None else bias.data_ptr(), Y.data_ptr(), None, None, 0, s_ptr)
+        a = (X.data_ptr(), wl.dtype, M, N, K, wl.threshold, CB.data_ptr(), SCB.data_ptr(),
+             None if bias is None else bias.data_ptr(), Y.data_ptr(), q.CA.data_ptr(),
+             q.SCA.data_ptr(), q.idx.data_ptr(), q.n_out.data_ptr(), q.XO.data_ptr(), None,
+             ws[0].data_ptr(), ws[1], s_ptr)
         if ev is None:
-            pkg.llmint8_matmul(*a)
+            pkg.llmint8_linear(*a)
         else:
-            pkg.llmint8_matmul_profiled(*a, ev[0], ev[1])
+            pkg.llmint8_linear_profiled(*a, ev[0], ev[1])
 
     # ---- warmup ---------------------------------------------------------------
     with torch.cuda.stream(stream):
@@ -257,9 +271,9 @@ def main():
     ms_per_step = total_ms / steps
     tops = 2.0 * M * N * K / (ms_per_step * 1e-3) / 1e12
     k_ms = float(np.mean(kern_ms))
-    fam = kernel_family(M)
-    alg_bytes = algorithmic_matmul_bytes(M, N, K, n_out, bias is not None)
-    if fam == "small_m":
+    fam = kernel_family(M, K)
+    alg_bytes = algorithmic_bytes(fam, M, N, K, n_out, bias is not None)
+    if fam != "tiled":
         achieved = alg_bytes / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
@@ -268,7 +282,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
     roof["traffic"] = load_traffic(args.config, fam)
-    roof["kernel"] = "gemm_small_m_kernel" if fam == "small_m" else "gemm_tiled_kernel"
+    roof["kernel"] = KERNEL_NAMES[fam]
     roof["kernel_ms"] = round(k_ms, 5)
     roof["algorithmic_bytes"] = alg_bytes
     roof["ops"] = 2 * M * N * K

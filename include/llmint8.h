@@ -137,6 +137,36 @@ llmint8_status llmint8_matmul_profiled(int dtype, int64_t M, int64_t N, int64_t 
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+/* Bytes of device workspace llmint8_linear needs for M x N x K (may be 0). */
+size_t llmint8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
+ * The whole forward of an LLM.int8() linear layer in one call: the results of
+ * llmint8_quantize_act followed by llmint8_matmul (the layer's forward in the
+ * "Usage" section: int8 weights placed once, 16-bit activations in, 16-bit
+ * output).  Arguments have the meanings given above; CA, SCA, outlier_idx,
+ * n_outliers and X_outlier are filled exactly as llmint8_quantize_act fills
+ * them.  C_i32 may be NULL.  For M <= 16 with M*K <= 65536 the forward is one
+ * fused kernel (each workgroup re-derives the tiny activation quantization
+ * while its weight slab streams in); otherwise it is the quantize_act launches
+ * followed by the matmul kernel.  workspace: llmint8_linear_workspace_size bytes.
+ */
+llmint8_status llmint8_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                              float threshold, const int8_t* CB, const float* SCB,
+                              const void* bias, void* Y, int8_t* CA, float* SCA,
+                              int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                              int32_t* C_i32, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* llmint8_linear with `start`/`stop` bound to the dispatch of its int8 GEMM
+ * kernel (the fused kernel when M is small), as in llmint8_matmul_profiled. */
+llmint8_status llmint8_linear_profiled(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                                       float threshold, const int8_t* CB, const float* SCB,
+                                       const void* bias, void* Y, int8_t* CA, float* SCA,
+                                       int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                       int32_t* C_i32, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 /* Static English text for a status code. */
 const char* llmint8_status_string(llmint8_status s);
 

@@ -37,6 +37,9 @@ EXPORTS = (
     "llmint8_matmul_workspace_size",
     "llmint8_matmul",
     "llmint8_matmul_profiled",
+    "llmint8_linear_workspace_size",
+    "llmint8_linear",
+    "llmint8_linear_profiled",
     "llmint8_status_string",
     "llmint8_last_hip_error",
 )
@@ -76,8 +79,14 @@ def lib() -> ctypes.CDLL:
     mm = [_INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
     L.llmint8_matmul.argtypes = mm
     L.llmint8_matmul_profiled.argtypes = mm + [_P, _P]
+    L.llmint8_linear_workspace_size.argtypes = [_I64, _I64, _I64]
+    L.llmint8_linear_workspace_size.restype = ctypes.c_size_t
+    lin = [_P, _INT, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+           ctypes.c_size_t, _P]
+    L.llmint8_linear.argtypes = lin
+    L.llmint8_linear_profiled.argtypes = lin + [_P, _P]
     for f in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
-              "llmint8_matmul_profiled"):
+              "llmint8_matmul_profiled", "llmint8_linear", "llmint8_linear_profiled"):
         getattr(L, f).restype = _INT
     L.llmint8_status_string.argtypes = [_INT]
     L.llmint8_status_string.restype = ctypes.c_char_p
@@ -127,6 +136,27 @@ def llmint8_matmul_profiled(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_
            lib().llmint8_matmul_profiled(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers,
                                          X_outlier, CB, SCB, bias, Y, C_i32, workspace,
                                          workspace_bytes, stream, start, stop))
+
+
+def llmint8_linear_workspace_size(M, N, K) -> int:
+    return int(lib().llmint8_linear_workspace_size(M, N, K))
+
+
+def llmint8_linear(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                   n_outliers, X_outlier, C_i32, workspace, workspace_bytes, stream=0):
+    _check("llmint8_linear",
+           lib().llmint8_linear(X, dtype, M, N, K, ctypes.c_float(threshold), CB, SCB, bias, Y, CA,
+                                SCA, outlier_idx, n_outliers, X_outlier, C_i32, workspace,
+                                workspace_bytes, stream))
+
+
+def llmint8_linear_profiled(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                            n_outliers, X_outlier, C_i32, workspace, workspace_bytes, stream,
+                            start, stop):
+    _check("llmint8_linear_profiled",
+           lib().llmint8_linear_profiled(X, dtype, M, N, K, ctypes.c_float(threshold), CB, SCB,
+                                         bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,
+                                         C_i32, workspace, workspace_bytes, stream, start, stop))
 
 
 def llmint8_status_string(status: int) -> str:
@@ -250,7 +280,32 @@ def matmul(q: QuantizedAct, CB, SCB, bias=None, out=None, C_i32=None, stream=Non
     return Y
 
 
-def linear(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None):
-    """Y = X . W^T through LLM.int8(), W given as (CB, SCB)."""
-    q = quantize_act(X, threshold, stream=stream)
-    return matmul(q, CB, SCB, bias=bias, stream=stream)
+def linear_workspace(M, N, K, device):
+    torch = _torch()
+    n = llmint8_linear_workspace_size(M, N, K)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+
+
+def linear(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None, out=None,
+           act: Optional[QuantizedAct] = None, C_i32=None, workspace=None, events=None):
+    """Y = X . W^T through LLM.int8() in one call, W given as (CB, SCB).
+
+    Returns (Y, QuantizedAct): the activation outputs are filled as by
+    quantize_act."""
+    torch = _torch()
+    _need(X, "X")
+    M, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K:
+        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
+    q = act if act is not None else alloc_act(M, K, X.dtype, X.device)
+    Y = out if out is not None else torch.empty((M, N), dtype=X.dtype, device=X.device)
+    ws, nbytes = workspace if workspace is not None else linear_workspace(M, N, K, X.device)
+    args = (_ptr(X), dtype_code(X), M, N, K, float(threshold), _ptr(CB), _ptr(SCB), _ptr(bias),
+            _ptr(Y), _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(C_i32),
+            _ptr(ws), nbytes, _stream(stream))
+    if events is None:
+        llmint8_linear(*args)
+    else:
+        llmint8_linear_profiled(*args, events[0], events[1])
+    return Y, q

@@ -91,6 +91,71 @@ llmint8_status matmul_impl(int dtype, int64_t M, int64_t N, int64_t K, const int
     return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
+    if (M == 0 || N == 0) return llmint8::quantize_act_workspace(M, K);
+    if (llmint8::linear_small_m_supported((int)M, (int)K)) return 0;
+    return align256(llmint8::quantize_act_workspace(M, K)) + llmint8::matmul_workspace(M, N, K);
+}
+
+llmint8_status linear_impl(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                           float threshold, const int8_t* CB, const float* SCB, const void* bias,
+                           void* Y, int8_t* CA, float* SCA, int32_t* outlier_idx,
+                           int32_t* n_outliers, void* X_outlier, int32_t* C_i32, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start,
+                           hipEvent_t ev_stop) {
+    llmint8_status s = check_dtype(dtype);
+    if (s != LLMINT8_OK) return s;
+    if ((s = check_sizes(M, N, K)) != LLMINT8_OK) return s;
+    if (threshold != threshold || threshold < 0.0f) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (bad_ptr(n_outliers)) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (M > 0 && (bad_ptr(X) || bad_ptr(CA) || bad_ptr(SCA) || bad_ptr(outlier_idx) ||
+                  bad_ptr(X_outlier)))
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (M > 0 && N > 0 && (bad_ptr(CB) || bad_ptr(SCB) || bad_ptr(Y)))
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    if ((bias && !aligned16(bias)) || (C_i32 && !aligned16(C_i32)) ||
+        (workspace && !aligned16(workspace)))
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    const size_t need = linear_workspace(M, N, K);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    if ((s = check_device()) != LLMINT8_OK) return s;
+    const bool bf16 = dtype == LLMINT8_BF16;
+    hipError_t e;
+    if (M > 0 && N > 0 && llmint8::linear_small_m_supported((int)M, (int)K)) {
+        e = llmint8::launch_linear_small_m(X, bf16, (int)M, (int)N, (int)K, threshold, CB, SCB,
+                                           bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,
+                                           C_i32, stream, ev_start, ev_stop);
+        return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+    }
+    e = llmint8::launch_quantize_act(X, bf16, (int)M, (int)K, threshold, CA, SCA, outlier_idx,
+                                     n_outliers, X_outlier, workspace, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (M == 0 || N == 0) return LLMINT8_OK;
+    llmint8::MatmulArgs a;
+    a.bf16 = bf16;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.CA = CA;
+    a.SCA = SCA;
+    a.idx = outlier_idx;
+    a.n_out = n_outliers;
+    a.XO = static_cast<const uint16_t*>(X_outlier);
+    a.CB = CB;
+    a.SCB = SCB;
+    a.bias = static_cast<const uint16_t*>(bias);
+    a.Y = static_cast<uint16_t*>(Y);
+    a.C_i32 = C_i32;
+    const size_t act_ws = align256(llmint8::quantize_act_workspace(M, K));
+    a.ws = workspace && workspace_bytes > act_ws ? static_cast<char*>(workspace) + act_ws : nullptr;
+    a.ws_bytes = a.ws ? workspace_bytes - act_ws : 0;
+    e = llmint8::launch_matmul(a, stream, ev_start, ev_stop);
+    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+}
+
 }  // namespace
 
 namespace llmint8 {
@@ -171,6 +236,33 @@ llmint8_status llmint8_matmul_profiled(int dtype, int64_t M, int64_t N, int64_t 
                                        hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     return matmul_impl(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB, bias,
                        Y, C_i32, workspace, workspace_bytes, stream, start, stop);
+}
+
+size_t llmint8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (check_sizes(M, N, K) != LLMINT8_OK) return 0;
+    return linear_workspace(M, N, K);
+}
+
+llmint8_status llmint8_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                              float threshold, const int8_t* CB, const float* SCB,
+                              const void* bias, void* Y, int8_t* CA, float* SCA,
+                              int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                              int32_t* C_i32, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+    return linear_impl(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                       n_outliers, X_outlier, C_i32, workspace, workspace_bytes, stream, nullptr,
+                       nullptr);
+}
+
+llmint8_status llmint8_linear_profiled(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                                       float threshold, const int8_t* CB, const float* SCB,
+                                       const void* bias, void* Y, int8_t* CA, float* SCA,
+                                       int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                       int32_t* C_i32, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    return linear_impl(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                       n_outliers, X_outlier, C_i32, workspace, workspace_bytes, stream, start,
+                       stop);
 }
 
 const char* llmint8_status_string(llmint8_status s) {

@@ -39,10 +39,52 @@ __device__ __forceinline__ uint16_t narrow16(float f) {
     }
 }
 
+// ---- magnitudes as 16-bit patterns ----------------------------------------
+// For finite fp16/bf16 values, |x| (sign bit cleared) orders like the bit
+// pattern read as an unsigned integer, so maxima and threshold tests can run on
+// packed u16 pairs and give exactly the fp32 results.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t abs2(uint32_t v) { return v & 0x7fff7fffu; }
+
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+
+// Smallest finite-or-infinite 16-bit magnitude pattern h with value(h) >= t, so
+// that for finite x:  |x| >= t  <=>  bits(|x|) >= threshold_bits(t).
+template <bool BF16>
+__device__ __forceinline__ uint32_t threshold_bits(float t) {
+    if (!(t > 0.0f)) return 0u;  // t == 0: every value qualifies
+    if constexpr (BF16) {
+        if (t == __builtin_inff()) return 0x7F80u;
+        uint32_t h = __builtin_bit_cast(uint32_t, t) >> 16;  // truncation toward zero
+        if (widen16<true>((uint16_t)h) < t) h += 1;
+        return h;
+    } else {
+        if (t > 65504.0f) return 0x7C00u;  // above the largest finite fp16
+        uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)t);
+        if (widen16<false>((uint16_t)h) < t) h += 1;
+        return h;
+    }
+}
+
 // ---- absmax quantization of one value ------------------------------------
 // scale = 127.0f / absmax is computed once per vector with the correctly
 // rounded fp32 divide; q = rne(x * scale) with one fp32 multiply and
 // v_rndne_f32, clamped to [-127, 127].
+// The int8 code of rne(x * scale) as the low byte of a 32-bit pattern, for
+// |x * scale| <= 127.5: the product is rounded to fp32 first, then adding
+// 1.5 * 2^23 rounds it to an integer (ties to even), which lands in the low
+// mantissa bits.  Contraction must stay off: a fused multiply-add would skip
+// the product's rounding and change ties.
+__device__ __forceinline__ uint32_t quantize_low_byte(float x, float scale) {
+#pragma clang fp contract(off)
+    const float p = x * scale;
+    return __builtin_bit_cast(uint32_t, p + 12582912.0f);
+}
+
 __device__ __forceinline__ int quantize_value(float x, float scale) {
     float p = x * scale;
     float r = __builtin_rintf(p);
@@ -50,16 +92,62 @@ __device__ __forceinline__ int quantize_value(float x, float scale) {
     return (int)r;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+// ---- cross-lane reductions and scans with DPP (no LDS round trips) --------
+// DPP controls of the gfx9 family: quad_perm, row_shr:n (0x110 + n), row_mirror
+// (0x140), row_half_mirror (0x141), row_bcast:15 (0x142), row_bcast:31 (0x143).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// max over the 64 lanes, returned to every lane (v >= 0 or any finite value)
+// max over 16-lane rows of packed u16 pairs: afterwards lanes 0, 16, 32 and 48
+// hold their row's maxima (every lane of a row holds the same value)
+__device__ __forceinline__ uint32_t row16_max_u16x2(uint32_t v) {
+    v = max_u16x2(v, (uint32_t)dpp_i<0xB1>(0, (int)v));
+    v = max_u16x2(v, (uint32_t)dpp_i<0x4E>(0, (int)v));
+    v = max_u16x2(v, (uint32_t)dpp_i<0x141>(0, (int)v));
+    v = max_u16x2(v, (uint32_t)dpp_i<0x140>(0, (int)v));
     return v;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0xB1>(0, __builtin_bit_cast(int, v))));   // xor 1
+    v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x4E>(0, __builtin_bit_cast(int, v))));   // xor 2
+    v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x141>(0, __builtin_bit_cast(int, v))));  // half-row
+    v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x140>(0, __builtin_bit_cast(int, v))));  // row
+    const int b = __builtin_bit_cast(int, v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += dpp_i<0x111>(0, v);        // row_shr:1 (lanes without a source add 0)
+    v += dpp_i<0x112>(0, v);        // row_shr:2
+    v += dpp_i<0x114>(0, v);        // row_shr:4
+    v += dpp_i<0x118>(0, v);        // row_shr:8
+    v += dpp_i<0x142, 0xA>(0, v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_i<0x143, 0xC>(0, v);   // row_bcast:31 into rows 2 and 3
     return v;
+}
+
+// max over the 64 lanes (unsigned), returned to every lane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)dpp_i<0xB1>(0, (int)v));
+    v = max(v, (uint32_t)dpp_i<0x4E>(0, (int)v));
+    v = max(v, (uint32_t)dpp_i<0x141>(0, (int)v));
+    v = max(v, (uint32_t)dpp_i<0x140>(0, (int)v));
+    const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
 }
 
 // ---- launchers (each returns hipGetLastError() after its launches) --------
@@ -91,6 +179,14 @@ struct MatmulArgs {
 size_t matmul_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
+
+// Fused one-launch forward for small M (activation quantization + product).
+bool linear_small_m_supported(int M, int K);
+hipError_t launch_linear_small_m(const void* X, bool bf16, int M, int N, int K, float t,
+                                 const int8_t* CB, const float* SCB, const void* bias, void* Y,
+                                 int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
+                                 int32_t* C_i32, hipStream_t stream, hipEvent_t ev_start,
+                                 hipEvent_t ev_stop);
 
 // Kernel families used by launch_matmul.
 constexpr int kSmallM = 16;  // M <= kSmallM takes the streaming kernel

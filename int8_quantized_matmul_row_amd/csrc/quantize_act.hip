@@ -54,12 +54,7 @@ __device__ __forceinline__ uint2 quantize8(v8u16 v, uint32_t bits, float scale) 
 // Exclusive scan of one int per thread over a 256-thread block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* lds /*[4]*/, int* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int t = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += t;
-    }
+    const int incl = wave_incl_scan(v);
     if (lane == 63) lds[wave] = incl;
     __syncthreads();
     int wave_off = 0, sum = 0;
@@ -220,10 +215,16 @@ __global__ __launch_bounds__(kThreads) void act_outlier_mask(const float* __rest
             }
         }
     }
+    // max over the 8 lanes of each mask byte: xor 1, xor 2 (quad_perm), then
+    // the half-row mirror (lane i <-> 7 - i within 8 lanes)
 #pragma unroll
-    for (int off = 1; off < 8; off <<= 1)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cm[e] = fmaxf(cm[e], __shfl_xor(cm[e], off, kWave));
+    for (int e = 0; e < 8; ++e) {
+        float v = cm[e];
+        v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0xB1>(0, __builtin_bit_cast(int, v))));
+        v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x4E>(0, __builtin_bit_cast(int, v))));
+        v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x141>(0, __builtin_bit_cast(int, v))));
+        cm[e] = v;
+    }
     uint32_t bits = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) bits |= (cm[e] >= t ? 1u : 0u) << e;

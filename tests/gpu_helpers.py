@@ -69,6 +69,34 @@ def run_gpu(wl, threshold=None, want_C=True, weight=None, device="cuda:0"):
     return out
 
 
+def run_gpu_linear(wl, threshold=None, weight=None, device="cuda:0"):
+    """The one-call forward (llmint8_linear) on workload wl; same dict as run_gpu."""
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    t = wl.threshold if threshold is None else threshold
+    dev = torch.device(device)
+    X = to_torch(wl.X, wl.dtype, dev)
+    if weight is None:
+        CB, SCB = pkg.quantize_weight(to_torch(wl.W, wl.dtype, dev))
+    else:
+        CB, SCB = weight
+    bias = None if wl.bias is None else to_torch(wl.bias, wl.dtype, dev)
+    C = torch.empty((wl.M, wl.N), dtype=torch.int32, device=dev)
+    Y, q = pkg.linear(X, CB, SCB, bias=bias, threshold=t, C_i32=C)
+    torch.cuda.synchronize()
+    n_out = int(q.n_out.item())
+    n_pad = (n_out + 31) // 32 * 32
+    out = dict(
+        CA=q.CA.cpu().numpy(), SCA=q.SCA.cpu().numpy(),
+        idx=q.idx[:n_out].cpu().numpy(), n_out=n_out,
+        XO=bits_of(q.XO[:wl.M * n_pad]).reshape(wl.M, n_pad),
+        Y=bits_of(Y), weight=(CB, SCB), C_dev=C, Y_dev=Y)
+    if weight is None:
+        out["CB"] = CB.cpu().numpy()
+        out["SCB"] = SCB.cpu().numpy()
+    return out
+
+
 def check_y(Ybits: np.ndarray, Yref: np.ndarray, dtype: int, label: str):
     y = synth.bits_to_f32(Ybits, dtype).astype(np.float64)
     assert np.all(np.isfinite(y)), label

@@ -189,3 +189,50 @@ def test_sweep_threshold_extremes_full_size(orc, t, sweep_weight):
 def test_bloom_ffn_full_size(orc, name):
     wl = synth.make_workload(name)
     sampled_check(orc, wl, 6)
+
+
+# ---- the one-call forward (llmint8_linear): fused small-M kernel and the
+# ---- quantize_act + matmul sequence, every stage against the oracle ----------
+from gpu_helpers import run_gpu_linear  # noqa: E402
+
+LINEAR = [
+    # M, N, K, dtype, planted outlier columns, bias, threshold
+    (8, 4096, 4096, F16, 4, False, 6.0),      # the decode workload's shape
+    (1, 100, 64, F16, 0, True, 6.0),
+    (5, 333, 1024, BF16, 3, True, 6.0),
+    (16, 1030, 4096, F16, 6, True, 6.0),      # largest fused M at K = 4096
+    (8, 520, 8192, BF16, 9, False, 6.0),      # largest fused K at M = 8
+    (12, 260, 2048, F16, 12, True, 0.0),      # every column an outlier
+    (7, 96, 512, F16, 2, True, float("inf")),
+    (16, 64, 8192, F16, 2, False, 6.0),       # M*K beyond the fused bound
+    (33, 300, 640, BF16, 3, True, 6.0),       # tiled path through llmint8_linear
+]
+
+
+@pytest.mark.parametrize("M,N,K,dt,nout,bias,t", LINEAR,
+                         ids=[f"{r[0]}x{r[1]}x{r[2]}-{synth.DTYPE_NAMES[r[3]]}-t{r[6]}"
+                              for r in LINEAR])
+def test_linear_one_call(orc, M, N, K, dt, nout, bias, t):
+    wl = synth.make_random(M, N, K, dt, seed=3 * M + N + K, n_outlier_cols=nout,
+                           bias_sigma=0.01 if bias else None)
+    label = f"linear {M}x{N}x{K} t={t}"
+    log(f"[parity] {label}")
+    g = run_gpu_linear(wl, t)
+    ref = orc.forward(wl.X, wl.W, wl.dtype, t, bias=wl.bias)
+    err, scale = compare(wl, g, ref, label=label)
+    log(f"[parity] {label}: ok, n_out={g['n_out']} max|dY|={err:.3g}")
+
+
+def test_linear_decode_workload_matches_two_calls(orc):
+    """The fused forward and quantize_act + matmul give identical integer stages
+    on the decode workload, and both match the oracle."""
+    wl = synth.make_workload("decode")
+    a = run_gpu_linear(wl)
+    b = run_gpu(wl, weight=a["weight"])
+    for key in ("CA", "SCA", "idx", "XO"):
+        assert np.array_equal(a[key], b[key]), key
+    import torch
+    assert torch.equal(a["C_dev"], b["C_dev"])
+    ref = orc.forward(wl.X, wl.W, wl.dtype, wl.threshold)
+    compare(wl, a, {**ref, "CB": a["weight"][0].cpu().numpy(),
+                    "SCB": a["weight"][1].cpu().numpy()}, label="linear decode")
