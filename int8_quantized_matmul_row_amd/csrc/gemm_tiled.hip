@@ -7,34 +7,43 @@
 // "absmax quantization" (denormalize by the outer product of the two absmax
 // vectors), section "Usage" (recovered weight CB * SCB / 127).
 //
-// Design (gfx950, 256 CUs in 8 XCDs, 160 KiB LDS per CU):
-//  * Workgroup tile 256 x 256, K step 128 bytes; 4 waves in a 2 x 2 grid, each
-//    wave owns a 128 x 128 sub-tile = 4 x 4 v_mfma_i32_32x32x32_i8 blocks
-//    (256 int32 accumulators per lane, kept in AGPRs).  One workgroup per CU.
-//  * CA [M,K] and CB [N,K] are both K-contiguous.  Each K step loads 2 x 32 KiB
-//    with 16-byte global loads (8 lanes cover one 128-byte row slice) into
-//    registers while the MFMAs run on the other LDS buffer (2 x 64 KiB double
-//    buffer, one barrier per step).  LDS rows are 128 bytes with the 16-byte
-//    slots XOR-swizzled by (row & 7), so both the 16-byte stores and the
-//    16-byte fragment reads of 8 consecutive rows hit distinct banks.
+// Design (gfx950: 256 CUs in 8 XCDs, 160 KiB LDS per CU, 64 LDS banks):
+//  * Workgroup tile 256 x 256; 4 waves in a 2 x 2 grid, each wave owns a
+//    128 x 128 sub-tile = 4 x 4 v_mfma_i32_32x32x32_i8 blocks (256 int32
+//    accumulators per lane, in AGPRs).  One workgroup per CU.
+//  * K advances in 64-byte stages through a 4-deep ring of LDS buffers
+//    (A 256 x 64 + B 256 x 64 bytes each, 128 KiB in all).  Stages are filled
+//    by global_load_lds_dwordx4: each wave instruction moves 16 rows x 64 bytes
+//    straight from memory into LDS, no registers involved, three stages ahead
+//    of the MFMAs.  One barrier per stage.
+//  * LDS rows are 64 bytes; 16-byte chunk c of row r sits in slot c ^ ((r>>2)&3),
+//    so a 16-lane phase of 16-byte fragment reads (16 consecutive rows, one
+//    chunk) touches all 64 banks once.
+//  * The fragments of the next K step are read while the MFMAs of the current
+//    one run; the stage barrier sits between the two MFMA halves of a stage.
 //  * Tile order: blocks are dispatched round-robin over the 8 XCDs; block b is
 //    remapped so that each XCD walks a contiguous range of a grouped raster
-//    (8 tile rows per group), which keeps an XCD's tiles on shared CA/CB
-//    panels in its own L2.
+//    (8 tile rows per group) and its tiles share CA/CB panels in its own L2.
 //  * Epilogue, fused: int32 -> fp32 times SCA[m]/127; the outlier columns
 //    (n_out read from device memory, no host sync) run as
-//    v_mfma_f32_32x32x16_{f16,bf16} of XO against the int8 weights gathered
-//    at idx and converted exactly to 16-bit, accumulating into the same
-//    registers; then times SCB[n]/127, plus bias, round to 16-bit, store.
+//    v_mfma_f32_32x32x16_{f16,bf16} of XO against the int8 weights gathered at
+//    idx (exact in 16-bit), into the same accumulators; then times SCB[n]/127,
+//    plus bias, rounded to 16-bit, staged in LDS and written with full 16-byte
+//    row-contiguous stores.
 #include "common.h"
 
 namespace llmint8 {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BM = 256, BN = 256, BKS = 64;
+constexpr int kStages = 4;
+constexpr int kStageBytes = (BM + BN) * BKS;  // 32 KiB
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
+constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
+constexpr int kSmemBytes =
+    kStages * kStageBytes > BM * kYStride ? kStages * kStageBytes : BM * kYStride;
 
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int total = tiles_m * tiles_n;
@@ -47,6 +56,43 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
     const int in_group = L - group * per_group;
     tm = first_m + in_group % gsz;
     tn = in_group / gsz;
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// workgroup barrier without the memory fence of __syncthreads (the LDS-DMA
+// completions are awaited explicitly with vmcnt); the empty asm keeps the
+// compiler from moving LDS accesses across it
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One global_load_lds_dwordx4: lane p's 16 bytes at gptr land in LDS at
+// lds_addr + 16 p.  Issued through asm so the compiler does not treat later LDS
+// reads as possibly aliasing it (it would wait for every load in flight); the
+// waits are explicit (wait_vmcnt + stage_barrier).  M0 is saved and restored.
+__device__ __forceinline__ void dma16(const int8_t* gptr, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(gptr)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const int8_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)p;
 }
 
 template <bool BF16>
@@ -69,6 +115,8 @@ __device__ __forceinline__ v16f mfma16(typename Vec16<BF16>::type a, typename Ve
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+}  // namespace
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
@@ -77,8 +125,8 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const uint16_t* __restrict__ XO, const int8_t* __restrict__ CB,
                        const float* __restrict__ SCB, const uint16_t* __restrict__ bias,
                        uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32) {
-    __shared__ __attribute__((aligned(16))) int8_t smem[2][2][BM * BK];
-    __shared__ float s_sa[BM], s_sb[BN];
+    __shared__ __attribute__((aligned(16))) int8_t smem[kSmemBytes];
+    __shared__ float s_sb[BN], s_bias[BN];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -86,34 +134,38 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // global -> LDS: thread owns rows lrow + 32 i (i < 8), 16-byte slot lchk
-    const int lrow = tid >> 3, lchk = tid & 7;
-    const int lslot = (lchk ^ (lrow & 7)) * 16;
-    const int8_t* pA = CA + (size_t)(m0 + lrow) * K + lchk * 16;
-    const int8_t* pB = CB + (size_t)(n0 + lrow) * K + lchk * 16;
-    const int a_rows = M - m0 - lrow;  // row i valid iff 32 i < a_rows
-    const int b_rows = N - n0 - lrow;
-    v4i ra[8], rb[8];
-
-    auto gload = [&](int kt) {
-        const bool kok = kt * BK + lchk * 16 < K;
+    // ---- stage loads: wave w fills rows [64w, 64w + 64) of A and of B, 16 rows
+    // per instruction; lane p lands in row 16 q + p/4, slot p%4, and so fetches
+    // the logical chunk (p%4) ^ ((p/16)&3).  Rows past M / N re-read the last
+    // valid row (their results are never stored).
+    const int dchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+    const int8_t* pa[4];
+    const int8_t* pb[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            ra[i] = (kok && 32 * i < a_rows)
-                        ? *reinterpret_cast<const v4i*>(pA + (size_t)(32 * i) * K + kt * BK)
-                        : v4i{0, 0, 0, 0};
-            rb[i] = (kok && 32 * i < b_rows)
-                        ? *reinterpret_cast<const v4i*>(pB + (size_t)(32 * i) * K + kt * BK)
-                        : v4i{0, 0, 0, 0};
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wave + 16 * i + (lane >> 2);
+        pa[i] = CA + (size_t)min(m0 + r, M - 1) * K + dchunk;
+        pb[i] = CB + (size_t)min(n0 + r, N - 1) * K + dchunk;
+    }
+    const uint32_t lds_base = lds_address(smem) + 64 * wave * BKS;  // this wave's rows
+    auto issue = [&](int kt) {
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (kt % kStages) * kStageBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(pa[i] + (size_t)kt * BKS, st + 16 * i * BKS);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(pb[i] + (size_t)kt * BKS, st + BM * BKS + 16 * i * BKS);
     };
-    auto lstore = [&](int buf) {
-        int8_t* sA = smem[buf][0];
-        int8_t* sB = smem[buf][1];
+
+    // ---- fragments: lane l reads row (l & 31) of each 32-row block, chunk
+    // 2 ks + l/32 of the stage
+    const int rr = lane & 31;
+    auto read_frags = [&](int kt, int ks, v4i* a, v4i* b) {
+        const int8_t* st = smem + (kt % kStages) * kStageBytes;
+        const int slot = ((2 * ks + (lane >> 5)) ^ ((rr >> 2) & 3)) * 16;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            *reinterpret_cast<v4i*>(sA + (lrow + 32 * i) * BK + lslot) = ra[i];
-            *reinterpret_cast<v4i*>(sB + (lrow + 32 * i) * BK + lslot) = rb[i];
+        for (int t = 0; t < 4; ++t) {
+            a[t] = *reinterpret_cast<const v4i*>(st + (wm * 128 + 32 * t + rr) * BKS + slot);
+            b[t] = *reinterpret_cast<const v4i*>(st + BM * BKS + (wn * 128 + 32 * t + rr) * BKS + slot);
         }
     };
 
@@ -122,132 +174,132 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
-
-    const int r32 = lane & 31, kh = lane >> 5;
-    auto compute = [&](int buf) {
-        const int8_t* sA = smem[buf][0] + (wm * 128 + r32) * BK;
-        const int8_t* sB = smem[buf][1] + (wn * 128 + r32) * BK;
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            const int slot = ((2 * ks + kh) ^ (r32 & 7)) * 16;
-            v4i a[4], b[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                a[t] = *reinterpret_cast<const v4i*>(sA + t * 32 * BK + slot);
-                b[t] = *reinterpret_cast<const v4i*>(sB + t * 32 * BK + slot);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-    };
-
-    const int nk = (K + BK - 1) / BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        compute(buf);
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue ----------------------------------------------------------
-    if (tid < BM) {
-        const int m = m0 + tid;
-        s_sa[tid] = m < M ? SCA[m] / 127.0f : 0.0f;
-        const int n = n0 + tid;
-        s_sb[tid] = n < N ? SCB[n] / 127.0f : 0.0f;
-    }
-    __syncthreads();
-
-    // accumulator register v of lane l in a 32x32 block: row 8(v/4) + 4(l/32) + v%4, col l%32
-    const int row_base = wm * 128 + 4 * kh;  // + 32 i + 8 (v/4) + v%4
-    const int col_base = wn * 128 + r32;     // + 32 j
-
-    if (C_i32) {
+    auto mfma_block = [&](const v4i* a, const v4i* b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
+                // operands swapped: the block is computed transposed, so a lane's
+                // accumulators run along N (see the epilogue)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
+    };
+
+    // epilogue operands, fetched now so their latency hides under the K loop
+    const int n_out = *n_out_ptr;
+    float sa_raw[4];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = m0 + row_base + 32 * i + 8 * (v >> 2) + (v & 3);
-                    const int n = n0 + col_base + 32 * j;
-                    if (m < M && n < N) C_i32[(size_t)m * N + n] = acc[i][j][v];
-                }
+    for (int i = 0; i < 4; ++i) sa_raw[i] = SCA[min(m0 + wm * 128 + 32 * i + (lane & 31), M - 1)];
+    {
+        const int n = min(n0 + tid, N - 1);
+        s_sb[tid] = SCB[n] / 127.0f;
+        s_bias[tid] = bias ? widen16<BF16>(bias[n]) : 0.0f;
     }
 
-    v16f f[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float sa = s_sa[row_base + 32 * i + 8 * (v >> 2) + (v & 3)];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) f[i][j][v] = (float)acc[i][j][v] * sa;
-        }
+    const int nk = K / BKS;
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 2) issue(2);
+    if (nk > 2) wait_vmcnt<16>();
+    else if (nk > 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
+    stage_barrier();
 
-    const int n_out = *n_out_ptr;
-    if (n_out > 0) {
-        typedef typename Vec16<BF16>::type vec_t;
-        const int n_pad = (n_out + 31) & ~31;
-        for (int j0 = 0; j0 < n_out; j0 += 16) {
-            vec_t xa[4], xb[4];
+    v4i fa0[4], fb0[4], fa1[4], fb1[4];
+    read_frags(0, 0, fa0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+        read_frags(kt, 1, fa1, fb1);
+        mfma_block(fa0, fb0);
+        if (kt + 2 < nk) wait_vmcnt<8>();  // stage kt+1 landed; kt+2 may be in flight
+        else wait_vmcnt<0>();
+        stage_barrier();  // stage kt+1 visible; stage kt-1 no longer read by anyone
+        if (kt + 3 < nk) issue(kt + 3);
+        if (kt + 1 < nk) read_frags(kt + 1, 0, fa0, fb0);
+        mfma_block(fa1, fb1);
+    }
+
+    // ---- epilogue ----------------------------------------------------------
+    // Block (i, j) is held transposed: register v of lane l is row
+    // m = 32 i + l%32 and column n = 32 j + 8 (v/4) + 4 (l/32) + v%4 of the
+    // wave's sub-tile, so four consecutive registers are four consecutive
+    // columns of one output row.  One 32-row block at a time: dequantize, add
+    // the outlier product, scale, bias, round, and stage 8-byte pieces in LDS.
+    __syncthreads();  // every wave is done reading the stage buffers
+    const int kh = lane >> 5;
+    const int m_lane = wm * 128 + rr;              // + 32 i
+    const int n_lane = wn * 128 + 4 * kh;          // + 32 j + 8 (v/4) + v%4
+    uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
+    typedef typename Vec16<BF16>::type vec_t;
+    const int n_pad = (n_out + 31) & ~31;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = m0 + wm * 128 + 32 * i + r32;
-                v8u16 raw = m < M ? *reinterpret_cast<const v8u16*>(XO + (size_t)m * n_pad + j0 + 8 * kh)
-                                  : v8u16{0, 0, 0, 0, 0, 0, 0, 0};
-                xa[i] = __builtin_bit_cast(vec_t, raw);
-            }
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + m_lane + 32 * i;
+        if (C_i32) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int n = n0 + n_lane + 32 * j + 8 * (v >> 2) + (v & 3);
+                    if (m < M && n < N) C_i32[(size_t)m * N + n] = acc[i][j][v];
+                }
+        }
+        const float sa = sa_raw[i] / 127.0f;
+        v16f f[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) f[j][v] = (float)acc[i][j][v] * sa;
+
+        for (int j0 = 0; j0 < n_out; j0 += 16) {
+            // outlier k-block j0: XO rows as the B operand (transposed product)
+            const vec_t xa = __builtin_bit_cast(
+                vec_t, *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + j0 + 8 * kh));
             int kcol[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int j = j0 + 8 * kh + e;
-                kcol[e] = j < n_out ? idx[j] : -1;
+                const int jj = j0 + 8 * kh + e;
+                kcol[e] = jj < n_out ? idx[jj] : -1;
             }
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int n = n0 + col_base + 32 * jj;
-                const int8_t* cb = CB + (size_t)(n < N ? n : 0) * K;
+            for (int j = 0; j < 4; ++j) {
+                const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr, N - 1) * K;
                 v8u16 raw;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float w = (kcol[e] >= 0 && n < N) ? (float)cb[kcol[e]] : 0.0f;
-                    raw[e] = narrow16<BF16>(w);  // |w| <= 127: exact in fp16 and bf16
-                }
-                xb[jj] = __builtin_bit_cast(vec_t, raw);
+                for (int e = 0; e < 8; ++e)  // |w| <= 127: exact in fp16 and bf16
+                    raw[e] = kcol[e] >= 0 ? narrow16<BF16>((float)cb[kcol[e]]) : (uint16_t)0;
+                f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
+        }
+
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) f[i][jj] = mfma16<BF16>(xa[i], xb[jj], f[i][jj]);
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int nl = n_lane + 32 * j + 8 * a4;
+                uint32_t h[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    h[b] = narrow16<BF16>(f[j][4 * a4 + b] * s_sb[nl + b] + s_bias[nl + b]);
+                *reinterpret_cast<uint2*>(ys + (m_lane + 32 * i) * (kYStride / 2) + nl) =
+                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            }
+    }
+    __syncthreads();
+    const int rows = min(BM, M - m0), cols = min(BN, N - n0);
+    if ((N & 7) == 0) {
+        // 32 lanes per 512-byte row, 8 rows per pass of the workgroup
+        const int c8 = (tid & 31) * 8;
+        for (int r = tid >> 5; r < rows; r += kThreads / 32) {
+            if (c8 < cols)
+                *reinterpret_cast<v4i*>(Y + (size_t)(m0 + r) * N + n0 + c8) =
+                    *reinterpret_cast<const v4i*>(smem + r * kYStride + c8 * 2);
+        }
+    } else {
+        for (int e = tid; e < rows * BN; e += kThreads) {
+            const int r = e / BN, c = e - r * BN;
+            if (c < cols) Y[(size_t)(m0 + r) * N + n0 + c] = ys[r * (kYStride / 2) + c];
         }
     }
-
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int nl = col_base + 32 * j;
-        const int n = n0 + nl;
-        if (n >= N) continue;
-        const float sb = s_sb[nl];
-        const float bv = bias ? widen16<BF16>(bias[n]) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + row_base + 32 * i + 8 * (v >> 2) + (v & 3);
-                if (m < M) Y[(size_t)m * N + n] = narrow16<BF16>(f[i][j][v] * sb + bv);
-            }
-    }
 }
-
-}  // namespace
 
 hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                              hipEvent_t ev_stop) {
