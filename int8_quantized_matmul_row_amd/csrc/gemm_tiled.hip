@@ -157,16 +157,15 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     };
 
     // ---- fragments: lane l reads row (l & 31) of each 32-row block, chunk
-    // 2 ks + l/32 of the stage
+    // 2 ks + l/32 of the stage.  Fragment f < 4 is A block f, f >= 4 is B block
+    // f - 4.
     const int rr = lane & 31;
-    auto read_frags = [&](int kt, int ks, v4i* a, v4i* b) {
-        const int8_t* st = smem + (kt % kStages) * kStageBytes;
+    const int a_off = wm * 128 * BKS, b_off = BM * BKS + wn * 128 * BKS;
+    auto read_frag = [&](int kt, int ks, int f) -> v4i {
         const int slot = ((2 * ks + (lane >> 5)) ^ ((rr >> 2) & 3)) * 16;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            a[t] = *reinterpret_cast<const v4i*>(st + (wm * 128 + 32 * t + rr) * BKS + slot);
-            b[t] = *reinterpret_cast<const v4i*>(st + BM * BKS + (wn * 128 + 32 * t + rr) * BKS + slot);
-        }
+        const int off = (kt % kStages) * kStageBytes + slot +
+                        (f < 4 ? a_off + 32 * f * BKS : b_off + 32 * (f - 4) * BKS);
+        return *reinterpret_cast<const v4i*>(smem + rr * BKS + off);
     };
 
     v16i acc[4][4];
@@ -174,15 +173,6 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
-    auto mfma_block = [&](const v4i* a, const v4i* b) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                // operands swapped: the block is computed transposed, so a lane's
-                // accumulators run along N (see the epilogue)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b[j], a[i], acc[i][j], 0, 0, 0);
-    };
 
     // epilogue operands, fetched now so their latency hides under the K loop
     const int n_out = *n_out_ptr;
@@ -204,17 +194,50 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     else wait_vmcnt<0>();
     stage_barrier();
 
-    v4i fa0[4], fb0[4], fa1[4], fb1[4];
-    read_frags(0, 0, fa0, fb0);
+    // Fragments are read in the order of first use by the MFMA sequence below
+    // (block (i, j) = step q with i = q/4, j = q%4): A0, B0..B3, A1, A2, A3.
+    constexpr int kReadOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+    v4i f0[8], f1[8];  // f[0..3] = A blocks, f[4..7] = B blocks
+#pragma unroll
+    for (int r = 0; r < 8; ++r) f0[kReadOrder[r]] = read_frag(0, 0, kReadOrder[r]);
+
+    // One stage = 2 K steps x 16 MFMAs per wave.  The order is pinned with
+    // sched_barrier so that every MFMA is followed by at most one LDS read or
+    // one LDS-DMA issue, and the loads of stage kt+3 are split over both halves
+    // (A rows in the first, B rows in the second): the four waves' 32 DMA
+    // instructions per stage then never queue up at the address unit at once.
+    // Stage kt+3 goes to buffer (kt+3)%4 = (kt-1)%4, whose last reads (second
+    // K step of stage kt-1) happened before the previous barrier.
     for (int kt = 0; kt < nk; ++kt) {
-        read_frags(kt, 1, fa1, fb1);
-        mfma_block(fa0, fb0);
-        if (kt + 2 < nk) wait_vmcnt<8>();  // stage kt+1 landed; kt+2 may be in flight
+        const bool more = kt + 1 < nk, dma = kt + 3 < nk;
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((kt + 3) % kStages) * kStageBytes);
+        // first K step: MFMAs on f0; reads of the second K step into f1; A part of stage kt+3
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = q >> 2, j = q & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f0[4 + j], f0[i], acc[i][j], 0, 0, 0);
+            if (q < 8) f1[kReadOrder[q]] = read_frag(kt, 1, kReadOrder[q]);
+            else if (q < 12 && dma) dma16(pa[q - 8] + (size_t)(kt + 3) * BKS, st + 16 * (q - 8) * BKS);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // stage kt+1 must have landed.  Issued after it: stage kt+2 (8 loads,
+        // if any) and the A part of stage kt+3 (4, if any).
+        if (kt + 3 < nk) wait_vmcnt<12>();
+        else if (kt + 2 < nk) wait_vmcnt<8>();
         else wait_vmcnt<0>();
-        stage_barrier();  // stage kt+1 visible; stage kt-1 no longer read by anyone
-        if (kt + 3 < nk) issue(kt + 3);
-        if (kt + 1 < nk) read_frags(kt + 1, 0, fa0, fb0);
-        mfma_block(fa1, fb1);
+        stage_barrier();  // stage kt+1 visible to every wave
+        // second K step: MFMAs on f1; B part of stage kt+3; reads of stage kt+1 into f0
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = q >> 2, j = q & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1[4 + j], f1[i], acc[i][j], 0, 0, 0);
+            if (q < 4) {
+                if (dma) dma16(pb[q] + (size_t)(kt + 3) * BKS, st + BM * BKS + 16 * q * BKS);
+            } else if (q >= 8 && more) {
+                f0[kReadOrder[q - 8]] = read_frag(kt + 1, 0, kReadOrder[q - 8]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 
     // ---- epilogue ----------------------------------------------------------
