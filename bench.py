@@ -34,6 +34,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 ROTATE_BYTES = 512 << 20     # > 2x the Infinity Cache
 KERNEL_SOURCES = {
+    "decode": ["int8_quantized_matmul_row_amd/csrc/linear_decode.hip",
+               "int8_quantized_matmul_row_amd/csrc/common.h"],
     "fused": ["int8_quantized_matmul_row_amd/csrc/linear_small_m.hip",
               "int8_quantized_matmul_row_amd/csrc/common.h"],
     "small_m": ["int8_quantized_matmul_row_amd/csrc/gemm_small_m.hip",
@@ -43,12 +45,14 @@ KERNEL_SOURCES = {
 }
 
 
-KERNEL_NAMES = {"fused": "linear_small_m_kernel", "small_m": "gemm_small_m_kernel",
+KERNEL_NAMES = {"decode": "linear_decode_kernel", "fused": "linear_small_m_kernel", "small_m": "gemm_small_m_kernel",
                 "tiled": "gemm_tiled_kernel"}
 
 
 def kernel_family(M, K):
     """The kernel that carries the product in llmint8_linear for this shape."""
+    if 1 <= M <= 8 and M * K <= 32768 and K <= 8192:
+        return "decode"
     if 1 <= M <= 16 and M * K <= 65536 and K <= 8192:
         return "fused"
     return "small_m" if M <= 16 else "tiled"
@@ -70,7 +74,7 @@ def algorithmic_bytes(family, M, N, K, n_out, has_bias):
     n_pad = (n_out + 31) // 32 * 32
     common = N * K + 4 * N + (2 * N if has_bias else 0) + 2 * M * N
     act_out = M * K + 4 * M + 2 * M * n_pad + 4 * n_out
-    if family == "fused":
+    if family in ("decode", "fused"):
         return common + 2 * M * K + act_out + 4
     return common + act_out
 
@@ -147,6 +151,17 @@ def cpu_baseline(wl, budget_s=12.0):
             "kind": "oracle", "sample": sample, "ms_per_step": round(step_s * 1e3, 3)}
 
 
+def calibrate_copy(torch, dev, nbytes, launches):
+    """A plain copy of known size: each launch reads and writes nbytes once."""
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "launches": launches}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +171,9 @@ def main():
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (steps times), "
+                         "the reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -169,6 +187,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev, args.calibrate_copy << 20, args.steps)
+        return
     hip = Hip()
     wl = synth.make_workload(args.config)
     if args.threshold is not None:

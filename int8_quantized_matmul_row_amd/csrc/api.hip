@@ -124,6 +124,12 @@ llmint8_status linear_impl(const void* X, int dtype, int64_t M, int64_t N, int64
     if ((s = check_device()) != LLMINT8_OK) return s;
     const bool bf16 = dtype == LLMINT8_BF16;
     hipError_t e;
+    if (M > 0 && N > 0 && llmint8::linear_decode_supported((int)M, (int)K)) {
+        e = llmint8::launch_linear_decode(X, bf16, (int)M, (int)N, (int)K, threshold, CB, SCB,
+                                          bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,
+                                          C_i32, stream, ev_start, ev_stop);
+        return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+    }
     if (M > 0 && N > 0 && llmint8::linear_small_m_supported((int)M, (int)K)) {
         e = llmint8::launch_linear_small_m(X, bf16, (int)M, (int)N, (int)K, threshold, CB, SCB,
                                            bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,

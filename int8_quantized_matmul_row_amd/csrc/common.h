@@ -150,6 +150,44 @@ __device__ __forceinline__ int wave_sum(int v) {
     return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
 }
 
+// ---- LDS-DMA and explicit waits -------------------------------------------
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// workgroup barrier without the memory fence of __syncthreads (the LDS-DMA
+// completions are awaited explicitly with vmcnt); the empty asm keeps the
+// compiler from moving LDS accesses across it
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One global_load_lds_dwordx4: lane p's 16 bytes at gptr land in LDS at
+// lds_addr + 16 p.  Issued through asm so the compiler does not treat later LDS
+// reads as possibly aliasing it (it would wait for every load in flight); the
+// waits are explicit (wait_vmcnt + stage_barrier).  M0 is saved and restored.
+__device__ __forceinline__ void dma16(const int8_t* gptr, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(gptr)
+        : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const int8_t* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)p;
+}
+
 // ---- launchers (each returns hipGetLastError() after its launches) --------
 hipError_t launch_quantize_weight(const void* W, bool bf16, int N, int K, int8_t* CB, float* SCB,
                                   hipStream_t stream);
@@ -187,6 +225,15 @@ hipError_t launch_linear_small_m(const void* X, bool bf16, int M, int N, int K, 
                                  int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
                                  int32_t* C_i32, hipStream_t stream, hipEvent_t ev_start,
                                  hipEvent_t ev_stop);
+
+// Fused one-launch forward for decode batches (M <= 8, M*K <= 32768): compact
+// code, activations staged in LDS.  Preferred over launch_linear_small_m.
+bool linear_decode_supported(int M, int K);
+hipError_t launch_linear_decode(const void* X, bool bf16, int M, int N, int K, float t,
+                                const int8_t* CB, const float* SCB, const void* bias, void* Y,
+                                int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
+                                int32_t* C_i32, hipStream_t stream, hipEvent_t ev_start,
+                                hipEvent_t ev_stop);
 
 // Kernel families used by launch_matmul.
 constexpr int kSmallM = 16;  // M <= kSmallM takes the streaming kernel

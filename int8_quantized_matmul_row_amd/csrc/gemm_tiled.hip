@@ -58,43 +58,6 @@ __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int&
     tn = in_group / gsz;
 }
 
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// workgroup barrier without the memory fence of __syncthreads (the LDS-DMA
-// completions are awaited explicitly with vmcnt); the empty asm keeps the
-// compiler from moving LDS accesses across it
-__device__ __forceinline__ void stage_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// One global_load_lds_dwordx4: lane p's 16 bytes at gptr land in LDS at
-// lds_addr + 16 p.  Issued through asm so the compiler does not treat later LDS
-// reads as possibly aliasing it (it would wait for every load in flight); the
-// waits are explicit (wait_vmcnt + stage_barrier).  M0 is saved and restored.
-__device__ __forceinline__ void dma16(const int8_t* gptr, uint32_t lds_addr) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds_addr), "v"(gptr)
-        : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const int8_t* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)p;
-}
-
 template <bool BF16>
 struct Vec16;
 template <>

@@ -1,0 +1,378 @@
+// Fused LLM.int8() linear layer for decode batches (M <= 8, M*K <= 32768), one
+// launch, written for a short instruction stream.
+//
+// "A Gentle Introduction to 8-bit Matrix Multiplication for transformers at
+// scale": section "LLM.int8() summary" (1. extract the outlier columns of the
+// hidden states, 2. multiply outliers in 16-bit and the rest in int8, 3.
+// dequantize the int8 result and add the outlier result), section "inside the
+// MatMul" (magnitude 6 or more; row-wise scales for the hidden states,
+// per-output-channel scales for the weight), section "absmax quantization"
+// (scale by 127/absmax; denormalize by the outer product of the two absmax
+// vectors), section "Usage" (recovered weight CB * SCB / 127).
+//
+// Every workgroup runs its code once, from an instruction cache that is cold
+// at each launch and refilled through an L2 that the weight stream keeps busy,
+// so the instruction bytes executed are a first-order cost here.  Hence:
+//  * X (at most 64 KiB) goes to LDS with global_load_lds_dwordx4, 1 KiB per
+//    instruction, and every activation pass is a short loop over rows reading
+//    LDS, not unrolled code over registers;
+//  * the workgroup's NB x K weight block (NB = 16 or 32 output channels) is
+//    issued right after, into registers in the MFMA operand layout, and
+//    streams in while the activations are quantized; loads retire in issue
+//    order, so X is complete as soon as no more than the weight loads (and the
+//    two epilogue operands) are outstanding;
+//  * the outlier columns' weight bytes each output needs are fetched with a
+//    few byte loads as soon as the outlier list is known (they land with or
+//    after the weight block), and the outlier activations are read from LDS.
+// Per workgroup: column maxima and the outlier mask, row absmax over
+// non-outlier columns (packed 16-bit maxima, DPP wave reductions), ascending
+// outlier ranks, int8 codes into LDS, v_mfma_i32_16x16x64_i8 over K, and one
+// thread per (token, channel) for
+//   Y = (C * SCA[m]/127 + sum_j XO[m,j] * CB[n, idx[j]]) * SCB[n]/127 + bias[n].
+// The activation outputs (CA spread over the workgroups; SCA, the outlier list
+// and count, XO from workgroup 0) are written too, so the call has the results
+// of llmint8_quantize_act followed by llmint8_matmul.
+#include "common.h"
+
+namespace llmint8 {
+
+namespace {
+
+constexpr int kDecThreads = 512;
+constexpr int kDecWaves = 8;
+constexpr int kDecMaxRows = 8;
+constexpr int kDecXBytes = 65536;                  // M * K * 2
+constexpr int kDecCaBytes = 32896;                 // >= M * (K + 16) for M * K <= 32768
+constexpr int kDecMaxK = 8192;
+constexpr int kDecMaxChunks = kDecMaxK / 8;
+constexpr int kDecGather = 8;                      // outlier weight bytes fetched early
+
+// CPT: 8-column chunks per thread (K <= 4096 -> 1, else 2); NB: output
+// channels per workgroup; SPW: 64-wide K steps per wave.  Waves split as NB/16
+// channel tiles x 8/(NB/16) K groups: wave w takes tile w % T and the
+// contiguous steps [g * SPW, g * SPW + SPW) of group g = w / T.
+template <bool BF16, int CPT, int NB, int SPW>
+__global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
+    const uint16_t* __restrict__ X, int M, int N, int K, float t,
+    const int8_t* __restrict__ CB, const float* __restrict__ SCB,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
+    int8_t* __restrict__ CA_out, float* __restrict__ SCA_out, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ n_out_out, uint16_t* __restrict__ XO_out,
+    int32_t* __restrict__ C_i32) {
+    constexpr int T = NB / 16;
+    constexpr int G = kDecWaves / T;
+    __shared__ __attribute__((aligned(16))) uint16_t xl[(kDecXBytes + 1024) / 2];
+    __shared__ __attribute__((aligned(16))) int8_t ca[kDecCaBytes];
+    __shared__ uint16_t idx_s[kDecMaxK];           // ascending outlier columns
+    __shared__ uint8_t mask[kDecMaxChunks];
+    __shared__ int chunk_rank[kDecMaxChunks + 1];  // outliers before each 8-column chunk
+    __shared__ uint32_t rmax_w[kDecWaves][kDecMaxRows];
+    __shared__ float sca[kDecMaxRows];
+    __shared__ float scl[kDecMaxRows];             // 127 / SCA (0 for an all-zero row)
+    __shared__ int scan_lds[kDecWaves];
+    __shared__ int red[kDecWaves][4][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.x * NB;
+    const int nchunk = K >> 3, nsteps = K >> 6;
+    const int ca_stride = K + 16;  // 16 rows at one offset hit distinct banks
+    const int xbytes = M * K * 2;
+
+    // ---- 1a. X into LDS: instruction q (1 KiB) issued by wave q % 8 ----------
+    {
+        const int nq = (xbytes + 1023) >> 10;
+        const uint32_t base = lds_address(reinterpret_cast<const int8_t*>(xl));
+        const int8_t* xg = reinterpret_cast<const int8_t*>(X);
+        const int w0 = __builtin_amdgcn_readfirstlane(wave);
+        for (int q = w0; q < nq; q += kDecWaves)  // the tail lanes re-read the last 16 bytes
+            dma16(xg + min(q * 1024 + lane * 16, xbytes - 16),
+                  __builtin_amdgcn_readfirstlane(base + q * 1024));
+    }
+    // ---- 1b. epilogue operands: thread -> (token e_m, channel n0 + e_n) -------
+    const int e_n = tid % NB, e_m = tid / NB;
+    const int n_e = n0 + e_n;
+    const bool e_ok = e_m < M && n_e < N;
+    const int n_c = min(n_e, N - 1);
+    // raw values only: using them here would make the stream wait for them
+    const float scb_raw = SCB[n_c];
+    const uint16_t bias_raw = *(bias ? bias + n_c : reinterpret_cast<const uint16_t*>(SCB + n_c));
+    // ---- 1c. the weight block: lane (row r16, 16-byte group kg) holds
+    // CB[n0 + 16 tt + r16, 64 s + 16 kg ...] for this wave's steps s ----------
+    const int tt = wave % T, grp = wave / T, r16 = lane & 15, kg = lane >> 4;
+    const int8_t* pb = CB + (size_t)min(n0 + tt * 16 + r16, N - 1) * K + kg * 16;
+    v4i breg[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i) {
+        const int s = min(grp * SPW + i, nsteps - 1);
+        breg[i] = *reinterpret_cast<const v4i*>(pb + (size_t)s * 64);
+    }
+    // X has landed once at most the SPW + 2 younger loads are outstanding
+    wait_vmcnt<SPW + 2>();
+    __syncthreads();
+
+    // ---- 2. outlier mask: column max over the M rows, one byte per 8 columns --
+    // Magnitudes are compared as 16-bit patterns (packed pairs); for finite
+    // values this orders exactly like the fp32 values.
+    const uint32_t tb = threshold_bits<BF16>(t);
+    uint32_t mbits[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + kDecThreads * j;
+        const int cc = c < nchunk ? c : 0;
+        uint32_t cm[4] = {0, 0, 0, 0};
+        for (int r = 0; r < M; ++r) {
+            const v4i w = *reinterpret_cast<const v4i*>(xl + (size_t)r * K + cc * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cm[i] = max_u16x2(cm[i], abs2((uint32_t)w[i]));
+        }
+        uint32_t bits = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bits |= ((cm[i] & 0xffffu) >= tb ? 1u : 0u) << (2 * i);
+            bits |= ((cm[i] >> 16) >= tb ? 1u : 0u) << (2 * i + 1);
+        }
+        mbits[j] = c < nchunk ? bits : 0u;
+        if (c < nchunk) mask[c] = (uint8_t)bits;
+    }
+    // ---- 3. row absmax over non-outlier columns (a thread's own mask bits
+    // suffice): one wave maximum per row into LDS --------------------------------
+    {
+        uint32_t keep16[CPT][4];  // 0x7fff in the 16-bit halves of non-outlier columns
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const bool ok = tid + kDecThreads * j < nchunk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                keep16[j][i] = !ok ? 0u
+                                   : ((((mbits[j] >> (2 * i)) & 1u) ? 0u : 0x7fffu) |
+                                      (((mbits[j] >> (2 * i + 1)) & 1u) ? 0u : 0x7fff0000u));
+        }
+        for (int r = 0; r < M; ++r) {
+            uint32_t m2 = 0;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int c = tid + kDecThreads * j;
+                const v4i w = *reinterpret_cast<const v4i*>(xl + (size_t)r * K + (c < nchunk ? c : 0) * 8);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m2 = max_u16x2(m2, (uint32_t)w[i] & keep16[j][i]);
+            }
+            const uint32_t wm = wave_max_u32(max(m2 & 0xffffu, m2 >> 16));
+            if (lane == 0) rmax_w[wave][r] = wm;
+        }
+    }
+    __syncthreads();  // mask and per-wave row maxima complete
+
+    // ---- 4. ranks: exclusive scan of the chunks' outlier counts; row scales ---
+    {
+        // thread t owns chunks 2t and 2t + 1 (K/8 <= 1024)
+        const int c0 = 2 * tid;
+        const int a0 = c0 < nchunk ? __popc((uint32_t)mask[c0]) : 0;
+        const int a1 = c0 + 1 < nchunk ? __popc((uint32_t)mask[c0 + 1]) : 0;
+        const int cnt = a0 + a1;
+        const int incl = wave_incl_scan(cnt);
+        if (lane == 63) scan_lds[wave] = incl;
+        if (tid < M) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int w = 0; w < kDecWaves; ++w) m = max(m, rmax_w[w][tid]);
+            const float amax = widen16<BF16>((uint16_t)m);
+            sca[tid] = amax;
+            scl[tid] = amax == 0.0f ? 0.0f : 127.0f / amax;
+        }
+        __syncthreads();
+        int base = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) {
+            if (w < wave) base += scan_lds[w];
+            total += scan_lds[w];
+        }
+        const int ex = base + incl - cnt;
+        if (c0 < nchunk) chunk_rank[c0] = ex;
+        if (c0 + 1 < nchunk) chunk_rank[c0 + 1] = ex + a0;
+        if (tid == 0) chunk_rank[nchunk] = total;
+    }
+    __syncthreads();
+    const int n_out = chunk_rank[nchunk];
+    // the ascending outlier list
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + kDecThreads * j;
+        uint32_t bits = mbits[j];
+        if (bits) {
+            int rk = chunk_rank[c];
+            while (bits) {
+                idx_s[rk++] = (uint16_t)(c * 8 + __builtin_ctz(bits));
+                bits &= bits - 1;
+            }
+        }
+    }
+    __syncthreads();
+    // this output's weight bytes in the first outlier columns, fetched now
+    int cbg[kDecGather];
+    {
+        const int8_t* cbrow = CB + (size_t)n_c * K;
+#pragma unroll
+        for (int j = 0; j < kDecGather; ++j) cbg[j] = cbrow[j < n_out ? (int)idx_s[j] : 0];
+    }
+
+    // ---- 5. int8 activations into LDS (row by row) ----------------------------
+    {
+        uint32_t keep_lo[CPT], keep_hi[CPT];  // 0xff per non-outlier byte
+        bool export_ca[CPT];                  // this workgroup's share of the CA output
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const uint32_t bits = mbits[j];
+            keep_lo[j] = 0;
+            keep_hi[j] = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                keep_lo[j] |= ((bits >> e) & 1u) ? 0u : (0xffu << (8 * e));
+                keep_hi[j] |= ((bits >> (e + 4)) & 1u) ? 0u : (0xffu << (8 * e));
+            }
+            export_ca[j] = (tid + kDecThreads * j) % gridDim.x == blockIdx.x;
+        }
+        for (int r = 0; r < M; ++r) {
+            const float scale = scl[r];
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                const int c = tid + kDecThreads * j;
+                if (c < nchunk) {
+                    const v8u16 v = *reinterpret_cast<const v8u16*>(xl + (size_t)r * K + c * 8);
+                    // non-outlier |x| <= SCA, so |x * scale| <= 127 and the low
+                    // byte is the code; outlier columns are masked to 0
+                    uint32_t q[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) q[e] = quantize_low_byte(widen16<BF16>(v[e]), scale);
+                    const uint32_t lo = __builtin_amdgcn_perm(
+                        __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
+                        __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(
+                        __builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
+                        __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
+                    const uint2 packed = make_uint2(lo & keep_lo[j], hi & keep_hi[j]);
+                    *reinterpret_cast<uint2*>(ca + r * ca_stride + c * 8) = packed;
+                    if (export_ca[j])
+                        *reinterpret_cast<uint2*>(CA_out + (size_t)r * K + c * 8) = packed;
+                }
+            }
+        }
+    }
+    // workgroup 0 writes the outlier list, its count, XO and SCA
+    if (blockIdx.x == 0) {
+        const int n_pad = (n_out + 31) & ~31;
+        for (int j = tid; j < n_out; j += kDecThreads) idx_out[j] = idx_s[j];
+        for (int p = tid; p < M * n_pad; p += kDecThreads) {
+            const int r = p / n_pad, j = p - r * n_pad;
+            XO_out[p] = j < n_out ? xl[(size_t)r * K + idx_s[j]] : (uint16_t)0;
+        }
+        if (tid == 0) *n_out_out = n_out;
+        if (tid < M) SCA_out[tid] = sca[tid];
+    }
+    __syncthreads();
+
+    // ---- 6. int8 MFMA over this wave's K steps --------------------------------
+    // A = CA rows (lane row r16 = token), B = CB rows (channel): accumulator
+    // register v of lane l holds token 4*(l/16) + v, channel n0 + 16 tt + l%16.
+    {
+        const bool a_ok = r16 < M;
+        const int8_t* pa = ca + r16 * ca_stride + kg * 16;
+        v4i acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int s = grp * SPW + i;
+            if (s < nsteps) {
+                const v4i a = a_ok ? *reinterpret_cast<const v4i*>(pa + s * 64) : v4i{0, 0, 0, 0};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, breg[i], acc, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[v];
+    }
+    __syncthreads();
+
+    // ---- 7. epilogue: one output per thread ------------------------------------
+    if (!e_ok) return;
+    const int et = e_n >> 4, l = (e_n & 15) + 16 * (e_m >> 2), v = e_m & 3;
+    int c32 = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) c32 += red[et + T * g][v][l];
+    if (C_i32) C_i32[(size_t)e_m * N + n_e] = c32;
+    float y = (float)c32 * (sca[e_m] / 127.0f);
+    const uint16_t* xrow = xl + (size_t)e_m * K;
+#pragma unroll
+    for (int j = 0; j < kDecGather; ++j)
+        if (j < n_out) y += widen16<BF16>(xrow[idx_s[j]]) * (float)(int8_t)cbg[j];
+    for (int j = kDecGather; j < n_out; ++j) {
+        const int k = idx_s[j];
+        y += widen16<BF16>(xrow[k]) * (float)CB[(size_t)n_e * K + k];
+    }
+    const float bv = bias ? widen16<BF16>(bias_raw) : 0.0f;
+    Y[(size_t)e_m * N + n_e] = narrow16<BF16>(y * (scb_raw / 127.0f) + bv);
+}
+
+template <bool BF16, int CPT, int NB, int SPW>
+void launch_variant(hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
+                    const uint16_t* x, int M, int N, int K, float t, const int8_t* CB,
+                    const float* SCB, const uint16_t* b, uint16_t* y, int8_t* CA, float* SCA,
+                    int32_t* idx, int32_t* n_out, uint16_t* xo, int32_t* C_i32) {
+    auto fn = linear_decode_kernel<BF16, CPT, NB, SPW>;
+    const dim3 grid((N + NB - 1) / NB);
+    if (ev_start || ev_stop)
+        hipExtLaunchKernelGGL(fn, grid, dim3(kDecThreads), 0, stream, ev_start, ev_stop, 0, x, M,
+                              N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32);
+    else
+        fn<<<grid, kDecThreads, 0, stream>>>(x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out,
+                                             xo, C_i32);
+}
+
+#define DEC_ARGS stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32
+#define DEC_PARAMS                                                                              \
+    hipStream_t stream, hipEvent_t e0, hipEvent_t e1, const uint16_t *x, int M, int N, int K,   \
+        float t, const int8_t *CB, const float *SCB, const uint16_t *b, uint16_t *y,           \
+        int8_t *CA, float *SCA, int32_t *idx, int32_t *n_out, uint16_t *xo, int32_t *C_i32
+
+// steps per wave: K / 64 over the K groups, rounded up to a power of two
+template <bool BF16, int CPT, int NB>
+void launch_steps(DEC_PARAMS) {
+    constexpr int G = kDecWaves / (NB / 16);
+    const int spw = (K / 64 + G - 1) / G;
+    if (spw <= 1) launch_variant<BF16, CPT, NB, 1>(DEC_ARGS);
+    else if (spw <= 2) launch_variant<BF16, CPT, NB, 2>(DEC_ARGS);
+    else if (spw <= 4) launch_variant<BF16, CPT, NB, 4>(DEC_ARGS);
+    else if (spw <= 8) launch_variant<BF16, CPT, NB, 8>(DEC_ARGS);
+    else launch_variant<BF16, CPT, NB, 16>(DEC_ARGS);
+}
+
+template <bool BF16>
+void launch_dtype(DEC_PARAMS) {
+    if (K > 4096) launch_steps<BF16, 2, 16>(DEC_ARGS);
+    else launch_steps<BF16, 1, 16>(DEC_ARGS);
+}
+
+#undef DEC_ARGS
+#undef DEC_PARAMS
+
+}  // namespace
+
+bool linear_decode_supported(int M, int K) {
+    return M >= 1 && M <= kDecMaxRows && K <= kDecMaxK && (int64_t)M * K <= kDecXBytes / 2;
+}
+
+hipError_t launch_linear_decode(const void* X, bool bf16, int M, int N, int K, float t,
+                                const int8_t* CB, const float* SCB, const void* bias, void* Y,
+                                int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
+                                int32_t* C_i32, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+    const uint16_t* x = static_cast<const uint16_t*>(X);
+    const uint16_t* b = static_cast<const uint16_t*>(bias);
+    uint16_t* y = static_cast<uint16_t*>(Y);
+    uint16_t* xo = static_cast<uint16_t*>(XO);
+    if (bf16)
+        launch_dtype<true>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo,
+                           C_i32);
+    else
+        launch_dtype<false>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo,
+                            C_i32);
+    return hipGetLastError();
+}
+
+}  // namespace llmint8

@@ -69,7 +69,7 @@ def run_gpu(wl, threshold=None, want_C=True, weight=None, device="cuda:0"):
     return out
 
 
-def run_gpu_linear(wl, threshold=None, weight=None, device="cuda:0"):
+def run_gpu_linear(wl, threshold=None, weight=None, device="cuda:0", workspace=None):
     """The one-call forward (llmint8_linear) on workload wl; same dict as run_gpu."""
     import torch
     import int8_quantized_matmul_row_amd as pkg
@@ -82,7 +82,7 @@ def run_gpu_linear(wl, threshold=None, weight=None, device="cuda:0"):
         CB, SCB = weight
     bias = None if wl.bias is None else to_torch(wl.bias, wl.dtype, dev)
     C = torch.empty((wl.M, wl.N), dtype=torch.int32, device=dev)
-    Y, q = pkg.linear(X, CB, SCB, bias=bias, threshold=t, C_i32=C)
+    Y, q = pkg.linear(X, CB, SCB, bias=bias, threshold=t, C_i32=C, workspace=workspace)
     torch.cuda.synchronize()
     n_out = int(q.n_out.item())
     n_pad = (n_out + 31) // 32 * 32

@@ -206,6 +206,10 @@ LINEAR = [
     (7, 96, 512, F16, 2, True, float("inf")),
     (16, 64, 8192, F16, 2, False, 6.0),       # M*K beyond the fused bound
     (33, 300, 640, BF16, 3, True, 6.0),       # tiled path through llmint8_linear
+    (8, 200, 4160, F16, 3, True, 6.0),        # last K slice one step deep
+    (3, 64, 192, BF16, 1, False, 6.0),        # one slice, a wave with no step
+    (16, 77, 2112, BF16, 2, True, 2.5),       # ~90 outlier columns per slice
+    (8, 4096, 1024, F16, 1, True, 6.0),       # four slices of 256 columns
 ]
 
 
@@ -236,3 +240,59 @@ def test_linear_decode_workload_matches_two_calls(orc):
     ref = orc.forward(wl.X, wl.W, wl.dtype, wl.threshold)
     compare(wl, a, {**ref, "CB": a["weight"][0].cpu().numpy(),
                     "SCB": a["weight"][1].cpu().numpy()}, label="linear decode")
+
+
+def test_linear_workspace_reuse_any_shape(orc):
+    """One workspace, sized for the largest call, serves fused and unfused
+    calls of different shapes in turn."""
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    dev = torch.device("cuda:0")
+    shapes = [(8, 4096, 4096, F16), (33, 300, 640, BF16), (16, 1030, 4096, F16),
+              (5, 333, 1024, BF16), (8, 4096, 4096, F16)]
+    size = max(pkg.llmint8_linear_workspace_size(M, N, K) for M, N, K, _ in shapes)
+    ws = (torch.empty((max(size, 1),), dtype=torch.uint8, device=dev), size)
+    for i, (M, N, K, dt) in enumerate(shapes):
+        wl = synth.make_random(M, N, K, dt, seed=100 + i, n_outlier_cols=3, bias_sigma=0.01)
+        log(f"[parity] workspace reuse {M}x{N}x{K}")
+        g = run_gpu_linear(wl, workspace=ws)
+        ref = orc.forward(wl.X, wl.W, wl.dtype, wl.threshold, bias=wl.bias)
+        compare(wl, g, ref, label=f"reuse {M}x{N}x{K}")
+
+
+def test_linear_fused_repeatable_and_graph_replays():
+    """The fused forward gives the same bits on every call, and replays of a
+    captured HIP graph (with eager work between them) match the eager call."""
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    dev = torch.device("cuda:0")
+    wl = synth.make_workload("decode")
+    X = torch.from_numpy(wl.X.view(np.int16)).to(dev).view(torch.float16)
+    W = torch.from_numpy(wl.W.view(np.int16)).to(dev).view(torch.float16)
+    CB, SCB = pkg.quantize_weight(W)
+    ws = pkg.linear_workspace(wl.M, wl.N, wl.K, dev)
+    q = pkg.alloc_act(wl.M, wl.K, torch.float16, dev)
+    Y = torch.empty((wl.M, wl.N), dtype=torch.float16, device=dev)
+    C = torch.empty((wl.M, wl.N), dtype=torch.int32, device=dev)
+    pkg.linear(X, CB, SCB, threshold=wl.threshold, out=Y, act=q, C_i32=C, workspace=ws)
+    torch.cuda.synchronize()
+    Y0, C0 = Y.clone(), C.clone()
+    for _ in range(3):
+        Y.zero_()
+        pkg.linear(X, CB, SCB, threshold=wl.threshold, out=Y, act=q, C_i32=C, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y0) and torch.equal(C, C0)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        pkg.linear(X, CB, SCB, threshold=wl.threshold, out=Y, act=q, C_i32=C, workspace=ws,
+                   stream=stream)
+    for r in range(4):
+        Y.zero_()
+        C.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y0), f"graph replay {r}: Y differs"
+        assert torch.equal(C, C0), f"graph replay {r}: C differs"
+        _ = (X.float() * 2).sum().item()  # unrelated eager work between replays
