@@ -14,6 +14,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -186,6 +187,21 @@ __device__ __forceinline__ void dma16(const int8_t* gptr, uint32_t lds_addr) {
 
 __device__ __forceinline__ uint32_t lds_address(const int8_t* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)p;
+}
+
+// LDS accesses with 32-bit addressing: base + byte offset in address space 3.
+// (Generic-pointer arithmetic on an LDS array can be done in 64 bits, with an
+// operand register that may still be the target of a load in flight, which
+// then forces a wait for that load.)
+template <typename T>
+__device__ __forceinline__ T lds_load(const void* base, uint32_t byte_off) {
+    typedef const __attribute__((address_space(3))) char* lds_cptr;
+    return *(const __attribute__((address_space(3))) T*)((lds_cptr)base + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(void* base, uint32_t byte_off, T v) {
+    typedef __attribute__((address_space(3))) char* lds_ptr;
+    *(__attribute__((address_space(3))) T*)((lds_ptr)base + byte_off) = v;
 }
 
 // ---- launchers (each returns hipGetLastError() after its launches) --------

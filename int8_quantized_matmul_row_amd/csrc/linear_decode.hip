@@ -88,6 +88,8 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             dma16(xg + min(q * 1024 + lane * 16, xbytes - 16),
                   __builtin_amdgcn_readfirstlane(base + q * 1024));
     }
+    // every wave's X requests reach the memory pipeline ahead of any weight load
+    stage_barrier();
     // ---- 1b. epilogue operands: thread -> (token e_m, channel n0 + e_n) -------
     const int e_n = tid % NB, e_m = tid / NB;
     const int n_e = n0 + e_n;
