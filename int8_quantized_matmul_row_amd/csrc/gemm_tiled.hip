@@ -228,6 +228,31 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                     if (m < M && n < N) C_i32[(size_t)m * N + n] = acc[i][j][v];
                 }
         }
+        // outlier k-block 0 operands, requested before the conversion below so
+        // that their latency overlaps it: all loads unconditional from clamped
+        // addresses (a load under a branch is awaited where the branch rejoins)
+        const bool have_out = n_out > 0;
+        v8u16 xraw;
+        int8_t wb[4][8];
+        bool kv[8];
+        {
+            // in bounds for n_pad = 0 too: XO holds M * K >= 16 elements
+            xraw = *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + 8 * kh);
+            int kc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jj = 8 * kh + e;
+                kv[e] = jj < n_out;
+                const int col = idx[jj];  // idx holds K >= 64 entries; beyond n_out unused
+                kc[e] = kv[e] ? col : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr, N - 1) * K;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wb[j][e] = cb[kc[e]];
+            }
+        }
         const float sa = sa_raw[i] / 127.0f;
         v16f f[4];
 #pragma unroll
@@ -235,8 +260,21 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 #pragma unroll
             for (int v = 0; v < 16; ++v) f[j][v] = (float)acc[i][j][v] * sa;
 
-        for (int j0 = 0; j0 < n_out; j0 += 16) {
-            // outlier k-block j0: XO rows as the B operand (transposed product)
+        if (have_out) {
+            // XO rows as the B operand (transposed product); |w| <= 127 is
+            // exact in fp16 and bf16
+            const vec_t xa = __builtin_bit_cast(vec_t, xraw);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v8u16 raw;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    raw[e] = kv[e] ? narrow16<BF16>((float)wb[j][e]) : (uint16_t)0;
+                f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
+            }
+        }
+        for (int j0 = 16; j0 < n_out; j0 += 16) {
+            // further outlier k-blocks (more than 16 outlier columns)
             const vec_t xa = __builtin_bit_cast(
                 vec_t, *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + j0 + 8 * kh));
             int kcol[8];
