@@ -57,13 +57,15 @@ class Oracle:
         lib = ctypes.CDLL(path)
         lib.oracle_widen.argtypes = [_P, ctypes.c_int, _I64, _P]
         lib.oracle_quantize_weight.argtypes = [_P, ctypes.c_int, _I64, _I64, _P, _P]
+        lib.oracle_quantize_tensor.argtypes = [_P, ctypes.c_int, _I64, _I64, _P, _P]
         lib.oracle_quantize_act.argtypes = [_P, ctypes.c_int, _I64, _I64, ctypes.c_float,
                                             _P, _P, _P, _P, _P]
         lib.oracle_int8_rows.argtypes = [_P, _P, _I64, _I64, _I64, _P, _I64, _P]
         lib.oracle_recover_weight.argtypes = [_P, _P, _I64, _I64, _P]
         lib.oracle_output_rows.argtypes = [_P, _P, _P, _P, ctypes.c_int, _P, ctypes.c_int32,
                                            _P, _P, _I64, _I64, _I64, _P, _I64, _P]
-        for f in ("oracle_widen", "oracle_quantize_weight", "oracle_quantize_act",
+        for f in ("oracle_widen", "oracle_quantize_weight", "oracle_quantize_tensor",
+                  "oracle_quantize_act",
                   "oracle_int8_rows", "oracle_recover_weight", "oracle_output_rows"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
@@ -88,6 +90,17 @@ class Oracle:
         self._check(self.lib.oracle_quantize_weight(_ptr(W), dtype, N, K, _ptr(CB), _ptr(SCB)),
                     "quantize_weight")
         return CB, SCB
+
+    def quantize_tensor(self, A: np.ndarray, dtype: int):
+        """A uint16 [R,C] -> (Q int8 [R,C], scale float32 [R]): one absmax for the
+        whole tensor, written to every row's scale."""
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        R, C = A.shape
+        Q = np.empty((R, C), dtype=np.int8)
+        scale = np.empty(R, dtype=np.float32)
+        self._check(self.lib.oracle_quantize_tensor(_ptr(A), dtype, R, C, _ptr(Q), _ptr(scale)),
+                    "quantize_tensor")
+        return Q, scale
 
     def quantize_act(self, X: np.ndarray, dtype: int, threshold: float):
         """X uint16 [M,K] -> (CA int8 [M,K], SCA f32 [M], idx int32 [n_out], XO uint16 [M,n_out])."""

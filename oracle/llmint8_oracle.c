@@ -101,6 +101,50 @@ static int8_t quantize_value(float x, float scale) {
     return (int8_t)r;
 }
 
+/* ---- per-tensor absmax quantization (the baseline) ------------------------ */
+/* One scale for the whole tensor: amax = max over every element of |A|;       */
+/* Q = q(A, 127/amax); scale[r] = amax for every row r (so the pair can stand  */
+/* in for a vector-wise (codes, scales) pair).  [GENTLE] "absmax quantization" */
+/* (the scale of a whole vector/tensor), the scheme that the vector-wise and   */
+/* decomposed schemes are measured against.                                    */
+
+int oracle_quantize_tensor(const uint16_t* A, int dtype, int64_t rows, int64_t cols,
+                           int8_t* Q, float* scale) {
+    if ((dtype != 0 && dtype != 1) || rows < 0 || cols < 0) return ERR_ARG;
+    if (fegetround() != FE_TONEAREST) return ERR_ARG;
+    const int64_t n = rows * cols;
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = widen(A[i], dtype);
+        if (!isfinite(a)) return ERR_NONFINITE;
+        a = fabsf(a);
+        if (a > amax) amax = a;
+    }
+#if ORACLE_MUTANT == 12
+    /* mistake: the scale taken per row, not over the whole tensor */
+    for (int64_t r = 0; r < rows; ++r) {
+        float ra = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) {
+            float a = fabsf(widen(A[r * cols + c], dtype));
+            if (a > ra) ra = a;
+        }
+        scale[r] = ra;
+        for (int64_t c = 0; c < cols; ++c)
+            Q[r * cols + c] = ra == 0.0f ? 0 : quantize_value(widen(A[r * cols + c], dtype), absmax_scale(ra));
+    }
+    (void)amax;
+    return OK;
+#endif
+    for (int64_t r = 0; r < rows; ++r) scale[r] = amax;
+    if (amax == 0.0f) {
+        memset(Q, 0, (size_t)n);
+        return OK;
+    }
+    float s = absmax_scale(amax);
+    for (int64_t i = 0; i < n; ++i) Q[i] = quantize_value(widen(A[i], dtype), s);
+    return OK;
+}
+
 /* ---- weight quantization: per output row n ------------------------------ */
 /* SCB[n] = max_k |W[n,k]|; CB[n,k] = q(W[n,k], 127/SCB[n]).                   */
 /* [GENTLE] "absmax quantization" (vector-wise: absmax per column of B = W^T,  */

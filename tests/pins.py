@@ -200,6 +200,46 @@ def pin_invariants(orc):
     assert np.abs(base["C"].astype(np.int64)).max() <= 64 * 127 * 127
 
 
+# -- P10: per-tensor absmax, the baseline scheme ([GENTLE] "absmax
+# quantization": one scale 127/absmax for the whole vector or tensor) -------
+def _tensor_bruteforce(bits, dt):
+    """numpy float32 arithmetic: amax over the tensor, s = 127/amax in float32,
+    q = rint(x * s) (round half to even), clamped."""
+    a = bruteforce.widen(bits, dt).astype(np.float32)
+    amax = np.float32(np.abs(a).max()) if a.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(a.shape, np.int8), np.full(a.shape[0], amax, np.float32)
+    s = np.float32(127.0) / amax
+    q = np.clip(np.rint((a * s).astype(np.float32)), -127, 127).astype(np.int8)
+    return q, np.full(a.shape[0], amax, np.float32)
+
+
+def pin_per_tensor_absmax(orc):
+    # the worked example, read as a one-row tensor
+    g = _golden("absmax_worked_example.json")
+    Q, scale = orc.quantize_tensor(_f16(g["input"]).reshape(1, -1), F16)
+    assert np.array_equal(Q[0], np.array(g["expected_int8"], dtype=np.int8))
+    # brute force on tensors whose rows have different maxima
+    rng = np.random.default_rng([10, 0])
+    for trial in range(20):
+        R, C = (int(v) for v in rng.integers(1, 9, size=2))
+        dt = F16 if trial % 2 == 0 else BF16
+        conv = _f16 if dt == F16 else _bf16
+        A = conv(rng.normal(0, 1.0, (R, C)).astype(np.float32) *
+                 rng.uniform(0.1, 10.0, (R, 1)).astype(np.float32))
+        Q, scale = orc.quantize_tensor(A, dt)
+        Qb, sb = _tensor_bruteforce(A, dt)
+        assert np.array_equal(Q, Qb) and np.array_equal(scale, sb), (trial, R, C)
+    # rows that all share one absmax: per-tensor equals per-row (vector-wise)
+    x = np.array([[1.0, -3.0, 0.5], [3.0, 2.0, -1.25]], dtype=np.float32)
+    Q, scale = orc.quantize_tensor(_f16(x), F16)
+    CB, SCB = orc.quantize_weight(_f16(x), F16)
+    assert np.array_equal(Q, CB) and np.array_equal(scale, SCB)
+    # an all-zero tensor
+    Q, scale = orc.quantize_tensor(np.zeros((3, 4), np.uint16), F16)
+    assert not Q.any() and not scale.any()
+
+
 ALL_PINS = [
     pin_absmax_worked_example,
     pin_zero_point_example,
@@ -210,4 +250,5 @@ ALL_PINS = [
     pin_threshold_zero_closed_form,
     pin_bruteforce_tiny,
     pin_invariants,
+    pin_per_tensor_absmax,
 ]

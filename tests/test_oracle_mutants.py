@@ -22,6 +22,7 @@ MUTANTS = {
     9: "outlier part subtracted",
     10: "outlier gather ignores the index list",
     11: "int8 product drops a term",
+    12: "per-tensor scale taken per row",
 }
 
 
