@@ -71,6 +71,26 @@ typedef enum llmint8_dtype { LLMINT8_F16 = 0, LLMINT8_BF16 = 1 } llmint8_dtype;
 llmint8_status llmint8_quantize_weight(const void* W, int dtype, int64_t N, int64_t K,
                                        int8_t* CB, float* SCB, hipStream_t stream);
 
+/* Bytes of device workspace llmint8_quantize_tensor needs (0 for invalid sizes). */
+size_t llmint8_quantize_tensor_workspace_size(int64_t rows, int64_t cols);
+
+/*
+ * Per-tensor absmax quantization, the baseline scheme ("absmax quantization":
+ * scale by 127 / absmax, with one absmax for the whole tensor), for comparing
+ * schemes.  No outlier extraction.
+ *   A      [rows, cols] 16-bit, read only, finite; cols a positive multiple of 64.
+ *   Q      [rows, cols] int8 out: rne(A * (127 / amax)), amax = max |A| over the
+ *          whole tensor; all 0 when amax == 0.
+ *   scale  [rows] fp32 out: amax in every entry, so (Q, scale) can be passed to
+ *          llmint8_matmul as (CA, SCA) or as (CB, SCB) -- with n_outliers = 0 the
+ *          product is dequantized by amax_X * amax_W / 127^2.
+ *   workspace  llmint8_quantize_tensor_workspace_size bytes, no initialization.
+ * rows == 0 is a no-op.  Errors: as llmint8_quantize_act.
+ */
+llmint8_status llmint8_quantize_tensor(const void* A, int dtype, int64_t rows, int64_t cols,
+                                       int8_t* Q, float* scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of device workspace llmint8_quantize_act needs for M x K (may be 0). */
 size_t llmint8_quantize_act_workspace_size(int64_t M, int64_t K);
 

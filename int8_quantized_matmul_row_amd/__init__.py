@@ -32,6 +32,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or device", 3: "
 
 EXPORTS = (
     "llmint8_quantize_weight",
+    "llmint8_quantize_tensor_workspace_size",
+    "llmint8_quantize_tensor",
     "llmint8_quantize_act_workspace_size",
     "llmint8_quantize_act",
     "llmint8_matmul_workspace_size",
@@ -70,6 +72,9 @@ def lib() -> ctypes.CDLL:
                            "`python -m int8_quantized_matmul_row_amd.build`")
     L = ctypes.CDLL(LIBRARY_PATH)
     L.llmint8_quantize_weight.argtypes = [_P, _INT, _I64, _I64, _P, _P, _P]
+    L.llmint8_quantize_tensor_workspace_size.argtypes = [_I64, _I64]
+    L.llmint8_quantize_tensor_workspace_size.restype = ctypes.c_size_t
+    L.llmint8_quantize_tensor.argtypes = [_P, _INT, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P]
     L.llmint8_quantize_act_workspace_size.argtypes = [_I64, _I64]
     L.llmint8_quantize_act_workspace_size.restype = ctypes.c_size_t
     L.llmint8_quantize_act.argtypes = [_P, _INT, _I64, _I64, ctypes.c_float, _P, _P, _P, _P, _P,
@@ -85,8 +90,9 @@ def lib() -> ctypes.CDLL:
            ctypes.c_size_t, _P]
     L.llmint8_linear.argtypes = lin
     L.llmint8_linear_profiled.argtypes = lin + [_P, _P]
-    for f in ("llmint8_quantize_weight", "llmint8_quantize_act", "llmint8_matmul",
-              "llmint8_matmul_profiled", "llmint8_linear", "llmint8_linear_profiled"):
+    for f in ("llmint8_quantize_weight", "llmint8_quantize_tensor", "llmint8_quantize_act",
+              "llmint8_matmul", "llmint8_matmul_profiled", "llmint8_linear",
+              "llmint8_linear_profiled"):
         getattr(L, f).restype = _INT
     L.llmint8_status_string.argtypes = [_INT]
     L.llmint8_status_string.restype = ctypes.c_char_p
@@ -105,6 +111,16 @@ def _check(fn: str, status: int):
 
 def llmint8_quantize_weight(W, dtype, N, K, CB, SCB, stream=0):
     _check("llmint8_quantize_weight", lib().llmint8_quantize_weight(W, dtype, N, K, CB, SCB, stream))
+
+
+def llmint8_quantize_tensor_workspace_size(rows, cols) -> int:
+    return int(lib().llmint8_quantize_tensor_workspace_size(rows, cols))
+
+
+def llmint8_quantize_tensor(A, dtype, rows, cols, Q, scale, workspace, workspace_bytes, stream=0):
+    _check("llmint8_quantize_tensor",
+           lib().llmint8_quantize_tensor(A, dtype, rows, cols, Q, scale, workspace,
+                                         workspace_bytes, stream))
 
 
 def llmint8_quantize_act_workspace_size(M, K) -> int:
@@ -232,6 +248,32 @@ def alloc_act(M, K, dtype_t, device):
         torch.empty((1,), dtype=torch.int32, device=device),
         torch.empty((max(M * K, 1),), dtype=dtype_t, device=device),
         F16 if dtype_t == torch.float16 else BF16)
+
+
+def quantize_tensor(A, stream=None):
+    """A [R,C] fp16/bf16 -> (Q int8 [R,C], scale fp32 [R]): per-tensor absmax,
+    the baseline scheme (one scale for the whole tensor in every row's entry)."""
+    torch = _torch()
+    _need(A, "A")
+    R, C = A.shape
+    Q = torch.empty((R, C), dtype=torch.int8, device=A.device)
+    scale = torch.empty((R,), dtype=torch.float32, device=A.device)
+    n = llmint8_quantize_tensor_workspace_size(R, C)
+    ws = torch.empty((max(n, 1),), dtype=torch.uint8, device=A.device)
+    llmint8_quantize_tensor(_ptr(A), dtype_code(A), R, C, _ptr(Q), _ptr(scale), _ptr(ws), n,
+                            _stream(stream))
+    return Q, scale
+
+
+def matmul_codes(CA, SCA, CB, SCB, dtype_t, bias=None, out=None, stream=None):
+    """Y = dequant(CA . CB^T) (+ bias) from int8 codes and row / channel scales
+    with no outlier columns -- e.g. two quantize_tensor results (per-tensor
+    absmax) -- through llmint8_matmul."""
+    M, K = CA.shape
+    q = alloc_act(M, K, dtype_t, CA.device)
+    q.n_out.zero_()
+    q = q._replace(CA=CA, SCA=SCA)
+    return matmul(q, CB, SCB, bias=bias, out=out, stream=stream)
 
 
 def act_workspace(M, K, device):

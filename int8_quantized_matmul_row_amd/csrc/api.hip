@@ -191,6 +191,27 @@ llmint8_status llmint8_quantize_weight(const void* W, int dtype, int64_t N, int6
     return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
 }
 
+size_t llmint8_quantize_tensor_workspace_size(int64_t rows, int64_t cols) {
+    if (check_sizes(rows, 0, cols) != LLMINT8_OK) return 0;
+    return llmint8::quantize_tensor_workspace();
+}
+
+llmint8_status llmint8_quantize_tensor(const void* A, int dtype, int64_t rows, int64_t cols,
+                                       int8_t* Q, float* scale, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    llmint8_status s = check_dtype(dtype);
+    if (s != LLMINT8_OK) return s;
+    if ((s = check_sizes(rows, 0, cols)) != LLMINT8_OK) return s;
+    if (rows == 0) return LLMINT8_OK;
+    if (bad_ptr(A) || bad_ptr(Q) || bad_ptr(scale) || bad_ptr(workspace) ||
+        workspace_bytes < llmint8::quantize_tensor_workspace())
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    if ((s = check_device()) != LLMINT8_OK) return s;
+    hipError_t e = llmint8::launch_quantize_tensor(A, dtype == LLMINT8_BF16, rows, cols, Q, scale,
+                                                   workspace, stream);
+    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+}
+
 size_t llmint8_quantize_act_workspace_size(int64_t M, int64_t K) {
     if (check_sizes(M, 0, K) != LLMINT8_OK) return 0;
     return llmint8::quantize_act_workspace(M, K);

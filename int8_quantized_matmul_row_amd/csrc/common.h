@@ -208,6 +208,12 @@ __device__ __forceinline__ void lds_store(void* base, uint32_t byte_off, T v) {
 hipError_t launch_quantize_weight(const void* W, bool bf16, int N, int K, int8_t* CB, float* SCB,
                                   hipStream_t stream);
 
+// Per-tensor absmax quantization (one scale for the whole tensor, written to
+// every row's scale); workspace of quantize_tensor_workspace() bytes.
+size_t quantize_tensor_workspace();
+hipError_t launch_quantize_tensor(const void* A, bool bf16, int64_t rows, int64_t cols, int8_t* Q,
+                                  float* scale, void* ws, hipStream_t stream);
+
 size_t quantize_act_workspace(int64_t M, int64_t K);
 hipError_t launch_quantize_act(const void* X, bool bf16, int M, int K, float threshold,
                                int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
