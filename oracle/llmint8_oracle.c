@@ -336,6 +336,7 @@ int oracle_output_rows(const int32_t* C, const float* SCA, const float* SCB,
                 y_out += (double)widen(X[m * K + k], dtype) * recovered_weight(CB, SCB, K, n, k);
             }
 #if ORACLE_MUTANT == 7
+            (void)bias;
             double b = 0.0; /* mistake: bias dropped */
 #else
             double b = bias ? (double)widen(bias[n], dtype) : 0.0;
