@@ -10,6 +10,10 @@ Page titles cited:
             transformers at scale" (Chinese translation)
   [HF-INT8] "Hugging Face 将 LLM.int8() 8 位矩阵乘法集成到 Transformers 和
             Accelerate 中"
+  [ZHICHAI] the zhichai.top summary of LLM.int8(), outlook section ("未来展望"),
+            which names an 8-bit floating-point type as future work; the FP8
+            pins (P11-P15) fix the E4M3 reading of it against torch's
+            float8_e4m3fn casts, integer arithmetic and exact closed forms.
 """
 from __future__ import annotations
 
@@ -240,6 +244,163 @@ def pin_per_tensor_absmax(orc):
     assert not Q.any() and not scale.any()
 
 
+# -- FP8 (E4M3) variant ([ZHICHAI] "未来展望") ---------------------------------
+def _torch_e4m3(x):
+    """float32 -> E4M3 codes by torch's float8_e4m3fn cast (a library routine:
+    nearest, ties to even, NaN beyond the finite range)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3_values(codes):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+
+
+# -- P11: the code book and the rounding of E4M3 ------------------------------
+def pin_e4m3_codec(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = _torch_e4m3_values(codes)
+    got = orc.e4m3_decode(codes)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), np.nonzero(~same)
+    assert np.isnan(got[[0x7F, 0xFF]]).all() and np.isnan(got).sum() == 2
+    assert got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0x38] == 1.0 and np.signbit(got[0x80])
+    # encoding: every finite code, every midpoint between neighbours (ties),
+    # a float32 ulp either side of each midpoint, log-uniform random values
+    # from far below the smallest subnormal to beyond the largest finite value
+    fin = np.sort(np.unique(got[np.isfinite(got) & (got >= 0)]))
+    mid = ((fin[1:] + fin[:-1]) / 2).astype(np.float32)
+    rng = np.random.default_rng([11, 0])
+    rnd = (2.0 ** rng.uniform(-13, 8.9, 20000)).astype(np.float32)
+    pos = np.concatenate([fin.astype(np.float32), mid, np.nextafter(mid, np.float32(0)),
+                          np.nextafter(mid, np.float32(np.inf)), rnd, np.float32([456.0, 463.9])])
+    x = np.concatenate([pos, -pos, np.float32([0.0, -0.0])])
+    e = orc.e4m3_encode(x)
+    r = _torch_e4m3(x)
+    assert np.array_equal(e, r), x[e != r][:10]
+    # and by search: the encoded value is a nearest finite value; at a tie the
+    # code with the even mantissa field wins
+    v = got[e[:4000].astype(np.int64)]
+    for xi, vi, ci in zip(x[:4000].astype(np.float64), v, e[:4000]):
+        if not np.isfinite(vi):
+            continue
+        d = np.abs(got[np.isfinite(got)] - xi).min()
+        assert abs(vi - xi) == d, (xi, vi)
+    assert orc.e4m3_encode(np.float32([480.0]))[0] == 0x7F  # no finite code
+
+
+# -- P12: weight quantization to E4M3 ----------------------------------------
+def pin_fp8_weight(orc):
+    rng = np.random.default_rng([12, 0])
+    for trial, dt in enumerate((F16, BF16, F16)):
+        conv = _f16 if dt == F16 else _bf16
+        N, K = 7, 96
+        w = rng.normal(0, 0.05, (N, K)).astype(np.float32) * rng.uniform(0.1, 20, (N, 1)).astype(np.float32)
+        w[3] = 0.0
+        w[4, ::2] = -0.0
+        w[5, :] = 0.0
+        w[5, 10] = -2.0 ** -20
+        bits = conv(w)
+        CB, SCB = orc.quantize_weight_fp8(bits, dt)
+        a = bruteforce.widen(bits, dt).astype(np.float32)
+        amax = np.abs(a).max(axis=1).astype(np.float32)
+        assert np.array_equal(SCB, amax), trial
+        for n in range(N):
+            s = np.float32(448.0) / amax[n] if amax[n] > 0 else np.float32(0.0)
+            exp = _torch_e4m3((a[n] * s).astype(np.float32))
+            assert np.array_equal(CB[n], exp), (trial, n)
+            if amax[n] > 0:  # the row maximum becomes +-448
+                k = int(np.argmax(np.abs(a[n])))
+                assert CB[n, k] in (0x7E, 0xFE), (trial, n, CB[n, k])
+        assert not (CB[3] & 0x7F).any() and (CB[4, ::2] == 0x80).all()
+        # the recovered weight is within half an E4M3 step of the weight
+        vals = orc.e4m3_decode(CB) * SCB[:, None].astype(np.float64) / 448.0
+        step = np.maximum(np.abs(a) * 2.0 ** -4, amax[:, None] / 448.0 * 2.0 ** -10)
+        assert (np.abs(vals - a) <= step * (1 + 1e-9)).all()
+
+
+# -- P13: activation quantization to E4M3 ------------------------------------
+def pin_fp8_activation(orc):
+    wl = synth.make_random(9, 4, 128, F16, seed=13, n_outlier_cols=3)
+    for t in (6.0, 2.0, 0.0, float("inf")):
+        CA, SCA, idx, XO = orc.quantize_act_fp8(wl.X, F16, t)
+        # the outlier split and the row scales do not depend on the code format
+        CAi, SCAi, idxi, XOi = orc.quantize_act(wl.X, F16, t)
+        assert np.array_equal(idx, idxi) and np.array_equal(XO, XOi)
+        assert np.array_equal(SCA, SCAi)
+        a = bruteforce.widen(wl.X, F16).astype(np.float32)
+        keep = np.ones(128, bool)
+        keep[idx] = False
+        for m in range(9):
+            s = np.float32(448.0) / SCA[m] if SCA[m] > 0 else np.float32(0.0)
+            exp = _torch_e4m3((a[m] * s).astype(np.float32))
+            exp[~keep] = 0
+            assert np.array_equal(CA[m], exp), (t, m)
+            if SCA[m] > 0:
+                k = int(np.argmax(np.where(keep, np.abs(a[m]), -1)))
+                assert CA[m, k] in (0x7E, 0xFE)
+
+
+# -- P14: the FP8 product, exact, by integer arithmetic ----------------------
+def pin_fp8_product(orc):
+    rng = np.random.default_rng([14, 0])
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    for M, N, K in ((3, 5, 64), (1, 1, 1), (4, 2, 8192)):
+        CA = rng.choice(finite, (M, K)).astype(np.uint8)
+        CB = rng.choice(finite, (N, K)).astype(np.uint8)
+        if K == 8192:  # the largest sum: every product 448^2, one sign
+            CA[0] = 0x7E
+            CB[0] = 0x7E
+        C = orc.fp8_rows(CA, CB)
+        ia = np.rint(_torch_e4m3_values(CA) * 512).astype(np.int64)  # multiples of 2^-9
+        ib = np.rint(_torch_e4m3_values(CB) * 512).astype(np.int64)
+        exact = ia @ ib.T
+        assert np.array_equal(C * 2.0 ** 18, exact.astype(np.float64)), (M, N, K)
+    rows = np.array([2, 0], dtype=np.int64)
+    assert np.array_equal(orc.fp8_rows(CA, CB, rows), orc.fp8_rows(CA, CB)[rows])
+
+
+# -- P15: the FP8 output is exact on E4M3-representable inputs ---------------
+def fp8_exact_case(seed, dt, M=6, N=5, K=128, n_out=3, bias=True):
+    """X, W whose non-outlier rows are E4M3 values times a power of two with
+    each row's maximum at 448 times that power, so that every code and every
+    scale is exact and the method returns X . W^T + bias exactly."""
+    rng = np.random.default_rng([15, seed])
+    conv = _f16 if dt == F16 else _bf16
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = _torch_e4m3_values(finite)
+    cols = rng.choice(K, n_out, replace=False)
+    rest = np.setdiff1d(np.arange(K), cols)
+    w = rng.choice(vals, (N, K)) * 2.0 ** -6
+    w[np.arange(N), rng.integers(0, K, N)] = 448.0 * 2.0 ** -6 * rng.choice([-1, 1], N)
+    x = rng.choice(vals, (M, K)) * 2.0 ** -7          # |x| <= 3.5 < 6
+    x[np.arange(M), rng.choice(rest, M)] = 448.0 * 2.0 ** -7 * rng.choice([-1, 1], M)
+    x[:, cols] = rng.uniform(-3, 3, (M, n_out))
+    x[0, cols] = rng.choice([-1, 1], n_out) * rng.uniform(6, 40, n_out)
+    X, W = conv(x.astype(np.float32)), conv(w.astype(np.float32))
+    b = conv(rng.normal(0, 0.5, N).astype(np.float32)) if bias else None
+    return X, W, b, np.sort(cols)
+
+
+def pin_fp8_exact_closed_form(orc):
+    for seed, dt in ((0, F16), (1, BF16), (2, F16)):
+        X, W, b, cols = fp8_exact_case(seed, dt, bias=seed != 2)
+        out = orc.forward_fp8(X, W, dt, 6.0, bias=b)
+        assert np.array_equal(out["idx"], cols)
+        x = bruteforce.widen(X, dt).astype(np.float64)
+        w = bruteforce.widen(W, dt).astype(np.float64)
+        ref = x @ w.T + (bruteforce.widen(b, dt).astype(np.float64) if b is not None else 0.0)
+        assert np.allclose(out["Y"], ref, rtol=1e-12, atol=1e-12), np.abs(out["Y"] - ref).max()
+        # threshold +inf: the outlier columns go through E4M3 too and are no
+        # longer exact; the error is bounded by the codes' half step
+        inf = orc.forward_fp8(X, W, dt, float("inf"), bias=b)
+        assert inf["idx"].size == 0 and not np.allclose(inf["Y"], ref, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_absmax_worked_example,
     pin_zero_point_example,
@@ -251,4 +412,9 @@ ALL_PINS = [
     pin_bruteforce_tiny,
     pin_invariants,
     pin_per_tensor_absmax,
+    pin_e4m3_codec,
+    pin_fp8_weight,
+    pin_fp8_activation,
+    pin_fp8_product,
+    pin_fp8_exact_closed_form,
 ]

@@ -23,6 +23,10 @@ MUTANTS = {
     10: "outlier gather ignores the index list",
     11: "int8 product drops a term",
     12: "per-tensor scale taken per row",
+    13: "E4M3 ties rounded away from zero",
+    14: "FP8 product dequantized by 448 instead of 448^2",
+    15: "E4M3 subnormals flushed to zero",
+    16: "FP8 scale uses the int8 range 127",
 }
 
 
