@@ -166,10 +166,11 @@ size_t llmint8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
  * "Usage" section: int8 weights placed once, 16-bit activations in, 16-bit
  * output).  Arguments have the meanings given above; CA, SCA, outlier_idx,
  * n_outliers and X_outlier are filled exactly as llmint8_quantize_act fills
- * them.  C_i32 may be NULL.  For M <= 16 with M*K <= 65536 the forward is one
- * fused kernel (each workgroup re-derives the tiny activation quantization
- * while its weight slab streams in); otherwise it is the quantize_act launches
- * followed by the matmul kernel.  workspace: llmint8_linear_workspace_size bytes.
+ * them.  C_i32 may be NULL.  For M <= 16 with K <= 4096, or M <= 8 with
+ * K <= 8192, the forward is one fused kernel (each workgroup re-derives the
+ * tiny activation quantization while its weight slab streams in); otherwise it
+ * is the quantize_act launches followed by the matmul kernel.
+ * workspace: llmint8_linear_workspace_size bytes.
  */
 llmint8_status llmint8_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
                               float threshold, const int8_t* CB, const float* SCB,
@@ -186,6 +187,89 @@ llmint8_status llmint8_linear_profiled(const void* X, int dtype, int64_t M, int6
                                        int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
                                        int32_t* C_i32, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
+/*
+ * ---- FP8 (E4M3) variant of the decomposition -------------------------------
+ * The zhichai.top summary of LLM.int8() (outlook section, its list of the
+ * method's limitations) names an 8-bit floating-point type as future work.
+ * These entry points run the same decomposition -- the same outlier columns,
+ * row and channel absmax scales and 16-bit outlier product -- with OCP FP8
+ * E4M3 codes in place of int8, on gfx950's fp8 matrix instructions:
+ *   code  = e4m3(x * (448 / absmax)): fp32 divide, fp32 multiply, then the
+ *           nearest E4M3 value (ties to the even code, subnormals kept, a
+ *           result that rounds to zero keeps its sign).  E4M3: sign, 4
+ *           exponent bits (bias 7), 3 mantissa bits, largest finite 448, no
+ *           infinities; codes 0x7F/0xFF (NaN) are never produced.
+ *   value(code) is that E4M3 number; the recovered weight is
+ *           value(CB[n,k]) * SCB[n] / 448.
+ *   C[m,n] = sum_k value(CA[m,k]) * value(CB[n,k]), accumulated in fp32 by the
+ *           matrix cores (every product is exact; the sum's rounding order is
+ *           the hardware's), and
+ *   Y[m,n] = (C[m,n] * SCA[m] / 448 + sum_{j<n_out} XO[m,j] * value(CB[n,idx[j]]))
+ *            * SCB[n] / 448 + bias[n].
+ * Codes travel as uint8 bytes.  Sizes, dtypes, pointers, streams and errors
+ * follow the conventions at the top of this file.  A vector whose absmax is 0
+ * gets scale 0 and the codes of its signed zeros (0x00 / 0x80).
+ */
+
+/* E4M3 weight codes, as llmint8_quantize_weight with 448 for 127:
+ *   CB [N,K] uint8 out: e4m3(W[n,k] * (448 / SCB[n]));  SCB [N] fp32 out: row absmax. */
+llmint8_status llmint8_quantize_weight_fp8(const void* W, int dtype, int64_t N, int64_t K,
+                                           uint8_t* CB, float* SCB, hipStream_t stream);
+
+/* E4M3 activation codes with outlier extraction, as llmint8_quantize_act (same
+ * outlier_idx, n_outliers, X_outlier, SCA and workspace) except
+ *   CA [M,K] uint8 out: e4m3(X[m,k] * (448 / SCA[m])) for non-outlier k, 0x00 for
+ *      outlier k. */
+llmint8_status llmint8_quantize_act_fp8(const void* X, int dtype, int64_t M, int64_t K,
+                                        float threshold, uint8_t* CA, float* SCA,
+                                        int32_t* outlier_idx, int32_t* n_outliers,
+                                        void* X_outlier, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
+/* The FP8 product Y (formula above) from llmint8_quantize_act_fp8 and
+ * llmint8_quantize_weight_fp8 outputs.  C_f32 [M,N] fp32 out or NULL: the
+ * accumulated C before scaling.  workspace: as llmint8_matmul. */
+llmint8_status llmint8_matmul_fp8(int dtype, int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* CA, const float* SCA,
+                                  const int32_t* outlier_idx, const int32_t* n_outliers,
+                                  const void* X_outlier, const uint8_t* CB, const float* SCB,
+                                  const void* bias, void* Y, float* C_f32, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* llmint8_matmul_fp8 with `start`/`stop` bound to the dispatch of its GEMM kernel. */
+llmint8_status llmint8_matmul_fp8_profiled(int dtype, int64_t M, int64_t N, int64_t K,
+                                           const uint8_t* CA, const float* SCA,
+                                           const int32_t* outlier_idx,
+                                           const int32_t* n_outliers, const void* X_outlier,
+                                           const uint8_t* CB, const float* SCB, const void* bias,
+                                           void* Y, float* C_f32, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream,
+                                           hipEvent_t start, hipEvent_t stop);
+
+/* Bytes of device workspace llmint8_linear_fp8 needs for M x N x K (may be 0). */
+size_t llmint8_linear_fp8_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* The whole FP8 forward: llmint8_quantize_act_fp8 then llmint8_matmul_fp8 (two or
+ * four launches), filling CA, SCA, outlier_idx, n_outliers, X_outlier as the
+ * former does and C_f32 (may be NULL) as the latter.
+ * workspace: llmint8_linear_fp8_workspace_size bytes. */
+llmint8_status llmint8_linear_fp8(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                                  float threshold, const uint8_t* CB, const float* SCB,
+                                  const void* bias, void* Y, uint8_t* CA, float* SCA,
+                                  int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                  float* C_f32, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* llmint8_linear_fp8 with `start`/`stop` bound to the dispatch of its GEMM kernel. */
+llmint8_status llmint8_linear_fp8_profiled(const void* X, int dtype, int64_t M, int64_t N,
+                                           int64_t K, float threshold, const uint8_t* CB,
+                                           const float* SCB, const void* bias, void* Y,
+                                           uint8_t* CA, float* SCA, int32_t* outlier_idx,
+                                           int32_t* n_outliers, void* X_outlier, float* C_f32,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream, hipEvent_t start,
+                                           hipEvent_t stop);
 
 /* Static English text for a status code. */
 const char* llmint8_status_string(llmint8_status s);

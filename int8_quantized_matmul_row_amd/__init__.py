@@ -10,6 +10,8 @@ in the library's HIP kernels):
   ``Llmint8Error`` on a non-OK status.
 * ``quantize_weight``, ``quantize_act``, ``matmul`` and ``linear``: the same
   calls on torch tensors; torch supplies device memory and the current stream.
+* ``*_fp8``: the FP8 (E4M3) variant of the same decomposition (codes as uint8
+  tensors; ``t.view(torch.float8_e4m3fn)`` gives their values).
 
 The library must be built (``python -m int8_quantized_matmul_row_amd.build``);
 there is no fallback path.
@@ -42,6 +44,13 @@ EXPORTS = (
     "llmint8_linear_workspace_size",
     "llmint8_linear",
     "llmint8_linear_profiled",
+    "llmint8_quantize_weight_fp8",
+    "llmint8_quantize_act_fp8",
+    "llmint8_matmul_fp8",
+    "llmint8_matmul_fp8_profiled",
+    "llmint8_linear_fp8_workspace_size",
+    "llmint8_linear_fp8",
+    "llmint8_linear_fp8_profiled",
     "llmint8_status_string",
     "llmint8_last_hip_error",
 )
@@ -90,9 +99,19 @@ def lib() -> ctypes.CDLL:
            ctypes.c_size_t, _P]
     L.llmint8_linear.argtypes = lin
     L.llmint8_linear_profiled.argtypes = lin + [_P, _P]
+    L.llmint8_quantize_weight_fp8.argtypes = L.llmint8_quantize_weight.argtypes
+    L.llmint8_quantize_act_fp8.argtypes = L.llmint8_quantize_act.argtypes
+    L.llmint8_matmul_fp8.argtypes = mm
+    L.llmint8_matmul_fp8_profiled.argtypes = mm + [_P, _P]
+    L.llmint8_linear_fp8_workspace_size.argtypes = [_I64, _I64, _I64]
+    L.llmint8_linear_fp8_workspace_size.restype = ctypes.c_size_t
+    L.llmint8_linear_fp8.argtypes = lin
+    L.llmint8_linear_fp8_profiled.argtypes = lin + [_P, _P]
     for f in ("llmint8_quantize_weight", "llmint8_quantize_tensor", "llmint8_quantize_act",
               "llmint8_matmul", "llmint8_matmul_profiled", "llmint8_linear",
-              "llmint8_linear_profiled"):
+              "llmint8_linear_profiled", "llmint8_quantize_weight_fp8",
+              "llmint8_quantize_act_fp8", "llmint8_matmul_fp8", "llmint8_matmul_fp8_profiled",
+              "llmint8_linear_fp8", "llmint8_linear_fp8_profiled"):
         getattr(L, f).restype = _INT
     L.llmint8_status_string.argtypes = [_INT]
     L.llmint8_status_string.restype = ctypes.c_char_p
@@ -175,6 +194,57 @@ def llmint8_linear_profiled(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, 
                                          C_i32, workspace, workspace_bytes, stream, start, stop))
 
 
+def llmint8_quantize_weight_fp8(W, dtype, N, K, CB, SCB, stream=0):
+    _check("llmint8_quantize_weight_fp8",
+           lib().llmint8_quantize_weight_fp8(W, dtype, N, K, CB, SCB, stream))
+
+
+def llmint8_quantize_act_fp8(X, dtype, M, K, threshold, CA, SCA, outlier_idx, n_outliers,
+                             X_outlier, workspace, workspace_bytes, stream=0):
+    _check("llmint8_quantize_act_fp8",
+           lib().llmint8_quantize_act_fp8(X, dtype, M, K, ctypes.c_float(threshold), CA, SCA,
+                                          outlier_idx, n_outliers, X_outlier, workspace,
+                                          workspace_bytes, stream))
+
+
+def llmint8_matmul_fp8(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB,
+                       bias, Y, C_f32, workspace, workspace_bytes, stream=0):
+    _check("llmint8_matmul_fp8",
+           lib().llmint8_matmul_fp8(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier,
+                                    CB, SCB, bias, Y, C_f32, workspace, workspace_bytes, stream))
+
+
+def llmint8_matmul_fp8_profiled(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB,
+                                SCB, bias, Y, C_f32, workspace, workspace_bytes, stream, start,
+                                stop):
+    _check("llmint8_matmul_fp8_profiled",
+           lib().llmint8_matmul_fp8_profiled(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers,
+                                             X_outlier, CB, SCB, bias, Y, C_f32, workspace,
+                                             workspace_bytes, stream, start, stop))
+
+
+def llmint8_linear_fp8_workspace_size(M, N, K) -> int:
+    return int(lib().llmint8_linear_fp8_workspace_size(M, N, K))
+
+
+def llmint8_linear_fp8(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                       n_outliers, X_outlier, C_f32, workspace, workspace_bytes, stream=0):
+    _check("llmint8_linear_fp8",
+           lib().llmint8_linear_fp8(X, dtype, M, N, K, ctypes.c_float(threshold), CB, SCB, bias,
+                                    Y, CA, SCA, outlier_idx, n_outliers, X_outlier, C_f32,
+                                    workspace, workspace_bytes, stream))
+
+
+def llmint8_linear_fp8_profiled(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA,
+                                outlier_idx, n_outliers, X_outlier, C_f32, workspace,
+                                workspace_bytes, stream, start, stop):
+    _check("llmint8_linear_fp8_profiled",
+           lib().llmint8_linear_fp8_profiled(X, dtype, M, N, K, ctypes.c_float(threshold), CB,
+                                             SCB, bias, Y, CA, SCA, outlier_idx, n_outliers,
+                                             X_outlier, C_f32, workspace, workspace_bytes,
+                                             stream, start, stop))
+
+
 def llmint8_status_string(status: int) -> str:
     return lib().llmint8_status_string(status).decode()
 
@@ -239,10 +309,11 @@ class QuantizedAct(NamedTuple):
     dtype: int
 
 
-def alloc_act(M, K, dtype_t, device):
+def alloc_act(M, K, dtype_t, device, fp8: bool = False):
+    """Output buffers of quantize_act (CA int8) or quantize_act_fp8 (CA uint8)."""
     torch = _torch()
     return QuantizedAct(
-        torch.empty((M, K), dtype=torch.int8, device=device),
+        torch.empty((M, K), dtype=torch.uint8 if fp8 else torch.int8, device=device),
         torch.empty((M,), dtype=torch.float32, device=device),
         torch.empty((K,), dtype=torch.int32, device=device),
         torch.empty((1,), dtype=torch.int32, device=device),
@@ -350,4 +421,82 @@ def linear(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None, out=None,
         llmint8_linear(*args)
     else:
         llmint8_linear_profiled(*args, events[0], events[1])
+    return Y, q
+
+
+# ---- FP8 (E4M3) variant --------------------------------------------------------
+
+def quantize_weight_fp8(W, stream=None, out=None):
+    """W [N,K] fp16/bf16 -> (CB uint8 E4M3 codes [N,K], SCB fp32 [N])."""
+    torch = _torch()
+    _need(W, "W")
+    N, K = W.shape
+    CB, SCB = out if out is not None else (
+        torch.empty((N, K), dtype=torch.uint8, device=W.device),
+        torch.empty((N,), dtype=torch.float32, device=W.device))
+    llmint8_quantize_weight_fp8(_ptr(W), dtype_code(W), N, K, _ptr(CB), _ptr(SCB),
+                                _stream(stream))
+    return CB, SCB
+
+
+def quantize_act_fp8(X, threshold: float = 6.0, stream=None, out: Optional[QuantizedAct] = None,
+                     workspace=None):
+    """X [M,K] fp16/bf16 -> QuantizedAct with CA as uint8 E4M3 codes."""
+    _need(X, "X")
+    M, K = X.shape
+    q = out if out is not None else alloc_act(M, K, X.dtype, X.device, fp8=True)
+    ws, nbytes = workspace if workspace is not None else act_workspace(M, K, X.device)
+    llmint8_quantize_act_fp8(_ptr(X), dtype_code(X), M, K, float(threshold), _ptr(q.CA),
+                             _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(ws),
+                             nbytes, _stream(stream))
+    return q
+
+
+def matmul_fp8(q: QuantizedAct, CB, SCB, bias=None, out=None, C_f32=None, stream=None,
+               workspace=None, events=None):
+    """The FP8 product Y [M,N] from quantize_act_fp8 / quantize_weight_fp8 outputs."""
+    torch = _torch()
+    M, K = q.CA.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K:
+        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
+    dt_t = torch.float16 if q.dtype == F16 else torch.bfloat16
+    Y = out if out is not None else torch.empty((M, N), dtype=dt_t, device=q.CA.device)
+    ws, nbytes = (None, 0) if workspace is None else workspace
+    args = (q.dtype, M, N, K, _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO),
+            _ptr(CB), _ptr(SCB), _ptr(bias), _ptr(Y), _ptr(C_f32), _ptr(ws), nbytes,
+            _stream(stream))
+    if events is None:
+        llmint8_matmul_fp8(*args)
+    else:
+        llmint8_matmul_fp8_profiled(*args, events[0], events[1])
+    return Y
+
+
+def linear_fp8_workspace(M, N, K, device):
+    torch = _torch()
+    n = llmint8_linear_fp8_workspace_size(M, N, K)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+
+
+def linear_fp8(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None, out=None,
+               act: Optional[QuantizedAct] = None, C_f32=None, workspace=None, events=None):
+    """Y = X . W^T through the FP8 variant in one call, W given as (CB, SCB) from
+    quantize_weight_fp8.  Returns (Y, QuantizedAct)."""
+    torch = _torch()
+    _need(X, "X")
+    M, K = X.shape
+    N = CB.shape[0]
+    if CB.shape[1] != K:
+        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
+    q = act if act is not None else alloc_act(M, K, X.dtype, X.device, fp8=True)
+    Y = out if out is not None else torch.empty((M, N), dtype=X.dtype, device=X.device)
+    ws, nbytes = workspace if workspace is not None else linear_fp8_workspace(M, N, K, X.device)
+    args = (_ptr(X), dtype_code(X), M, N, K, float(threshold), _ptr(CB), _ptr(SCB), _ptr(bias),
+            _ptr(Y), _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(C_f32),
+            _ptr(ws), nbytes, _stream(stream))
+    if events is None:
+        llmint8_linear_fp8(*args)
+    else:
+        llmint8_linear_fp8_profiled(*args, events[0], events[1])
     return Y, q

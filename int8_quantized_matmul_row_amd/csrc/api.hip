@@ -53,12 +53,13 @@ llmint8_status check_device() {
     return g_dev_ok[dev] == 1 ? LLMINT8_OK : LLMINT8_ERR_UNSUPPORTED;
 }
 
-llmint8_status matmul_impl(int dtype, int64_t M, int64_t N, int64_t K, const int8_t* CA,
-                           const float* SCA, const int32_t* outlier_idx,
+// fp8: CA / CB hold E4M3 code bytes and the product goes to C_f32 (C_i32 unused)
+llmint8_status matmul_impl(int dtype, bool fp8, int64_t M, int64_t N, int64_t K,
+                           const int8_t* CA, const float* SCA, const int32_t* outlier_idx,
                            const int32_t* n_outliers, const void* X_outlier, const int8_t* CB,
                            const float* SCB, const void* bias, void* Y, int32_t* C_i32,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t ev_start, hipEvent_t ev_stop) {
+                           float* C_f32, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     llmint8_status s = check_dtype(dtype);
     if (s != LLMINT8_OK) return s;
     if ((s = check_sizes(M, N, K)) != LLMINT8_OK) return s;
@@ -67,11 +68,13 @@ llmint8_status matmul_impl(int dtype, int64_t M, int64_t N, int64_t K, const int
         bad_ptr(X_outlier) || bad_ptr(CB) || bad_ptr(SCB) || bad_ptr(Y))
         return LLMINT8_ERR_INVALID_ARGUMENT;
     if ((bias && !aligned16(bias)) || (C_i32 && !aligned16(C_i32)) ||
-        (workspace && !aligned16(workspace)))
+        (C_f32 && !aligned16(C_f32)) || (workspace && !aligned16(workspace)))
         return LLMINT8_ERR_INVALID_ARGUMENT;
     if ((s = check_device()) != LLMINT8_OK) return s;
     llmint8::MatmulArgs a;
     a.bf16 = dtype == LLMINT8_BF16;
+    a.fp8 = fp8;
+    a.C_f32 = fp8 ? C_f32 : nullptr;
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
@@ -84,7 +87,7 @@ llmint8_status matmul_impl(int dtype, int64_t M, int64_t N, int64_t K, const int
     a.SCB = SCB;
     a.bias = static_cast<const uint16_t*>(bias);
     a.Y = static_cast<uint16_t*>(Y);
-    a.C_i32 = C_i32;
+    a.C_i32 = fp8 ? nullptr : C_i32;
     a.ws = workspace;
     a.ws_bytes = workspace ? workspace_bytes : 0;
     hipError_t e = llmint8::launch_matmul(a, stream, ev_start, ev_stop);
@@ -93,18 +96,21 @@ llmint8_status matmul_impl(int dtype, int64_t M, int64_t N, int64_t K, const int
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t linear_workspace(int64_t M, int64_t N, int64_t K) {
+// The FP8 forward has no fused small-M kernel: always quantize_act + matmul.
+size_t linear_workspace(int64_t M, int64_t N, int64_t K, bool fp8) {
     if (M == 0 || N == 0) return llmint8::quantize_act_workspace(M, K);
-    if (llmint8::linear_small_m_supported((int)M, (int)K)) return 0;
-    return align256(llmint8::quantize_act_workspace(M, K)) + llmint8::matmul_workspace(M, N, K);
+    if (!fp8 && llmint8::linear_small_m_supported((int)M, (int)K)) return 0;
+    const size_t act = llmint8::quantize_act_workspace(M, K);
+    const size_t mm = llmint8::matmul_workspace(M, N, K);
+    return mm == 0 ? act : align256(act) + mm;
 }
 
-llmint8_status linear_impl(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_t N, int64_t K,
                            float threshold, const int8_t* CB, const float* SCB, const void* bias,
                            void* Y, int8_t* CA, float* SCA, int32_t* outlier_idx,
-                           int32_t* n_outliers, void* X_outlier, int32_t* C_i32, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream, hipEvent_t ev_start,
-                           hipEvent_t ev_stop) {
+                           int32_t* n_outliers, void* X_outlier, int32_t* C_i32, float* C_f32,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           hipEvent_t ev_start, hipEvent_t ev_stop) {
     llmint8_status s = check_dtype(dtype);
     if (s != LLMINT8_OK) return s;
     if ((s = check_sizes(M, N, K)) != LLMINT8_OK) return s;
@@ -116,32 +122,34 @@ llmint8_status linear_impl(const void* X, int dtype, int64_t M, int64_t N, int64
     if (M > 0 && N > 0 && (bad_ptr(CB) || bad_ptr(SCB) || bad_ptr(Y)))
         return LLMINT8_ERR_INVALID_ARGUMENT;
     if ((bias && !aligned16(bias)) || (C_i32 && !aligned16(C_i32)) ||
-        (workspace && !aligned16(workspace)))
+        (C_f32 && !aligned16(C_f32)) || (workspace && !aligned16(workspace)))
         return LLMINT8_ERR_INVALID_ARGUMENT;
-    const size_t need = linear_workspace(M, N, K);
+    const size_t need = linear_workspace(M, N, K, fp8);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return LLMINT8_ERR_INVALID_ARGUMENT;
     if ((s = check_device()) != LLMINT8_OK) return s;
     const bool bf16 = dtype == LLMINT8_BF16;
     hipError_t e;
-    if (M > 0 && N > 0 && llmint8::linear_decode_supported((int)M, (int)K)) {
+    if (!fp8 && M > 0 && N > 0 && llmint8::linear_decode_supported((int)M, (int)K)) {
         e = llmint8::launch_linear_decode(X, bf16, (int)M, (int)N, (int)K, threshold, CB, SCB,
                                           bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,
                                           C_i32, stream, ev_start, ev_stop);
         return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
     }
-    if (M > 0 && N > 0 && llmint8::linear_small_m_supported((int)M, (int)K)) {
+    if (!fp8 && M > 0 && N > 0 && llmint8::linear_small_m_supported((int)M, (int)K)) {
         e = llmint8::launch_linear_small_m(X, bf16, (int)M, (int)N, (int)K, threshold, CB, SCB,
                                            bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,
                                            C_i32, stream, ev_start, ev_stop);
         return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
     }
-    e = llmint8::launch_quantize_act(X, bf16, (int)M, (int)K, threshold, CA, SCA, outlier_idx,
+    e = llmint8::launch_quantize_act(X, bf16, fp8, (int)M, (int)K, threshold, CA, SCA, outlier_idx,
                                      n_outliers, X_outlier, workspace, stream);
     if (e != hipSuccess) return hip_fail(e);
     if (M == 0 || N == 0) return LLMINT8_OK;
     llmint8::MatmulArgs a;
     a.bf16 = bf16;
+    a.fp8 = fp8;
+    a.C_f32 = fp8 ? C_f32 : nullptr;
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
@@ -154,7 +162,7 @@ llmint8_status linear_impl(const void* X, int dtype, int64_t M, int64_t N, int64
     a.SCB = SCB;
     a.bias = static_cast<const uint16_t*>(bias);
     a.Y = static_cast<uint16_t*>(Y);
-    a.C_i32 = C_i32;
+    a.C_i32 = fp8 ? nullptr : C_i32;
     const size_t act_ws = align256(llmint8::quantize_act_workspace(M, K));
     a.ws = workspace && workspace_bytes > act_ws ? static_cast<char*>(workspace) + act_ws : nullptr;
     a.ws_bytes = a.ws ? workspace_bytes - act_ws : 0;
@@ -176,19 +184,56 @@ hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_
 
 }  // namespace llmint8
 
-extern "C" {
+namespace {
 
-llmint8_status llmint8_quantize_weight(const void* W, int dtype, int64_t N, int64_t K, int8_t* CB,
-                                       float* SCB, hipStream_t stream) {
+llmint8_status quantize_weight_impl(const void* W, int dtype, bool fp8, int64_t N, int64_t K,
+                                   int8_t* CB, float* SCB, hipStream_t stream) {
     llmint8_status s = check_dtype(dtype);
     if (s != LLMINT8_OK) return s;
     if ((s = check_sizes(0, N, K)) != LLMINT8_OK) return s;
     if (N == 0) return LLMINT8_OK;
     if (bad_ptr(W) || bad_ptr(CB) || bad_ptr(SCB)) return LLMINT8_ERR_INVALID_ARGUMENT;
     if ((s = check_device()) != LLMINT8_OK) return s;
-    hipError_t e = llmint8::launch_quantize_weight(W, dtype == LLMINT8_BF16, (int)N, (int)K, CB,
-                                                   SCB, stream);
+    hipError_t e = llmint8::launch_quantize_weight(W, dtype == LLMINT8_BF16, fp8, (int)N, (int)K,
+                                                   CB, SCB, stream);
     return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+}
+
+llmint8_status quantize_act_impl(const void* X, int dtype, bool fp8, int64_t M, int64_t K,
+                                 float threshold, int8_t* CA, float* SCA, int32_t* outlier_idx,
+                                 int32_t* n_outliers, void* X_outlier, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    llmint8_status s = check_dtype(dtype);
+    if (s != LLMINT8_OK) return s;
+    if ((s = check_sizes(M, 0, K)) != LLMINT8_OK) return s;
+    if (threshold != threshold || threshold < 0.0f) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (bad_ptr(n_outliers)) return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (M > 0) {
+        if (bad_ptr(X) || bad_ptr(CA) || bad_ptr(SCA) || bad_ptr(outlier_idx) || bad_ptr(X_outlier))
+            return LLMINT8_ERR_INVALID_ARGUMENT;
+        const size_t need = llmint8::quantize_act_workspace(M, K);
+        if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+            return LLMINT8_ERR_INVALID_ARGUMENT;
+    }
+    if ((s = check_device()) != LLMINT8_OK) return s;
+    hipError_t e = llmint8::launch_quantize_act(X, dtype == LLMINT8_BF16, fp8, (int)M, (int)K,
+                                                threshold, CA, SCA, outlier_idx, n_outliers,
+                                                X_outlier, workspace, stream);
+    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+llmint8_status llmint8_quantize_weight(const void* W, int dtype, int64_t N, int64_t K, int8_t* CB,
+                                       float* SCB, hipStream_t stream) {
+    return quantize_weight_impl(W, dtype, false, N, K, CB, SCB, stream);
+}
+
+llmint8_status llmint8_quantize_weight_fp8(const void* W, int dtype, int64_t N, int64_t K,
+                                           uint8_t* CB, float* SCB, hipStream_t stream) {
+    return quantize_weight_impl(W, dtype, true, N, K, reinterpret_cast<int8_t*>(CB), SCB, stream);
 }
 
 size_t llmint8_quantize_tensor_workspace_size(int64_t rows, int64_t cols) {
@@ -221,23 +266,18 @@ llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t
                                     float threshold, int8_t* CA, float* SCA,
                                     int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    llmint8_status s = check_dtype(dtype);
-    if (s != LLMINT8_OK) return s;
-    if ((s = check_sizes(M, 0, K)) != LLMINT8_OK) return s;
-    if (threshold != threshold || threshold < 0.0f) return LLMINT8_ERR_INVALID_ARGUMENT;
-    if (bad_ptr(n_outliers)) return LLMINT8_ERR_INVALID_ARGUMENT;
-    if (M > 0) {
-        if (bad_ptr(X) || bad_ptr(CA) || bad_ptr(SCA) || bad_ptr(outlier_idx) || bad_ptr(X_outlier))
-            return LLMINT8_ERR_INVALID_ARGUMENT;
-        const size_t need = llmint8::quantize_act_workspace(M, K);
-        if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
-            return LLMINT8_ERR_INVALID_ARGUMENT;
-    }
-    if ((s = check_device()) != LLMINT8_OK) return s;
-    hipError_t e = llmint8::launch_quantize_act(X, dtype == LLMINT8_BF16, (int)M, (int)K, threshold,
-                                                CA, SCA, outlier_idx, n_outliers, X_outlier,
-                                                workspace, stream);
-    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
+    return quantize_act_impl(X, dtype, false, M, K, threshold, CA, SCA, outlier_idx, n_outliers,
+                             X_outlier, workspace, workspace_bytes, stream);
+}
+
+llmint8_status llmint8_quantize_act_fp8(const void* X, int dtype, int64_t M, int64_t K,
+                                        float threshold, uint8_t* CA, float* SCA,
+                                        int32_t* outlier_idx, int32_t* n_outliers,
+                                        void* X_outlier, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    return quantize_act_impl(X, dtype, true, M, K, threshold, reinterpret_cast<int8_t*>(CA), SCA,
+                             outlier_idx, n_outliers, X_outlier, workspace, workspace_bytes,
+                             stream);
 }
 
 size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K) {
@@ -250,8 +290,9 @@ llmint8_status llmint8_matmul(int dtype, int64_t M, int64_t N, int64_t K, const 
                               const int32_t* n_outliers, const void* X_outlier, const int8_t* CB,
                               const float* SCB, const void* bias, void* Y, int32_t* C_i32,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return matmul_impl(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB, bias,
-                       Y, C_i32, workspace, workspace_bytes, stream, nullptr, nullptr);
+    return matmul_impl(dtype, false, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB,
+                       bias, Y, C_i32, nullptr, workspace, workspace_bytes, stream, nullptr,
+                       nullptr);
 }
 
 llmint8_status llmint8_matmul_profiled(int dtype, int64_t M, int64_t N, int64_t K,
@@ -261,13 +302,13 @@ llmint8_status llmint8_matmul_profiled(int dtype, int64_t M, int64_t N, int64_t 
                                        const void* bias, void* Y, int32_t* C_i32,
                                        void* workspace, size_t workspace_bytes,
                                        hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    return matmul_impl(dtype, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB, bias,
-                       Y, C_i32, workspace, workspace_bytes, stream, start, stop);
+    return matmul_impl(dtype, false, M, N, K, CA, SCA, outlier_idx, n_outliers, X_outlier, CB, SCB,
+                       bias, Y, C_i32, nullptr, workspace, workspace_bytes, stream, start, stop);
 }
 
 size_t llmint8_linear_workspace_size(int64_t M, int64_t N, int64_t K) {
     if (check_sizes(M, N, K) != LLMINT8_OK) return 0;
-    return linear_workspace(M, N, K);
+    return linear_workspace(M, N, K, false);
 }
 
 llmint8_status llmint8_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
@@ -276,9 +317,9 @@ llmint8_status llmint8_linear(const void* X, int dtype, int64_t M, int64_t N, in
                               int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
                               int32_t* C_i32, void* workspace, size_t workspace_bytes,
                               hipStream_t stream) {
-    return linear_impl(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
-                       n_outliers, X_outlier, C_i32, workspace, workspace_bytes, stream, nullptr,
-                       nullptr);
+    return linear_impl(X, dtype, false, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                       n_outliers, X_outlier, C_i32, nullptr, workspace, workspace_bytes, stream,
+                       nullptr, nullptr);
 }
 
 llmint8_status llmint8_linear_profiled(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
@@ -287,9 +328,63 @@ llmint8_status llmint8_linear_profiled(const void* X, int dtype, int64_t M, int6
                                        int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
                                        int32_t* C_i32, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-    return linear_impl(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
-                       n_outliers, X_outlier, C_i32, workspace, workspace_bytes, stream, start,
-                       stop);
+    return linear_impl(X, dtype, false, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                       n_outliers, X_outlier, C_i32, nullptr, workspace, workspace_bytes, stream,
+                       start, stop);
+}
+
+llmint8_status llmint8_matmul_fp8(int dtype, int64_t M, int64_t N, int64_t K, const uint8_t* CA,
+                                  const float* SCA, const int32_t* outlier_idx,
+                                  const int32_t* n_outliers, const void* X_outlier,
+                                  const uint8_t* CB, const float* SCB, const void* bias, void* Y,
+                                  float* C_f32, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    return matmul_impl(dtype, true, M, N, K, reinterpret_cast<const int8_t*>(CA), SCA, outlier_idx,
+                       n_outliers, X_outlier, reinterpret_cast<const int8_t*>(CB), SCB, bias, Y,
+                       nullptr, C_f32, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+llmint8_status llmint8_matmul_fp8_profiled(int dtype, int64_t M, int64_t N, int64_t K,
+                                           const uint8_t* CA, const float* SCA,
+                                           const int32_t* outlier_idx,
+                                           const int32_t* n_outliers, const void* X_outlier,
+                                           const uint8_t* CB, const float* SCB, const void* bias,
+                                           void* Y, float* C_f32, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream,
+                                           hipEvent_t start, hipEvent_t stop) {
+    return matmul_impl(dtype, true, M, N, K, reinterpret_cast<const int8_t*>(CA), SCA, outlier_idx,
+                       n_outliers, X_outlier, reinterpret_cast<const int8_t*>(CB), SCB, bias, Y,
+                       nullptr, C_f32, workspace, workspace_bytes, stream, start, stop);
+}
+
+size_t llmint8_linear_fp8_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (check_sizes(M, N, K) != LLMINT8_OK) return 0;
+    return linear_workspace(M, N, K, true);
+}
+
+llmint8_status llmint8_linear_fp8(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                                  float threshold, const uint8_t* CB, const float* SCB,
+                                  const void* bias, void* Y, uint8_t* CA, float* SCA,
+                                  int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                  float* C_f32, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    return linear_impl(X, dtype, true, M, N, K, threshold, reinterpret_cast<const int8_t*>(CB), SCB,
+                       bias, Y, reinterpret_cast<int8_t*>(CA), SCA, outlier_idx, n_outliers,
+                       X_outlier, nullptr, C_f32, workspace, workspace_bytes, stream, nullptr,
+                       nullptr);
+}
+
+llmint8_status llmint8_linear_fp8_profiled(const void* X, int dtype, int64_t M, int64_t N,
+                                           int64_t K, float threshold, const uint8_t* CB,
+                                           const float* SCB, const void* bias, void* Y,
+                                           uint8_t* CA, float* SCA, int32_t* outlier_idx,
+                                           int32_t* n_outliers, void* X_outlier, float* C_f32,
+                                           void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream, hipEvent_t start,
+                                           hipEvent_t stop) {
+    return linear_impl(X, dtype, true, M, N, K, threshold, reinterpret_cast<const int8_t*>(CB), SCB,
+                       bias, Y, reinterpret_cast<int8_t*>(CA), SCA, outlier_idx, n_outliers,
+                       X_outlier, nullptr, C_f32, workspace, workspace_bytes, stream, start, stop);
 }
 
 const char* llmint8_status_string(llmint8_status s) {

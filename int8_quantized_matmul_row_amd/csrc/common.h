@@ -93,6 +93,40 @@ __device__ __forceinline__ int quantize_value(float x, float scale) {
     return (int)r;
 }
 
+// ---- FP8 E4M3 codes (the 8-bit floating-point variant) --------------------
+// The zhichai.top summary of LLM.int8() (outlook section) names an 8-bit
+// floating-point type as future work for the method.  The variant here uses
+// OCP E4M3, the format gfx950's fp8 matrix instructions take: code =
+// e4m3(x * scale), scale = 448.0f / absmax, one fp32 multiply and then
+// v_cvt_pk_fp8_f32 (round to nearest, ties to even, subnormals kept, a result
+// that rounds to zero keeps its sign).  |x * scale| <= 448 (1 + 2^-23) < 464,
+// the magnitude from which the conversion would return NaN.
+typedef long v2l __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <bool FP8>
+__device__ __forceinline__ constexpr float code_max() {
+    return FP8 ? 448.0f : 127.0f;
+}
+
+// four codes, value a in the lowest byte
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float scale) {
+#pragma clang fp contract(off)
+    const float pa = a * scale, pb = b * scale, pc = c * scale, pd = d * scale;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(pa, pb, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(pc, pd, w, true);
+    return (uint32_t)w;
+}
+
+// value of a code byte: the int8 value, or the E4M3 value (exact in fp32)
+template <bool FP8>
+__device__ __forceinline__ float code_value(int8_t b) {
+    if constexpr (FP8)
+        return __builtin_amdgcn_cvt_f32_fp8((int)(uint8_t)b, 0);
+    else
+        return (float)b;
+}
+
 // ---- cross-lane reductions and scans with DPP (no LDS round trips) --------
 // DPP controls of the gfx9 family: quad_perm, row_shr:n (0x110 + n), row_mirror
 // (0x140), row_half_mirror (0x141), row_bcast:15 (0x142), row_bcast:31 (0x143).
@@ -205,8 +239,9 @@ __device__ __forceinline__ void lds_store(void* base, uint32_t byte_off, T v) {
 }
 
 // ---- launchers (each returns hipGetLastError() after its launches) --------
-hipError_t launch_quantize_weight(const void* W, bool bf16, int N, int K, int8_t* CB, float* SCB,
-                                  hipStream_t stream);
+// fp8: E4M3 codes (scale 448/absmax) instead of int8 (127/absmax)
+hipError_t launch_quantize_weight(const void* W, bool bf16, bool fp8, int N, int K, int8_t* CB,
+                                  float* SCB, hipStream_t stream);
 
 // Per-tensor absmax quantization (one scale for the whole tensor, written to
 // every row's scale); workspace of quantize_tensor_workspace() bytes.
@@ -215,12 +250,15 @@ hipError_t launch_quantize_tensor(const void* A, bool bf16, int64_t rows, int64_
                                   float* scale, void* ws, hipStream_t stream);
 
 size_t quantize_act_workspace(int64_t M, int64_t K);
-hipError_t launch_quantize_act(const void* X, bool bf16, int M, int K, float threshold,
+hipError_t launch_quantize_act(const void* X, bool bf16, bool fp8, int M, int K, float threshold,
                                int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
                                void* ws, hipStream_t stream);
 
+// CA / CB hold int8 codes, or E4M3 code bytes when fp8 is set; the product is
+// exported to C_i32 (int8) or C_f32 (fp8, the fp32 accumulation) when given.
 struct MatmulArgs {
     bool bf16;
+    bool fp8;
     int M, N, K;
     const int8_t* CA;
     const float* SCA;
@@ -232,6 +270,7 @@ struct MatmulArgs {
     const uint16_t* bias;
     uint16_t* Y;
     int32_t* C_i32;
+    float* C_f32;
     void* ws;
     size_t ws_bytes;
 };

@@ -17,6 +17,12 @@
 // steps ahead of the MFMAs that consume them.  The per-wave partial tiles are
 // summed through LDS, then 256 threads each finish one (m, n):
 //   Y = (C * SCA[m]/127 + sum_j XO[m,j] * CB[n, idx[j]]) * SCB[n]/127 + bias[n]
+//
+// FP8 (the E4M3 variant; format in common.h): each 16-byte step feeds two
+// v_mfma_f32_16x16x32_fp8_fp8, one per 8-byte half (again the same split for
+// both operands), into fp32 accumulators; the per-wave tiles are summed in a
+// fixed order, and 127 becomes 448 in the epilogue, with CB's outlier codes
+// decoded to their E4M3 values.
 #include "common.h"
 
 namespace llmint8 {
@@ -43,13 +49,37 @@ __device__ __forceinline__ v4i mfma_steps(const v4i* a, const v4i* b, v4i acc) {
     return acc;
 }
 
-template <bool BF16, int WAVES>
+__device__ __forceinline__ v4f mfma_steps(const v4i* a, const v4i* b, v4f acc) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+        const v2l a2 = __builtin_bit_cast(v2l, a[i]), b2 = __builtin_bit_cast(v2l, b[i]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <bool FP8>
+struct SmallAcc {
+    typedef v4i vec;
+    typedef int elem;
+};
+template <>
+struct SmallAcc<true> {
+    typedef v4f vec;
+    typedef float elem;
+};
+
+template <bool BF16, bool FP8, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     int M, int N, int K, const int8_t* __restrict__ CA, const float* __restrict__ SCA,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
     const uint16_t* __restrict__ XO, const int8_t* __restrict__ CB, const float* __restrict__ SCB,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32) {
-    __shared__ int red[WAVES][4][64];
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32,
+    float* __restrict__ C_f32) {
+    typedef typename SmallAcc<FP8>::vec acc_t;
+    typedef typename SmallAcc<FP8>::elem elem_t;
+    __shared__ elem_t red[WAVES][4][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * 16;
     const int r16 = lane & 15, kg = lane >> 4;
@@ -59,7 +89,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     const int8_t* pa = CA + (size_t)(a_ok ? r16 : 0) * K + kg * 16;
     const int8_t* pb = CB + (size_t)(b_ok ? n0 + r16 : 0) * K + kg * 16;
 
-    v4i acc = {0, 0, 0, 0};
+    acc_t acc = {0, 0, 0, 0};
     v4i a0[kBatch], b0[kBatch], a1[kBatch], b1[kBatch];
     load_steps<WAVES>(pa, pb, a_ok, b_ok, wave, nsteps, a0, b0);
     for (int s = wave; s < nsteps; s += 2 * kBatch * WAVES) {
@@ -75,24 +105,28 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
 
     // element tid: accumulator register v of lane l -> row 4*(l/16) + v, column l%16
     const int v = tid >> 6, l = tid & 63;
-    int c = 0;
+    elem_t c = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) c += red[w][v][l];
     const int m = 4 * (l >> 4) + v;
     const int n = n0 + (l & 15);
     if (m >= M || n >= N) return;
-    if (C_i32) C_i32[(size_t)m * N + n] = c;
+    if constexpr (FP8) {
+        if (C_f32) C_f32[(size_t)m * N + n] = c;
+    } else {
+        if (C_i32) C_i32[(size_t)m * N + n] = c;
+    }
 
-    float y = (float)c * (SCA[m] / 127.0f);
+    float y = (float)c * (SCA[m] / code_max<FP8>());
     const int n_out = *n_out_ptr;
     if (n_out > 0) {
         const int n_pad = (n_out + 31) & ~31;
         const uint16_t* xo = XO + (size_t)m * n_pad;
         const int8_t* cb = CB + (size_t)n * K;
 #pragma unroll 4
-        for (int j = 0; j < n_out; ++j) y += widen16<BF16>(xo[j]) * (float)cb[idx[j]];
+        for (int j = 0; j < n_out; ++j) y += widen16<BF16>(xo[j]) * code_value<FP8>(cb[idx[j]]);
     }
-    y *= SCB[n] / 127.0f;
+    y *= SCB[n] / code_max<FP8>();
     if (bias) y += widen16<BF16>(bias[n]);
     Y[(size_t)m * N + n] = narrow16<BF16>(y);
 }
@@ -104,14 +138,17 @@ hipError_t launch_gemm_small_m(const MatmulArgs& a, hipStream_t stream, hipEvent
     constexpr int W = 8;
     dim3 grid((a.N + 15) / 16), block(W * 64);
     void (*fn)(int, int, int, const int8_t*, const float*, const int32_t*, const int32_t*,
-               const uint16_t*, const int8_t*, const float*, const uint16_t*, uint16_t*, int32_t*) =
-        a.bf16 ? gemm_small_m_kernel<true, W> : gemm_small_m_kernel<false, W>;
+               const uint16_t*, const int8_t*, const float*, const uint16_t*, uint16_t*, int32_t*,
+               float*) =
+        a.bf16 ? (a.fp8 ? gemm_small_m_kernel<true, true, W> : gemm_small_m_kernel<true, false, W>)
+               : (a.fp8 ? gemm_small_m_kernel<false, true, W> : gemm_small_m_kernel<false, false, W>);
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(fn, grid, block, 0, stream, ev_start, ev_stop, 0, a.M, a.N, a.K, a.CA,
-                              a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32);
+                              a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32,
+                              a.C_f32);
     } else {
         fn<<<grid, block, 0, stream>>>(a.M, a.N, a.K, a.CA, a.SCA, a.idx, a.n_out, a.XO, a.CB,
-                                       a.SCB, a.bias, a.Y, a.C_i32);
+                                       a.SCB, a.bias, a.Y, a.C_i32, a.C_f32);
     }
     return hipGetLastError();
 }

@@ -30,6 +30,15 @@
 //    idx (exact in 16-bit), into the same accumulators; then times SCB[n]/127,
 //    plus bias, rounded to 16-bit, staged in LDS and written with full 16-byte
 //    row-contiguous stores.
+//  * FP8 (the E4M3 variant; format in common.h): same tiles, ring and
+//    epilogue; one stage (64 columns) is one v_mfma_scale_f32_32x32x64_f8f6f4
+//    per block (E4M3 operands, unit scales, fp32 accumulators).  A lane's
+//    operand is its two 16-byte fragments of the stage (chunks l/32 and
+//    2 + l/32), the same for A and B, so the instruction sees one permutation
+//    of the 64 columns on both sides.  Each fragment register is refilled
+//    with stage kt+1 right after its last use in stage kt; one barrier per
+//    stage.  The epilogue divides by 448 and decodes the outlier weights'
+//    E4M3 codes (exact in fp16 and bf16).
 #include "common.h"
 
 namespace llmint8 {
@@ -78,16 +87,30 @@ __device__ __forceinline__ v16f mfma16(typename Vec16<BF16>::type a, typename Ve
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+template <bool FP8>
+struct TileAcc {
+    typedef v16i type;
+};
+template <>
+struct TileAcc<true> {
+    typedef v16f type;
+};
+
+__device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 }  // namespace
 
-template <bool BF16>
+template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const int8_t* __restrict__ CA, const float* __restrict__ SCA,
                        const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
                        const uint16_t* __restrict__ XO, const int8_t* __restrict__ CB,
                        const float* __restrict__ SCB, const uint16_t* __restrict__ bias,
-                       uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32) {
+                       uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32,
+                       float* __restrict__ C_f32) {
     __shared__ __attribute__((aligned(16))) int8_t smem[kSmemBytes];
     __shared__ float s_sb[BN], s_bias[BN];
 
@@ -131,11 +154,12 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         return *reinterpret_cast<const v4i*>(smem + rr * BKS + off);
     };
 
-    v16i acc[4][4];
+    typedef typename TileAcc<FP8>::type acc_t;
+    acc_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+        for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{};
 
     // epilogue operands, fetched now so their latency hides under the K loop
     const int n_out = *n_out_ptr;
@@ -144,7 +168,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     for (int i = 0; i < 4; ++i) sa_raw[i] = SCA[min(m0 + wm * 128 + 32 * i + (lane & 31), M - 1)];
     {
         const int n = min(n0 + tid, N - 1);
-        s_sb[tid] = SCB[n] / 127.0f;
+        s_sb[tid] = SCB[n] / code_max<FP8>();
         s_bias[tid] = bias ? widen16<BF16>(bias[n]) : 0.0f;
     }
 
@@ -160,6 +184,52 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // Fragments are read in the order of first use by the MFMA sequence below
     // (block (i, j) = step q with i = q/4, j = q%4): A0, B0..B3, A1, A2, A3.
     constexpr int kReadOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+    if constexpr (FP8) {
+        // g[2f], g[2f+1] = chunks l/32 and 2 + l/32 of fragment f.  MFMA q of a
+        // stage is block (i, j) = (q/4, q%4); each fragment is refilled with
+        // stage kt+1 right after its last use in stage kt (A block i after
+        // MFMA 4i+3, B block j after MFMA 12+j), so one set of 64 registers
+        // holds the operands and the reads overlap the MFMAs.
+        v4i g[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) g[r] = read_frag(0, r & 1, r >> 1);
+        // Stage kt+3 goes to buffer (kt-1)%4, last read (as stage kt-1) during
+        // stage kt-2; those reads were consumed by stage kt-1's MFMAs before
+        // every wave reached stage kt's barrier.
+        for (int kt = 0; kt < nk; ++kt) {
+            const bool more = kt + 1 < nk, dma = kt + 3 < nk;
+            if (more) {
+                // stage kt+1 must have landed; issued after it: stage kt+2 (8 loads, if any)
+                if (kt + 2 < nk) wait_vmcnt<8>();
+                else wait_vmcnt<0>();
+                stage_barrier();
+            }
+            const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((kt + 3) % kStages) * kStageBytes);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int i = q >> 2, j = q & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    cat8(g[2 * (4 + j)], g[2 * (4 + j) + 1]), cat8(g[2 * i], g[2 * i + 1]),
+                    acc[i][j], 0, 0, 0, 127, 0, 127);
+                if (more) {
+                    if (j == 3) {
+                        g[2 * i] = read_frag(kt + 1, 0, i);
+                        g[2 * i + 1] = read_frag(kt + 1, 1, i);
+                    }
+                    if (i == 3) {
+                        g[2 * (4 + j)] = read_frag(kt + 1, 0, 4 + j);
+                        g[2 * (4 + j) + 1] = read_frag(kt + 1, 1, 4 + j);
+                    }
+                }
+                if ((q & 1) == 0 && dma) {
+                    const int d = q >> 1;  // 0..3: A rows, 4..7: B rows
+                    if (d < 4) dma16(pa[d] + (size_t)(kt + 3) * BKS, st + 16 * d * BKS);
+                    else dma16(pb[d - 4] + (size_t)(kt + 3) * BKS, st + BM * BKS + 16 * (d - 4) * BKS);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
     v4i f0[8], f1[8];  // f[0..3] = A blocks, f[4..7] = B blocks
 #pragma unroll
     for (int r = 0; r < 8; ++r) f0[kReadOrder[r]] = read_frag(0, 0, kReadOrder[r]);
@@ -202,6 +272,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    }
 
     // ---- epilogue ----------------------------------------------------------
     // Block (i, j) is held transposed: register v of lane l is row
@@ -219,13 +290,16 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = m0 + m_lane + 32 * i;
-        if (C_i32) {
+        if (FP8 ? C_f32 != nullptr : C_i32 != nullptr) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int n = n0 + n_lane + 32 * j + 8 * (v >> 2) + (v & 3);
-                    if (m < M && n < N) C_i32[(size_t)m * N + n] = acc[i][j][v];
+                    if (m < M && n < N) {
+                        if constexpr (FP8) C_f32[(size_t)m * N + n] = acc[i][j][v];
+                        else C_i32[(size_t)m * N + n] = acc[i][j][v];
+                    }
                 }
         }
         // outlier k-block 0 operands, requested before the conversion below so
@@ -253,7 +327,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                 for (int e = 0; e < 8; ++e) wb[j][e] = cb[kc[e]];
             }
         }
-        const float sa = sa_raw[i] / 127.0f;
+        const float sa = sa_raw[i] / code_max<FP8>();
         v16f f[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -261,15 +335,15 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             for (int v = 0; v < 16; ++v) f[j][v] = (float)acc[i][j][v] * sa;
 
         if (have_out) {
-            // XO rows as the B operand (transposed product); |w| <= 127 is
-            // exact in fp16 and bf16
+            // XO rows as the B operand (transposed product); int8 codes and
+            // E4M3 values are exact in fp16 and bf16
             const vec_t xa = __builtin_bit_cast(vec_t, xraw);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 v8u16 raw;
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    raw[e] = kv[e] ? narrow16<BF16>((float)wb[j][e]) : (uint16_t)0;
+                    raw[e] = kv[e] ? narrow16<BF16>(code_value<FP8>(wb[j][e])) : (uint16_t)0;
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
@@ -288,8 +362,8 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                 const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr, N - 1) * K;
                 v8u16 raw;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)  // |w| <= 127: exact in fp16 and bf16
-                    raw[e] = kcol[e] >= 0 ? narrow16<BF16>((float)cb[kcol[e]]) : (uint16_t)0;
+                for (int e = 0; e < 8; ++e)  // exact in fp16 and bf16
+                    raw[e] = kcol[e] >= 0 ? narrow16<BF16>(code_value<FP8>(cb[kcol[e]])) : (uint16_t)0;
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
@@ -331,14 +405,16 @@ hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t
     dim3 grid(tiles_m * tiles_n), block(kThreads);
     void (*fn)(int, int, int, int, int, const int8_t*, const float*, const int32_t*,
                const int32_t*, const uint16_t*, const int8_t*, const float*, const uint16_t*,
-               uint16_t*, int32_t*) = a.bf16 ? gemm_tiled_kernel<true> : gemm_tiled_kernel<false>;
+               uint16_t*, int32_t*, float*) =
+        a.bf16 ? (a.fp8 ? gemm_tiled_kernel<true, true> : gemm_tiled_kernel<true, false>)
+               : (a.fp8 ? gemm_tiled_kernel<false, true> : gemm_tiled_kernel<false, false>);
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(fn, grid, block, 0, stream, ev_start, ev_stop, 0, a.M, a.N, a.K,
                               tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB,
-                              a.bias, a.Y, a.C_i32);
+                              a.bias, a.Y, a.C_i32, a.C_f32);
     } else {
         fn<<<grid, block, 0, stream>>>(a.M, a.N, a.K, tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out,
-                                       a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32);
+                                       a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32, a.C_f32);
     }
     return hipGetLastError();
 }

@@ -11,7 +11,8 @@
 //
 // Outputs: CA [M,K] int8 (outlier columns 0), SCA [M] fp32 (absmax over the
 // non-outlier columns), idx [n_out] ascending, n_out, XO [M, n_pad] 16-bit
-// (n_pad = round_up(n_out, 32), zero padded).
+// (n_pad = round_up(n_out, 32), zero padded).  With FP8 the codes of CA are
+// E4M3 bytes (scale 448/absmax, format in common.h; outlier columns 0x00).
 //
 // Two paths:
 //  * small M (M <= 16 and M*K <= 128K): one launch of M workgroups.  Each
@@ -41,14 +42,27 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xff) << 24);
 }
 
-// Quantize 8 values with a mask byte (set bit = outlier -> 0).
-template <bool BF16>
+// Quantize 8 values with a mask byte (set bit = outlier -> code 0).
+template <bool BF16, bool FP8>
 __device__ __forceinline__ uint2 quantize8(v8u16 v, uint32_t bits, float scale) {
-    int q[8];
+    if constexpr (FP8) {
+        uint32_t keep = 0;  // 0xff in the byte of every non-outlier value
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        q[e] = ((bits >> e) & 1u) ? 0 : quantize_value(widen16<BF16>(v[e]), scale);
-    return make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+        for (int e = 0; e < 4; ++e) keep |= ((bits >> e) & 1u) ? 0u : 0xffu << (8 * e);
+        const uint32_t keep_hi = ((bits & 0x10u) ? 0u : 0xffu) | ((bits & 0x20u) ? 0u : 0xff00u) |
+                                 ((bits & 0x40u) ? 0u : 0xff0000u) | ((bits & 0x80u) ? 0u : 0xff000000u);
+        const uint32_t lo = e4m3_pack4(widen16<BF16>(v[0]), widen16<BF16>(v[1]), widen16<BF16>(v[2]),
+                                       widen16<BF16>(v[3]), scale);
+        const uint32_t hi = e4m3_pack4(widen16<BF16>(v[4]), widen16<BF16>(v[5]), widen16<BF16>(v[6]),
+                                       widen16<BF16>(v[7]), scale);
+        return make_uint2(lo & keep, hi & keep_hi);
+    } else {
+        int q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            q[e] = ((bits >> e) & 1u) ? 0 : quantize_value(widen16<BF16>(v[e]), scale);
+        return make_uint2(pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]));
+    }
 }
 
 // Exclusive scan of one int per thread over a 256-thread block.
@@ -79,7 +93,7 @@ __device__ __forceinline__ float block_max(float v, float* lds /*[4]*/) {
 
 // ---------------------------------------------------------------------------
 // Small-M path: one workgroup per row, everything in one launch.
-template <bool BF16>
+template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) void act_quant_small(
     const uint16_t* __restrict__ X, int M, int K, float t, int8_t* __restrict__ CA,
     float* __restrict__ SCA, int32_t* __restrict__ idx, int32_t* __restrict__ n_out,
@@ -141,13 +155,13 @@ __global__ __launch_bounds__(kThreads) void act_quant_small(
     }
     amax = block_max(amax, red_lds);
     if (tid == 0) SCA[m] = amax;
-    const float scale = amax == 0.0f ? 0.0f : 127.0f / amax;
+    const float scale = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
 
     // 4. quantize the row
     int8_t* carow = CA + (size_t)m * K;
     for (int c = tid; c < nchunk; c += kThreads) {
         v8u16 v = *reinterpret_cast<const v8u16*>(xrow + (size_t)c * 8);
-        *reinterpret_cast<uint2*>(carow + (size_t)c * 8) = quantize8<BF16>(v, mask[c], scale);
+        *reinterpret_cast<uint2*>(carow + (size_t)c * 8) = quantize8<BF16, FP8>(v, mask[c], scale);
     }
 }
 
@@ -248,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void act_outlier_mask(const float* __rest
 
 // Kernel C: one wave per row.  Group offsets are rebuilt per workgroup from
 // the group counts (at most K/256 of them).
-template <bool BF16>
+template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) void act_quant_rows(
     const uint16_t* __restrict__ X, int M, int K, const uint8_t* __restrict__ mask_g,
     const int32_t* __restrict__ rank8, const int32_t* __restrict__ group_count, int n_groups,
@@ -300,14 +314,14 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
         }
         amax = wave_max(amax);
         if (lane == 0) SCA[m] = amax;
-        const float scale = amax == 0.0f ? 0.0f : 127.0f / amax;
+        const float scale = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
         int8_t* carow = CA + (size_t)m * K;
         uint16_t* xo = XO + (size_t)m * n_pad;
 #pragma unroll 4
         for (int c = lane; c < nchunk; c += kWave) {
             v8u16 v = *reinterpret_cast<const v8u16*>(xrow + (size_t)c * 8);
             uint32_t bits = mask[c];
-            *reinterpret_cast<uint2*>(carow + (size_t)c * 8) = quantize8<BF16>(v, bits, scale);
+            *reinterpret_cast<uint2*>(carow + (size_t)c * 8) = quantize8<BF16, FP8>(v, bits, scale);
             if (bits) {
                 int r = goff[c / kRankGroup] + rank8[c];
                 while (bits) {
@@ -363,9 +377,9 @@ size_t quantize_act_workspace(int64_t M, int64_t K) {
     return plan_act(M, K).bytes;
 }
 
-hipError_t launch_quantize_act(const void* Xv, bool bf16, int M, int K, float t, int8_t* CA,
-                               float* SCA, int32_t* idx, int32_t* n_out, void* XOv, void* ws,
-                               hipStream_t stream) {
+hipError_t launch_quantize_act(const void* Xv, bool bf16, bool fp8, int M, int K, float t,
+                               int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XOv,
+                               void* ws, hipStream_t stream) {
     const uint16_t* X = static_cast<const uint16_t*>(Xv);
     uint16_t* XO = static_cast<uint16_t*>(XOv);
     if (M == 0) {
@@ -374,10 +388,10 @@ hipError_t launch_quantize_act(const void* Xv, bool bf16, int M, int K, float t,
     }
     const ActPlan p = plan_act(M, K);
     if (p.small) {
-        if (bf16)
-            act_quant_small<true><<<M, kThreads, 0, stream>>>(X, M, K, t, CA, SCA, idx, n_out, XO);
-        else
-            act_quant_small<false><<<M, kThreads, 0, stream>>>(X, M, K, t, CA, SCA, idx, n_out, XO);
+        void (*fn)(const uint16_t*, int, int, float, int8_t*, float*, int32_t*, int32_t*, uint16_t*) =
+            bf16 ? (fp8 ? act_quant_small<true, true> : act_quant_small<true, false>)
+                 : (fp8 ? act_quant_small<false, true> : act_quant_small<false, false>);
+        fn<<<M, kThreads, 0, stream>>>(X, M, K, t, CA, SCA, idx, n_out, XO);
         return hipGetLastError();
     }
     char* base = static_cast<char*>(ws);
@@ -394,14 +408,12 @@ hipError_t launch_quantize_act(const void* Xv, bool bf16, int M, int K, float t,
                                                                rank8, gcount);
     int blocks = (M + 3) / 4;
     if (blocks > 65536) blocks = 65536;
-    if (bf16)
-        act_quant_rows<true><<<blocks, kThreads, 0, stream>>>(X, M, K, mask, rank8, gcount,
-                                                              p.n_rank_groups, CA, SCA, idx,
-                                                              n_out, XO);
-    else
-        act_quant_rows<false><<<blocks, kThreads, 0, stream>>>(X, M, K, mask, rank8, gcount,
-                                                               p.n_rank_groups, CA, SCA, idx,
-                                                               n_out, XO);
+    void (*fn)(const uint16_t*, int, int, const uint8_t*, const int32_t*, const int32_t*, int,
+               int8_t*, float*, int32_t*, int32_t*, uint16_t*) =
+        bf16 ? (fp8 ? act_quant_rows<true, true> : act_quant_rows<true, false>)
+             : (fp8 ? act_quant_rows<false, true> : act_quant_rows<false, false>);
+    fn<<<blocks, kThreads, 0, stream>>>(X, M, K, mask, rank8, gcount, p.n_rank_groups, CA, SCA, idx,
+                                        n_out, XO);
     return hipGetLastError();
 }
 

@@ -11,11 +11,16 @@
 // pass 1 finds the row absmax with a butterfly reduction, pass 2 re-reads the
 // row (an L2 hit) and writes 8 int8 codes per lane.  The kernel is HBM-bound:
 // 2NK bytes read once from HBM, NK + 4N written.
+//
+// FP8 = true writes E4M3 codes instead (scale 448/absmax, the 8-bit
+// floating-point variant that the zhichai.top summary of LLM.int8() lists as
+// future work; format and rounding in common.h).  A zero row has scale 0 and
+// the codes of its signed zeros.
 #include "common.h"
 
 namespace llmint8 {
 
-template <bool BF16>
+template <bool BF16, bool FP8>
 __global__ __launch_bounds__(256) void quantize_weight_kernel(const uint16_t* __restrict__ W,
                                                               int N, int K,
                                                               int8_t* __restrict__ CB,
@@ -33,33 +38,39 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const uint16_t* __
         }
         amax = wave_max(amax);
         if (lane == 0) SCB[row] = amax;
-        const float scale = amax == 0.0f ? 0.0f : 127.0f / amax;
+        const float scale = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
         int8_t* cb = CB + (size_t)row * K;
 #pragma unroll 4
         for (int c = lane; c < nchunk; c += kWave) {
             v8u16 v = *reinterpret_cast<const v8u16*>(w + (size_t)c * 8);
             uint32_t lo = 0, hi = 0;
+            if constexpr (FP8) {
+                lo = e4m3_pack4(widen16<BF16>(v[0]), widen16<BF16>(v[1]), widen16<BF16>(v[2]),
+                                widen16<BF16>(v[3]), scale);
+                hi = e4m3_pack4(widen16<BF16>(v[4]), widen16<BF16>(v[5]), widen16<BF16>(v[6]),
+                                widen16<BF16>(v[7]), scale);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lo |= (uint32_t)(quantize_value(widen16<BF16>(v[e]), scale) & 0xff) << (8 * e);
-                hi |= (uint32_t)(quantize_value(widen16<BF16>(v[e + 4]), scale) & 0xff) << (8 * e);
+                for (int e = 0; e < 4; ++e) {
+                    lo |= (uint32_t)(quantize_value(widen16<BF16>(v[e]), scale) & 0xff) << (8 * e);
+                    hi |= (uint32_t)(quantize_value(widen16<BF16>(v[e + 4]), scale) & 0xff) << (8 * e);
+                }
             }
             *reinterpret_cast<uint2*>(cb + (size_t)c * 8) = make_uint2(lo, hi);
         }
     }
 }
 
-hipError_t launch_quantize_weight(const void* W, bool bf16, int N, int K, int8_t* CB, float* SCB,
-                                  hipStream_t stream) {
+hipError_t launch_quantize_weight(const void* W, bool bf16, bool fp8, int N, int K, int8_t* CB,
+                                  float* SCB, hipStream_t stream) {
     const int rows_per_block = 4;
     long blocks = (N + rows_per_block - 1) / rows_per_block;
     if (blocks > 65536) blocks = 65536;  // grid-stride beyond this
-    if (bf16)
-        quantize_weight_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-            static_cast<const uint16_t*>(W), N, K, CB, SCB);
-    else
-        quantize_weight_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-            static_cast<const uint16_t*>(W), N, K, CB, SCB);
+    void (*fn)(const uint16_t*, int, int, int8_t*, float*) =
+        bf16 ? (fp8 ? quantize_weight_kernel<true, true> : quantize_weight_kernel<true, false>)
+             : (fp8 ? quantize_weight_kernel<false, true> : quantize_weight_kernel<false, false>);
+    fn<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(static_cast<const uint16_t*>(W), N, K, CB,
+                                                         SCB);
     return hipGetLastError();
 }
 

@@ -103,3 +103,27 @@ def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         pkg.quantize_weight(torch.zeros((4, 64), dtype=torch.float16))
+
+
+def test_fp8_entry_points_validation():
+    L = pkg.lib()
+    assert L.llmint8_quantize_weight_fp8(A, 0, 8, 100, A, A, None) == UNSUPPORTED
+    assert L.llmint8_quantize_weight_fp8(None, 0, 8, 64, A, A, None) == INVALID
+    assert L.llmint8_quantize_weight_fp8(None, 0, 0, 64, None, None, None) == OK
+    assert L.llmint8_quantize_act_fp8(A, 0, 64, 512, ctypes.c_float(float("nan")), A, A, A, A, A,
+                                      A, 1 << 30, None) == INVALID
+    assert L.llmint8_quantize_act_fp8(A, 0, 64, 512, ctypes.c_float(6.0), A, A, A, A, A, None, 0,
+                                      None) == INVALID          # workspace required
+    args = [0, 32, 64, 128, A, A, A, A, A, A, A, None, A, None, None, 0, None]
+    for i in (4, 5, 6, 7, 8, 9, 10, 12):                        # required pointers
+        bad = list(args)
+        bad[i] = None
+        assert L.llmint8_matmul_fp8(*bad) == INVALID, i
+    bad = list(args)
+    bad[13] = A + 4                                             # misaligned C_f32
+    assert L.llmint8_matmul_fp8(*bad) == INVALID
+    # the FP8 forward has no fused small-M kernel, so it needs the act workspace
+    assert pkg.llmint8_linear_fp8_workspace_size(2048, 4096, 4096) >= \
+        pkg.llmint8_quantize_act_workspace_size(2048, 4096) > 0
+    assert pkg.llmint8_linear_fp8_workspace_size(8, 4096, 4096) == 0
+    assert pkg.llmint8_linear_fp8_workspace_size(8, 4096, 100) == 0
