@@ -1,6 +1,7 @@
 """Benchmark of the LLM.int8() decomposition matmul on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode|prefill|...]
+                    [--variant int8|fp8]
 
 A step is one forward of the layer on resident inputs through llmint8_linear:
 outlier columns, row scales and int8 activations (llmint8_quantize_act's
@@ -15,6 +16,10 @@ its dispatch, and placed against its roofline: HBM bandwidth for small-M
 (decode) shapes, int8 MFMA throughput otherwise.  Distinct copies of the int8
 weight are rotated, more than 512 MiB in total, so each step streams its weight
 from HBM rather than from the 256 MiB Infinity Cache.
+
+--variant fp8 runs the FP8 (E4M3) variant of the same decomposition
+(llmint8_linear_fp8: the activation kernels, then the fp8 GEMM) and prices its
+GEMM against the dense fp8 MFMA peak or HBM.
 """
 from __future__ import annotations
 
@@ -32,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "LLM.int8 matmul effective TOPS (2MNK/s) + % of int8-MFMA / HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 ROTATE_BYTES = 512 << 20     # > 2x the Infinity Cache
 KERNEL_SOURCES = {
     "decode": ["int8_quantized_matmul_row_amd/csrc/linear_decode.hip",
@@ -49,8 +55,11 @@ KERNEL_NAMES = {"decode": "linear_decode_kernel", "fused": "linear_small_m_kerne
                 "tiled": "gemm_tiled_kernel"}
 
 
-def kernel_family(M, K):
-    """The kernel that carries the product in llmint8_linear for this shape."""
+def kernel_family(M, K, variant="int8"):
+    """The kernel that carries the product in llmint8_linear (or
+    llmint8_linear_fp8, which has no fused kernel) for this shape."""
+    if variant == "fp8":
+        return "small_m" if M <= 16 else "tiled"
     if 1 <= M <= 8 and M * K <= 32768 and K <= 8192:
         return "decode"
     if 1 <= M <= 16 and M * K <= 65536 and K <= 8192:
@@ -102,10 +111,11 @@ class Hip:
         return ms.value
 
 
-def load_traffic(config, family):
+def load_traffic(config, family, variant="int8"):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    suffix = "" if variant == "int8" else f"_{variant}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}{suffix}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -115,18 +125,20 @@ def load_traffic(config, family):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s=12.0):
+def cpu_baseline(wl, budget_s=12.0, variant="int8"):
     """The CPU oracle (single-threaded C) on a bounded sample of the same step."""
     import numpy as np
     import oracle
     orc = oracle.get()
-    CB, SCB = orc.quantize_weight(wl.W, wl.dtype)
+    fp8 = variant == "fp8"
+    CB, SCB = (orc.quantize_weight_fp8 if fp8 else orc.quantize_weight)(wl.W, wl.dtype)
+    forward = orc.forward_fp8 if fp8 else orc.forward
     M = wl.M
     if M * wl.N * wl.K <= (1 << 28):
         # whole forward, repeated
         reps, t0 = 0, time.perf_counter()
         while True:
-            orc.forward(wl.X, None, wl.dtype, wl.threshold, bias=wl.bias, weight=(CB, SCB))
+            forward(wl.X, None, wl.dtype, wl.threshold, bias=wl.bias, weight=(CB, SCB))
             reps += 1
             el = time.perf_counter() - t0
             if el >= budget_s or reps >= 1000:
@@ -135,14 +147,20 @@ def cpu_baseline(wl, budget_s=12.0):
         sample = f"full {M}x{wl.N}x{wl.K} forward (quantize_act + matmul), {reps} repetitions"
     else:
         t0 = time.perf_counter()
-        CA, SCA, idx, XO = orc.quantize_act(wl.X, wl.dtype, wl.threshold)
+        CA, SCA, idx, XO = (orc.quantize_act_fp8 if fp8 else orc.quantize_act)(
+            wl.X, wl.dtype, wl.threshold)
         t_act = time.perf_counter() - t0
         per_row = 2 * wl.N * wl.K
-        n_rows = max(2, min(M, int(budget_s * 1.0e9 / per_row)))  # ~1 GOP/s single core
+        rate = 0.2e9 if fp8 else 1.0e9  # single core, ops/s (E4M3 decode is slower)
+        n_rows = max(2, min(M, int(budget_s * rate / per_row)))
         rows = np.linspace(0, M - 1, n_rows).astype(np.int64)
         t0 = time.perf_counter()
-        C = orc.int8_rows(CA, CB, rows)
-        orc.output_rows(C, SCA, SCB, wl.X, wl.dtype, idx, CB, wl.bias, rows)
+        if fp8:
+            C = orc.fp8_rows(CA, CB, rows)
+            orc.output_rows_fp8(C, SCA, SCB, wl.X, wl.dtype, idx, CB, wl.bias, rows)
+        else:
+            C = orc.int8_rows(CA, CB, rows)
+            orc.output_rows(C, SCA, SCB, wl.X, wl.dtype, idx, CB, wl.bias, rows)
         t_rows = time.perf_counter() - t0
         step_s = t_act + t_rows * M / n_rows
         sample = (f"quantize_act on all {M} rows + matmul on {n_rows} evenly spaced rows, "
@@ -171,6 +189,8 @@ def main():
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--variant", choices=("int8", "fp8"), default="int8",
+                    help="int8 codes (the method) or the FP8 (E4M3) variant")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (steps times), "
                          "the reference kernel for scaling HBM byte counters")
@@ -204,17 +224,20 @@ def main():
     W = dev16(wl.W)
     bias = None if wl.bias is None else dev16(wl.bias)
 
+    fp8 = args.variant == "fp8"
+    quantize_w = pkg.quantize_weight_fp8 if fp8 else pkg.quantize_weight
+
     # ---- one-time weight quantization (S1), timed on its own ---------------
-    CB0 = torch.empty((N, K), dtype=torch.int8, device=dev)
+    CB0 = torch.empty((N, K), dtype=torch.uint8 if fp8 else torch.int8, device=dev)
     SCB0 = torch.empty((N,), dtype=torch.float32, device=dev)
     for _ in range(3):
-        pkg.quantize_weight(W, out=(CB0, SCB0))
+        quantize_w(W, out=(CB0, SCB0))
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 10
     e0.record()
     for _ in range(reps):
-        pkg.quantize_weight(W, out=(CB0, SCB0))
+        quantize_w(W, out=(CB0, SCB0))
     e1.record()
     torch.cuda.synchronize()
     wq_ms = e0.elapsed_time(e1) / reps
@@ -224,8 +247,10 @@ def main():
     # ---- resident buffers: rotated weight copies, activations, outputs -------
     n_copies = max(1, -(-ROTATE_BYTES // (N * K)))
     weights = [(CB0, SCB0)] + [(CB0.clone(), SCB0.clone()) for _ in range(n_copies - 1)]
-    q = pkg.alloc_act(M, K, dt_t, dev)
-    ws = pkg.linear_workspace(M, N, K, dev)
+    q = pkg.alloc_act(M, K, dt_t, dev, fp8=fp8)
+    ws = (pkg.linear_fp8_workspace if fp8 else pkg.linear_workspace)(M, N, K, dev)
+    linear_fn = pkg.llmint8_linear_fp8 if fp8 else pkg.llmint8_linear
+    linear_prof = pkg.llmint8_linear_fp8_profiled if fp8 else pkg.llmint8_linear_profiled
     Y = torch.empty((M, N), dtype=dt_t, device=dev)
     stream = torch.cuda.Stream()
     s_ptr = stream.cuda_stream
@@ -237,9 +262,9 @@ def main():
              q.SCA.data_ptr(), q.idx.data_ptr(), q.n_out.data_ptr(), q.XO.data_ptr(), None,
              ws[0].data_ptr(), ws[1], s_ptr)
         if ev is None:
-            pkg.llmint8_linear(*a)
+            linear_fn(*a)
         else:
-            pkg.llmint8_linear_profiled(*a, ev[0], ev[1])
+            linear_prof(*a, ev[0], ev[1])
 
     # ---- warmup ---------------------------------------------------------------
     with torch.cuda.stream(stream):
@@ -292,17 +317,18 @@ def main():
     ms_per_step = total_ms / steps
     tops = 2.0 * M * N * K / (ms_per_step * 1e-3) / 1e12
     k_ms = float(np.mean(kern_ms))
-    fam = kernel_family(M, K)
+    fam = kernel_family(M, K, args.variant)
     alg_bytes = algorithmic_bytes(fam, M, N, K, n_out, bias is not None)
     if fam != "tiled":
         achieved = alg_bytes / (k_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
+        peak = FP8_PEAK_TFLOPS if fp8 else INT8_PEAK_TOPS
         achieved = 2.0 * M * N * K / (k_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s", "frac": round(achieved / INT8_PEAK_TOPS, 4)}
-    roof["traffic"] = load_traffic(args.config, fam)
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s" if fp8 else "TOP/s", "frac": round(achieved / peak, 4)}
+    roof["traffic"] = load_traffic(args.config, fam, args.variant)
     roof["kernel"] = KERNEL_NAMES[fam]
     roof["kernel_ms"] = round(k_ms, 5)
     roof["algorithmic_bytes"] = alg_bytes
@@ -311,20 +337,22 @@ def main():
     result = {
         "metric": METRIC, "value": round(tops, 3), "unit": "TOPS", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "int8",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: X {synth.DTYPE_NAMES[wl.dtype]} [{M}x{K}], "
+        "config": {"workload": f"{args.config}{' (FP8 E4M3 variant)' if fp8 else ''}: "
+                               f"X {synth.DTYPE_NAMES[wl.dtype]} [{M}x{K}], "
                                f"W [{N}x{K}], threshold {wl.threshold}, {n_out} outlier columns"
                                + (", bias" if bias is not None else ""),
                    "M": M, "N": N, "K": K, "io_dtype": synth.DTYPE_NAMES[wl.dtype],
-                   "outlier_cols": n_out, "threshold": wl.threshold,
+                   "outlier_cols": n_out, "threshold": wl.threshold, "variant": args.variant,
                    "weight_copies_rotated": n_copies, "graph": graph is not None},
         "roofline": roof,
         "weight_quant_once": {"ms": round(wq_ms, 4), "GB/s": round(wq_bytes / wq_ms / 1e6, 1),
                               "frac_hbm": round(wq_bytes / wq_ms / 1e6 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, variant=args.variant)
     print(json.dumps(result), flush=True)
 
 

@@ -1,0 +1,43 @@
+"""Host-side logic of bench.py (no GPU): kernel choice per shape and variant,
+algorithmic byte counts, the single-GPU refusal, and the profile digests."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_kernel_family():
+    assert bench.kernel_family(8, 4096) == "decode"
+    assert bench.kernel_family(16, 4096) == "fused"
+    assert bench.kernel_family(16, 8192) == "small_m"
+    assert bench.kernel_family(2048, 4096) == "tiled"
+    # the FP8 forward has no fused kernel
+    assert bench.kernel_family(8, 4096, "fp8") == "small_m"
+    assert bench.kernel_family(2048, 4096, "fp8") == "tiled"
+
+
+def test_algorithmic_bytes_decode():
+    M, N, K, n_out = 8, 4096, 4096, 4
+    b = bench.algorithmic_bytes("decode", M, N, K, n_out, False)
+    # int8 weight + its scales + fp16 X in + Y out + the activation outputs
+    assert b == N * K + 4 * N + 2 * M * N + 2 * M * K + M * K + 4 * M + 2 * M * 32 + 4 * n_out + 4
+
+
+def test_refuses_several_gpus():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_profile_digests_name_their_kernel_sources():
+    prof = os.path.join(ROOT, "profiles")
+    for name in sorted(os.listdir(prof)):
+        if name.startswith("traffic_") and name.endswith(".json"):
+            with open(os.path.join(prof, name)) as f:
+                t = json.load(f)
+            assert t["kernel"] in bench.KERNEL_NAMES.values(), name
+            assert t["hbm_bytes_per_launch"] > 0 and t["algorithmic_bytes_per_launch"] > 0
