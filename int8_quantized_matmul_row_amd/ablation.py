@@ -11,7 +11,10 @@ exact reference (float64 on the host, from the same 16-bit X and W) for
     W (same page, section "inside the MatMul") -- LLM.int8() with no outlier
     columns (threshold +inf);
   * LLM.int8(): vector-wise int8 plus 16-bit outlier columns at thresholds
-    2, 4, 6 (the pages' value) and 8 (same page, section "LLM.int8() summary").
+    2, 4, 6 (the pages' value) and 8 (same page, section "LLM.int8() summary");
+  * the FP8 variant (E4M3 codes in place of int8, the 8-bit floating-point
+    type the zhichai.top summary lists as future work) at threshold 6, and
+    FP8 vector-wise (threshold +inf).
 across outlier-column densities 0, 0.1% (the density the pages report for
 large models: "LLM.int8() : Multiplication matricielle à 8 bits pour les
 Transformers à grande échelle", abstract), 1% and 5%.  Every scheme runs in
@@ -37,7 +40,7 @@ def _widen(bits, dtype):
 
 
 def run(M=256, N=2048, K=2048, densities=(0.0, 0.001, 0.01, 0.05), thresholds=(2.0, 4.0, 6.0, 8.0),
-        seed=0, device="cuda:0"):
+        seed=0, device="cuda:0", fp8=True):
     """Returns a list of dicts: density, scheme, threshold, n_out, rel_fro, max_rel."""
     if ROOT not in sys.path:
         sys.path.insert(0, ROOT)
@@ -71,6 +74,12 @@ def run(M=256, N=2048, K=2048, densities=(0.0, 0.001, 0.01, 0.05), thresholds=(2
             Y, q = pkg.linear(X, CB, SCB, threshold=t)
             name = "vector-wise" if t == float("inf") else "LLM.int8()"
             record(name, None if t == float("inf") else t, Y, int(q.n_out.item()))
+        if fp8:
+            CB8, SCB8 = pkg.quantize_weight_fp8(W)
+            for t in (float("inf"), 6.0):
+                Y, q = pkg.linear_fp8(X, CB8, SCB8, threshold=t)
+                name = "FP8 vector-wise" if t == float("inf") else "FP8 LLM.int8()"
+                record(name, None if t == float("inf") else t, Y, int(q.n_out.item()))
     return rows
 
 
