@@ -86,6 +86,16 @@ __device__ __forceinline__ uint32_t quantize_low_byte(float x, float scale) {
     return __builtin_bit_cast(uint32_t, p + 12582912.0f);
 }
 
+// The same code from a 16-bit value: fma(x, scale, +0) rounds the exact
+// product once, as the fp32 multiply of the (exactly) widened x does, in one
+// v_fma_mix_f32 that widens x itself.  A -0 product becomes +0, whose code is
+// 0 as well.
+__device__ __forceinline__ uint32_t quantize_low_byte_f16(_Float16 x, float scale) {
+#pragma clang fp contract(off)
+    const float p = __builtin_fmaf((float)x, scale, 0.0f);
+    return __builtin_bit_cast(uint32_t, p + 12582912.0f);
+}
+
 __device__ __forceinline__ int quantize_value(float x, float scale) {
     float p = x * scale;
     float r = __builtin_rintf(p);

@@ -10,17 +10,19 @@
 // (scale by 127/absmax; denormalize by the outer product of the two absmax
 // vectors), section "Usage" (recovered weight CB * SCB / 127).
 //
-// Every workgroup runs its code once, from an instruction cache that is cold
-// at each launch and refilled through an L2 that the weight stream keeps busy,
-// so the instruction bytes executed are a first-order cost here.  Hence:
+// Every workgroup (16 output channels, 8 waves) must derive the whole
+// activation quantization itself, so its latency chain sets the kernel time.
+// Measured per workgroup with in-kernel timestamps, the chain is: X arrives,
+// the activation passes run, then the MFMAs and the epilogue; the weight block
+// only has to land before the MFMAs.  Hence:
 //  * X (at most 64 KiB) goes to LDS with global_load_lds_dwordx4, 1 KiB per
-//    instruction, and every activation pass is a short loop over rows reading
-//    LDS, not unrolled code over registers;
-//  * the workgroup's NB x K weight block (NB = 16 or 32 output channels) is
-//    issued right after, into registers in the MFMA operand layout, and
-//    streams in while the activations are quantized; loads retire in issue
-//    order, so X is complete as soon as no more than the weight loads (and the
-//    two epilogue operands) are outstanding;
+//    instruction; the weight block (16 x K bytes) is issued into registers in
+//    the MFMA operand layout only once X has landed, because X's misses would
+//    otherwise queue behind the whole chip's weight requests;
+//  * each thread then reads its 8-column chunks of every row from LDS once,
+//    and the column maxima, the mask, the row maxima (two rows per packed
+//    word: four independent wave reductions), the ranks and the codes all
+//    work from those registers;
 //  * the outlier columns' weight bytes each output needs are fetched with a
 //    few byte loads as soon as the outlier list is known (they land with or
 //    after the weight block), and the outlier activations are read from LDS.
@@ -44,7 +46,6 @@ constexpr int kDecMaxRows = 8;
 constexpr int kDecXBytes = 65536;                  // M * K * 2
 constexpr int kDecCaBytes = 32896;                 // >= M * (K + 16) for M * K <= 32768
 constexpr int kDecMaxK = 8192;
-constexpr int kDecMaxChunks = kDecMaxK / 8;
 constexpr int kDecGather = 8;                      // outlier weight bytes fetched early
 
 // CPT: 8-column chunks per thread (K <= 4096 -> 1, else 2); NB: output
@@ -64,11 +65,9 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t xl[(kDecXBytes + 1024) / 2];
     __shared__ __attribute__((aligned(16))) int8_t ca[kDecCaBytes];
     __shared__ uint16_t idx_s[kDecMaxK];           // ascending outlier columns
-    __shared__ uint8_t mask[kDecMaxChunks];
-    __shared__ int chunk_rank[kDecMaxChunks + 1];  // outliers before each 8-column chunk
-    __shared__ uint32_t rmax_w[kDecWaves][kDecMaxRows];
+    __shared__ uint32_t rmax_w[kDecWaves][kDecMaxRows / 2];  // rows 2p, 2p+1 packed
     __shared__ float sca[kDecMaxRows];
-    __shared__ float scl[kDecMaxRows];             // 127 / SCA (0 for an all-zero row)
+    __shared__ __attribute__((aligned(16))) float scl[kDecMaxRows];  // 127 / SCA (0 for an all-zero row)
     __shared__ int scan_lds[kDecWaves];
     __shared__ int red[kDecWaves][4][64];
 
@@ -88,7 +87,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             dma16(xg + min(q * 1024 + lane * 16, xbytes - 16),
                   __builtin_amdgcn_readfirstlane(base + q * 1024));
     }
-    // every wave's X requests reach the memory pipeline ahead of any weight load
+    // every wave's X requests are issued before anything waits for them
     stage_barrier();
     // ---- 1b. epilogue operands: thread -> (token e_m, channel n0 + e_n) -------
     const int e_n = tid % NB, e_m = tid / NB;
@@ -98,6 +97,13 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     // raw values only: using them here would make the stream wait for them
     const float scb_raw = SCB[n_c];
     const uint16_t bias_raw = *(bias ? bias + n_c : reinterpret_cast<const uint16_t*>(SCB + n_c));
+    // X has landed once at most the two younger loads are outstanding.  The
+    // weight block is issued only now: issued earlier, its requests queue
+    // ahead of X's misses everywhere in the memory system (X then lands in
+    // ~4.8k cycles instead of ~1.8k), and it still arrives before the
+    // activation passes below are done.
+    wait_vmcnt<2>();
+    __syncthreads();
     // ---- 1c. the weight block: lane (row r16, 16-byte group kg) holds
     // CB[n0 + 16 tt + r16, 64 s + 16 kg ...] for this wave's steps s ----------
     const int tt = wave % T, grp = wave / T, r16 = lane & 15, kg = lane >> 4;
@@ -108,104 +114,117 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         const int s = min(grp * SPW + i, nsteps - 1);
         breg[i] = *reinterpret_cast<const v4i*>(pb + (size_t)s * 64);
     }
-    // X has landed once at most the SPW + 2 younger loads are outstanding
-    wait_vmcnt<SPW + 2>();
-    __syncthreads();
 
-    // ---- 2. outlier mask: column max over the M rows, one byte per 8 columns --
+    // ---- 2. this thread's 8-column chunks of every row, LDS -> registers ------
+    // (all reads issued together; rows >= M read as 0, which changes no maximum)
+    v4i xr[CPT][kDecMaxRows];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int c = tid + kDecThreads * j;
+        const uint32_t off = (uint32_t)(c < nchunk ? c : 0) * 16;
+#pragma unroll
+        for (int r = 0; r < kDecMaxRows; ++r)
+            xr[j][r] = r < M ? lds_load<v4i>(xl, (uint32_t)(r * K * 2) + off) : v4i{0, 0, 0, 0};
+    }
+
+    // ---- 3. outlier mask: column max over the M rows, 8 bits per chunk --------
     // Magnitudes are compared as 16-bit patterns (packed pairs); for finite
     // values this orders exactly like the fp32 values.
     const uint32_t tb = threshold_bits<BF16>(t);
     uint32_t mbits[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const int c = tid + kDecThreads * j;
-        const int cc = c < nchunk ? c : 0;
         uint32_t cm[4] = {0, 0, 0, 0};
-        for (int r = 0; r < M; ++r) {
-            const v4i w = *reinterpret_cast<const v4i*>(xl + (size_t)r * K + cc * 8);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cm[i] = max_u16x2(cm[i], abs2((uint32_t)w[i]));
-        }
+        for (int r = 0; r < kDecMaxRows; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cm[i] = max_u16x2(cm[i], abs2((uint32_t)xr[j][r][i]));
         uint32_t bits = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             bits |= ((cm[i] & 0xffffu) >= tb ? 1u : 0u) << (2 * i);
             bits |= ((cm[i] >> 16) >= tb ? 1u : 0u) << (2 * i + 1);
         }
-        mbits[j] = c < nchunk ? bits : 0u;
-        if (c < nchunk) mask[c] = (uint8_t)bits;
+        mbits[j] = tid + kDecThreads * j < nchunk ? bits : 0u;
     }
-    // ---- 3. row absmax over non-outlier columns (a thread's own mask bits
-    // suffice): one wave maximum per row into LDS --------------------------------
+
+    // ---- 4. row absmax over non-outlier columns: rows 2p and 2p+1 share one
+    // packed word, so four independent wave maxima cover eight rows -----------
     {
-        uint32_t keep16[CPT][4];  // 0x7fff in the 16-bit halves of non-outlier columns
+        uint32_t rm[kDecMaxRows / 2] = {0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const bool ok = tid + kDecThreads * j < nchunk;
+            const bool ok = tid + kDecThreads * j < nchunk;  // chunks past K count for nothing
+            uint32_t keep[4];  // 0x7fff in the 16-bit halves of non-outlier columns
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                keep16[j][i] = !ok ? 0u
-                                   : ((((mbits[j] >> (2 * i)) & 1u) ? 0u : 0x7fffu) |
-                                      (((mbits[j] >> (2 * i + 1)) & 1u) ? 0u : 0x7fff0000u));
-        }
-        for (int r = 0; r < M; ++r) {
-            uint32_t m2 = 0;
+                keep[i] = !ok ? 0u
+                              : ((((mbits[j] >> (2 * i)) & 1u) ? 0u : 0x7fffu) |
+                                 (((mbits[j] >> (2 * i + 1)) & 1u) ? 0u : 0x7fff0000u));
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                const int c = tid + kDecThreads * j;
-                const v4i w = *reinterpret_cast<const v4i*>(xl + (size_t)r * K + (c < nchunk ? c : 0) * 8);
+            for (int r = 0; r < kDecMaxRows; ++r) {
+                uint32_t m2 = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) m2 = max_u16x2(m2, (uint32_t)w[i] & keep16[j][i]);
+                for (int i = 0; i < 4; ++i) m2 = max_u16x2(m2, (uint32_t)xr[j][r][i] & keep[i]);
+                const uint32_t h = max(m2 & 0xffffu, m2 >> 16);
+                rm[r >> 1] = max_u16x2(rm[r >> 1], (r & 1) ? h << 16 : h);
             }
-            const uint32_t wm = wave_max_u32(max(m2 & 0xffffu, m2 >> 16));
-            if (lane == 0) rmax_w[wave][r] = wm;
+        }
+#pragma unroll
+        for (int p = 0; p < kDecMaxRows / 2; ++p) {
+            const uint32_t v = row16_max_u16x2(rm[p]);
+            const uint32_t a = __builtin_amdgcn_readlane((int)v, 0), b = __builtin_amdgcn_readlane((int)v, 16);
+            const uint32_t c = __builtin_amdgcn_readlane((int)v, 32), d = __builtin_amdgcn_readlane((int)v, 48);
+            rm[p] = max_u16x2(max_u16x2(a, b), max_u16x2(c, d));
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int p = 0; p < kDecMaxRows / 2; ++p) rmax_w[wave][p] = rm[p];
         }
     }
-    __syncthreads();  // mask and per-wave row maxima complete
 
-    // ---- 4. ranks: exclusive scan of the chunks' outlier counts; row scales ---
+    // ---- ranks: exclusive scan of the outlier counts in column order; the
+    // counts of chunk tid (low half) and chunk tid + 512 (high half) travel in
+    // one word (each total is at most K/2 < 2^16); row scales ----------------
+    int n_out;
+    int rank[CPT];
     {
-        // thread t owns chunks 2t and 2t + 1 (K/8 <= 1024)
-        const int c0 = 2 * tid;
-        const int a0 = c0 < nchunk ? __popc((uint32_t)mask[c0]) : 0;
-        const int a1 = c0 + 1 < nchunk ? __popc((uint32_t)mask[c0 + 1]) : 0;
-        const int cnt = a0 + a1;
-        const int incl = wave_incl_scan(cnt);
-        if (lane == 63) scan_lds[wave] = incl;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) cnt |= (uint32_t)__popc(mbits[j]) << (16 * j);
+        const uint32_t incl = (uint32_t)wave_incl_scan((int)cnt);
+        if (lane == 63) scan_lds[wave] = (int)incl;
+        __syncthreads();  // per-wave row maxima and scan totals complete
         if (tid < M) {
             uint32_t m = 0;
 #pragma unroll
-            for (int w = 0; w < kDecWaves; ++w) m = max(m, rmax_w[w][tid]);
+            for (int w = 0; w < kDecWaves; ++w) m = max(m, (rmax_w[w][tid >> 1] >> (16 * (tid & 1))) & 0xffffu);
             const float amax = widen16<BF16>((uint16_t)m);
             sca[tid] = amax;
             scl[tid] = amax == 0.0f ? 0.0f : 127.0f / amax;
         }
-        __syncthreads();
-        int base = 0, total = 0;
+        uint32_t base = 0, total = 0;
 #pragma unroll
         for (int w = 0; w < kDecWaves; ++w) {
-            if (w < wave) base += scan_lds[w];
-            total += scan_lds[w];
+            const uint32_t v = (uint32_t)scan_lds[w];
+            if (w < wave) base += v;
+            total += v;
         }
-        const int ex = base + incl - cnt;
-        if (c0 < nchunk) chunk_rank[c0] = ex;
-        if (c0 + 1 < nchunk) chunk_rank[c0 + 1] = ex + a0;
-        if (tid == 0) chunk_rank[nchunk] = total;
+        const uint32_t ex = base + incl - cnt;
+        const int tot0 = (int)(total & 0xffffu);
+        rank[0] = (int)(ex & 0xffffu);
+        if constexpr (CPT > 1) rank[1] = tot0 + (int)(ex >> 16);
+        n_out = tot0 + (int)(total >> 16);
     }
-    __syncthreads();
-    const int n_out = chunk_rank[nchunk];
     // the ascending outlier list
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + kDecThreads * j;
         uint32_t bits = mbits[j];
-        if (bits) {
-            int rk = chunk_rank[c];
-            while (bits) {
-                idx_s[rk++] = (uint16_t)(c * 8 + __builtin_ctz(bits));
-                bits &= bits - 1;
-            }
+        int rk = rank[j];
+        while (bits) {
+            idx_s[rk++] = (uint16_t)(c * 8 + __builtin_ctz(bits));
+            bits &= bits - 1;
         }
     }
     __syncthreads();
@@ -217,7 +236,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         for (int j = 0; j < kDecGather; ++j) cbg[j] = cbrow[j < n_out ? (int)idx_s[j] : 0];
     }
 
-    // ---- 5. int8 activations into LDS (row by row) ----------------------------
+    // ---- 5. int8 activations into LDS, from the registers ----------------------
     {
         uint32_t keep_lo[CPT], keep_hi[CPT];  // 0xff per non-outlier byte
         bool export_ca[CPT];                  // this workgroup's share of the CA output
@@ -233,28 +252,35 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             }
             export_ca[j] = (tid + kDecThreads * j) % gridDim.x == blockIdx.x;
         }
-        for (int r = 0; r < M; ++r) {
-            const float scale = scl[r];
+        const v4f sc0 = lds_load<v4f>(scl, 0), sc1 = lds_load<v4f>(scl, 16);
 #pragma unroll
-            for (int j = 0; j < CPT; ++j) {
-                const int c = tid + kDecThreads * j;
-                if (c < nchunk) {
-                    const v8u16 v = *reinterpret_cast<const v8u16*>(xl + (size_t)r * K + c * 8);
-                    // non-outlier |x| <= SCA, so |x * scale| <= 127 and the low
-                    // byte is the code; outlier columns are masked to 0
-                    uint32_t q[8];
+        for (int r = 0; r < kDecMaxRows; ++r) {
+            if (r < M) {
+                const float scale = r < 4 ? sc0[r & 3] : sc1[r & 3];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) q[e] = quantize_low_byte(widen16<BF16>(v[e]), scale);
-                    const uint32_t lo = __builtin_amdgcn_perm(
-                        __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
-                        __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
-                    const uint32_t hi = __builtin_amdgcn_perm(
-                        __builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
-                        __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
-                    const uint2 packed = make_uint2(lo & keep_lo[j], hi & keep_hi[j]);
-                    *reinterpret_cast<uint2*>(ca + r * ca_stride + c * 8) = packed;
-                    if (export_ca[j])
-                        *reinterpret_cast<uint2*>(CA_out + (size_t)r * K + c * 8) = packed;
+                for (int j = 0; j < CPT; ++j) {
+                    const int c = tid + kDecThreads * j;
+                    if (c < nchunk) {
+                        const v8u16 v = __builtin_bit_cast(v8u16, xr[j][r]);
+                        // non-outlier |x| <= SCA, so |x * scale| <= 127 and the low
+                        // byte is the code; outlier columns are masked to 0
+                        uint32_t q[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            if constexpr (BF16) q[e] = quantize_low_byte(widen16<true>(v[e]), scale);
+                            else q[e] = quantize_low_byte_f16(__builtin_bit_cast(_Float16, (uint16_t)v[e]), scale);
+                        }
+                        const uint32_t lo = __builtin_amdgcn_perm(
+                            __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
+                            __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
+                        const uint32_t hi = __builtin_amdgcn_perm(
+                            __builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
+                            __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
+                        const uint2 packed = make_uint2(lo & keep_lo[j], hi & keep_hi[j]);
+                        *reinterpret_cast<uint2*>(ca + r * ca_stride + c * 8) = packed;
+                        if (export_ca[j])
+                            *reinterpret_cast<uint2*>(CA_out + (size_t)r * K + c * 8) = packed;
+                    }
                 }
             }
         }
