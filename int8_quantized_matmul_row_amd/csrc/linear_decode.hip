@@ -49,10 +49,10 @@ constexpr int kDecMaxK = 8192;
 constexpr int kDecGather = 8;                      // outlier weight bytes fetched early
 
 // CPT: 8-column chunks per thread (K <= 4096 -> 1, else 2); NB: output
-// channels per workgroup; SPW: 64-wide K steps per wave.  Waves split as NB/16
+// channels per workgroup; SPW: 64-wide K steps per wave; FULL: M == 8.  Waves split as NB/16
 // channel tiles x 8/(NB/16) K groups: wave w takes tile w % T and the
 // contiguous steps [g * SPW, g * SPW + SPW) of group g = w / T.
-template <bool BF16, int CPT, int NB, int SPW>
+template <bool BF16, int CPT, int NB, int SPW, bool FULL>
 __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, float t,
     const int8_t* __restrict__ CB, const float* __restrict__ SCB,
@@ -105,15 +105,21 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     wait_vmcnt<2>();
     __syncthreads();
     // ---- 1c. the weight block: lane (row r16, 16-byte group kg) holds
-    // CB[n0 + 16 tt + r16, 64 s + 16 kg ...] for this wave's steps s ----------
+    // CB[n0 + 16 tt + r16, 64 s + 16 kg ...] for this wave's steps s.  It is
+    // issued in four slots spread over the register passes below: a wave that
+    // issues all of it at once stalls on the address path (~1k cycles) ahead
+    // of its own arithmetic, and the next barrier waits for the slowest wave.
     const int tt = wave % T, grp = wave / T, r16 = lane & 15, kg = lane >> 4;
     const int8_t* pb = CB + (size_t)min(n0 + tt * 16 + r16, N - 1) * K + kg * 16;
     v4i breg[SPW];
+    auto issue_weights = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < SPW; ++i) {
-        const int s = min(grp * SPW + i, nsteps - 1);
-        breg[i] = *reinterpret_cast<const v4i*>(pb + (size_t)s * 64);
-    }
+        for (int i = slot * SPW / 4; i < (slot + 1) * SPW / 4; ++i) {
+            const int s = min(grp * SPW + i, nsteps - 1);
+            breg[i] = *reinterpret_cast<const v4i*>(pb + (size_t)s * 64);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
     // ---- 2. this thread's 8-column chunks of every row, LDS -> registers ------
     // (all reads issued together; rows >= M read as 0, which changes no maximum)
@@ -126,6 +132,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         for (int r = 0; r < kDecMaxRows; ++r)
             xr[j][r] = r < M ? lds_load<v4i>(xl, (uint32_t)(r * K * 2) + off) : v4i{0, 0, 0, 0};
     }
+    issue_weights(0);
 
     // ---- 3. outlier mask: column max over the M rows, 8 bits per chunk --------
     // Magnitudes are compared as 16-bit patterns (packed pairs); for finite
@@ -147,6 +154,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         }
         mbits[j] = tid + kDecThreads * j < nchunk ? bits : 0u;
     }
+    issue_weights(1);
 
     // ---- 4. row absmax over non-outlier columns: rows 2p and 2p+1 share one
     // packed word, so four independent wave maxima cover eight rows -----------
@@ -170,6 +178,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
                 rm[r >> 1] = max_u16x2(rm[r >> 1], (r & 1) ? h << 16 : h);
             }
         }
+        issue_weights(2);
 #pragma unroll
         for (int p = 0; p < kDecMaxRows / 2; ++p) {
             const uint32_t v = row16_max_u16x2(rm[p]);
@@ -177,6 +186,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             const uint32_t c = __builtin_amdgcn_readlane((int)v, 32), d = __builtin_amdgcn_readlane((int)v, 48);
             rm[p] = max_u16x2(max_u16x2(a, b), max_u16x2(c, d));
         }
+        issue_weights(3);
         if (lane == 0) {
 #pragma unroll
             for (int p = 0; p < kDecMaxRows / 2; ++p) rmax_w[wave][p] = rm[p];
@@ -237,6 +247,9 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     }
 
     // ---- 5. int8 activations into LDS, from the registers ----------------------
+    // With all eight rows present (FULL) the rows need no test, so the compiler
+    // can interleave their independent chains; the codes stay in registers for
+    // the workgroup's share of the CA output, written after the loop.
     {
         uint32_t keep_lo[CPT], keep_hi[CPT];  // 0xff per non-outlier byte
         bool export_ca[CPT];                  // this workgroup's share of the CA output
@@ -250,38 +263,48 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
                 keep_lo[j] |= ((bits >> e) & 1u) ? 0u : (0xffu << (8 * e));
                 keep_hi[j] |= ((bits >> (e + 4)) & 1u) ? 0u : (0xffu << (8 * e));
             }
-            export_ca[j] = (tid + kDecThreads * j) % gridDim.x == blockIdx.x;
+            const int c = tid + kDecThreads * j;
+            export_ca[j] = c < nchunk && c % gridDim.x == blockIdx.x;
         }
         const v4f sc0 = lds_load<v4f>(scl, 0), sc1 = lds_load<v4f>(scl, 16);
+        v2u codes[CPT][kDecMaxRows];
 #pragma unroll
         for (int r = 0; r < kDecMaxRows; ++r) {
-            if (r < M) {
+            if (FULL || r < M) {
                 const float scale = r < 4 ? sc0[r & 3] : sc1[r & 3];
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) {
                     const int c = tid + kDecThreads * j;
-                    if (c < nchunk) {
-                        const v8u16 v = __builtin_bit_cast(v8u16, xr[j][r]);
-                        // non-outlier |x| <= SCA, so |x * scale| <= 127 and the low
-                        // byte is the code; outlier columns are masked to 0
-                        uint32_t q[8];
+                    const v8u16 v = __builtin_bit_cast(v8u16, xr[j][r]);
+                    // non-outlier |x| <= SCA, so |x * scale| <= 127 and the low
+                    // byte is the code; outlier columns are masked to 0
+                    uint32_t q[8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            if constexpr (BF16) q[e] = quantize_low_byte(widen16<true>(v[e]), scale);
-                            else q[e] = quantize_low_byte_f16(__builtin_bit_cast(_Float16, (uint16_t)v[e]), scale);
-                        }
-                        const uint32_t lo = __builtin_amdgcn_perm(
-                            __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
-                            __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
-                        const uint32_t hi = __builtin_amdgcn_perm(
-                            __builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
-                            __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
-                        const uint2 packed = make_uint2(lo & keep_lo[j], hi & keep_hi[j]);
-                        *reinterpret_cast<uint2*>(ca + r * ca_stride + c * 8) = packed;
-                        if (export_ca[j])
-                            *reinterpret_cast<uint2*>(CA_out + (size_t)r * K + c * 8) = packed;
+                    for (int e = 0; e < 8; ++e) {
+                        if constexpr (BF16) q[e] = quantize_low_byte(widen16<true>(v[e]), scale);
+                        else q[e] = quantize_low_byte_f16(__builtin_bit_cast(_Float16, (uint16_t)v[e]), scale);
                     }
+                    const uint32_t lo = __builtin_amdgcn_perm(
+                        __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
+                        __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(
+                        __builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
+                        __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
+                    codes[j][r] = v2u{lo & keep_lo[j], hi & keep_hi[j]};
+                    // a chunk past K (its registers hold chunk 0) parks its bytes in
+                    // the row's 16-byte pad, which no MFMA reads
+                    const uint32_t col = c < nchunk ? (uint32_t)c * 8 : (uint32_t)K;
+                    lds_store<v2u>(ca, (uint32_t)(r * ca_stride) + col, codes[j][r]);
                 }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            if (export_ca[j]) {
+                const int c = tid + kDecThreads * j;
+#pragma unroll
+                for (int r = 0; r < kDecMaxRows; ++r)
+                    if (FULL || r < M) *reinterpret_cast<v2u*>(CA_out + (size_t)r * K + c * 8) = codes[j][r];
             }
         }
     }
@@ -338,12 +361,12 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     Y[(size_t)e_m * N + n_e] = narrow16<BF16>(y * (scb_raw / 127.0f) + bv);
 }
 
-template <bool BF16, int CPT, int NB, int SPW>
+template <bool BF16, int CPT, int NB, int SPW, bool FULL>
 void launch_variant(hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                     const uint16_t* x, int M, int N, int K, float t, const int8_t* CB,
                     const float* SCB, const uint16_t* b, uint16_t* y, int8_t* CA, float* SCA,
                     int32_t* idx, int32_t* n_out, uint16_t* xo, int32_t* C_i32) {
-    auto fn = linear_decode_kernel<BF16, CPT, NB, SPW>;
+    auto fn = linear_decode_kernel<BF16, CPT, NB, SPW, FULL>;
     const dim3 grid((N + NB - 1) / NB);
     if (ev_start || ev_stop)
         hipExtLaunchKernelGGL(fn, grid, dim3(kDecThreads), 0, stream, ev_start, ev_stop, 0, x, M,
@@ -360,21 +383,23 @@ void launch_variant(hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
         int8_t *CA, float *SCA, int32_t *idx, int32_t *n_out, uint16_t *xo, int32_t *C_i32
 
 // steps per wave: K / 64 over the K groups, rounded up to a power of two
-template <bool BF16, int CPT, int NB>
+template <bool BF16, int CPT, int NB, bool FULL>
 void launch_steps(DEC_PARAMS) {
     constexpr int G = kDecWaves / (NB / 16);
     const int spw = (K / 64 + G - 1) / G;
-    if (spw <= 1) launch_variant<BF16, CPT, NB, 1>(DEC_ARGS);
-    else if (spw <= 2) launch_variant<BF16, CPT, NB, 2>(DEC_ARGS);
-    else if (spw <= 4) launch_variant<BF16, CPT, NB, 4>(DEC_ARGS);
-    else if (spw <= 8) launch_variant<BF16, CPT, NB, 8>(DEC_ARGS);
-    else launch_variant<BF16, CPT, NB, 16>(DEC_ARGS);
+    if (spw <= 1) launch_variant<BF16, CPT, NB, 1, FULL>(DEC_ARGS);
+    else if (spw <= 2) launch_variant<BF16, CPT, NB, 2, FULL>(DEC_ARGS);
+    else if (spw <= 4) launch_variant<BF16, CPT, NB, 4, FULL>(DEC_ARGS);
+    else if (spw <= 8) launch_variant<BF16, CPT, NB, 8, FULL>(DEC_ARGS);
+    else launch_variant<BF16, CPT, NB, 16, FULL>(DEC_ARGS);
 }
 
 template <bool BF16>
 void launch_dtype(DEC_PARAMS) {
-    if (K > 4096) launch_steps<BF16, 2, 16>(DEC_ARGS);
-    else launch_steps<BF16, 1, 16>(DEC_ARGS);
+    // K > 4096 implies M <= 4 (M * K <= 32768), so FULL needs CPT = 1
+    if (K > 4096) launch_steps<BF16, 2, 16, false>(DEC_ARGS);
+    else if (M == kDecMaxRows) launch_steps<BF16, 1, 16, true>(DEC_ARGS);
+    else launch_steps<BF16, 1, 16, false>(DEC_ARGS);
 }
 
 #undef DEC_ARGS
