@@ -35,9 +35,10 @@
 //    per block (E4M3 operands, unit scales, fp32 accumulators).  A lane's
 //    operand is its two 16-byte fragments of the stage (chunks l/32 and
 //    2 + l/32), the same for A and B, so the instruction sees one permutation
-//    of the 64 columns on both sides.  Each fragment register is refilled
-//    with stage kt+1 right after its last use in stage kt; one barrier per
-//    stage.  The epilogue divides by 448 and decodes the outlier weights'
+//    of the 64 columns on both sides.  A fragments are refilled with stage
+//    kt+1 right after their last use in stage kt; B fragments (used by every
+//    MFMA of a stage) have a second register set filled early in the stage;
+//    one barrier per stage.  The epilogue divides by 448 and decodes the outlier weights'
 //    E4M3 codes (exact in fp16 and bf16).
 #include "common.h"
 
@@ -185,18 +186,23 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // (block (i, j) = step q with i = q/4, j = q%4): A0, B0..B3, A1, A2, A3.
     constexpr int kReadOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
     if constexpr (FP8) {
-        // g[2f], g[2f+1] = chunks l/32 and 2 + l/32 of fragment f.  MFMA q of a
-        // stage is block (i, j) = (q/4, q%4); each fragment is refilled with
-        // stage kt+1 right after its last use in stage kt (A block i after
-        // MFMA 4i+3, B block j after MFMA 12+j), so one set of 64 registers
-        // holds the operands and the reads overlap the MFMAs.
-        v4i g[16];
+        // Fragment f is two 16-byte registers (chunks l/32 and 2 + l/32 of the
+        // stage).  MFMA q of a stage is block (i, j) = (q/4, q%4).  A block i is
+        // refilled with stage kt+1 in place, right after its last use (MFMA
+        // 4i+3); the B blocks, used until the stage's last MFMAs, have a second
+        // register set that takes stage kt+1 during the stage's first eight
+        // MFMAs.  Stages run in pairs so that the two B sets swap statically.
+        // u = kt % 4 is passed as a constant: with the ring slot known, every
+        // LDS offset folds into the instruction's immediate.
+        auto read_frag8 = [&](int u, int f) -> v8i {
+            return cat8(read_frag(u, 0, f), read_frag(u, 1, f));
+        };
+        v8i ga[4], gb0[4], gb1[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) g[r] = read_frag(0, r & 1, r >> 1);
-        // Stage kt+3 goes to buffer (kt-1)%4, last read (as stage kt-1) during
-        // stage kt-2; those reads were consumed by stage kt-1's MFMAs before
-        // every wave reached stage kt's barrier.
-        for (int kt = 0; kt < nk; ++kt) {
+        for (int f = 0; f < 4; ++f) ga[f] = read_frag8(0, f);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) gb0[f] = read_frag8(0, 4 + f);
+        auto stage = [&](int kt, int u, const v8i* bc, v8i* bn) {
             const bool more = kt + 1 < nk, dma = kt + 3 < nk;
             if (more) {
                 // stage kt+1 must have landed; issued after it: stage kt+2 (8 loads, if any)
@@ -204,22 +210,16 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                 else wait_vmcnt<0>();
                 stage_barrier();
             }
-            const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((kt + 3) % kStages) * kStageBytes);
+            const int un = (u + 1) & 3;
+            const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int i = q >> 2, j = q & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    cat8(g[2 * (4 + j)], g[2 * (4 + j) + 1]), cat8(g[2 * i], g[2 * i + 1]),
-                    acc[i][j], 0, 0, 0, 127, 0, 127);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bc[j], ga[i], acc[i][j], 0, 0, 0,
+                                                                            127, 0, 127);
                 if (more) {
-                    if (j == 3) {
-                        g[2 * i] = read_frag(kt + 1, 0, i);
-                        g[2 * i + 1] = read_frag(kt + 1, 1, i);
-                    }
-                    if (i == 3) {
-                        g[2 * (4 + j)] = read_frag(kt + 1, 0, 4 + j);
-                        g[2 * (4 + j) + 1] = read_frag(kt + 1, 1, 4 + j);
-                    }
+                    if (q < 4) bn[q] = read_frag8(un, 4 + q);
+                    if (j == 3) ga[i] = read_frag8(un, i);
                 }
                 if ((q & 1) == 0 && dma) {
                     const int d = q >> 1;  // 0..3: A rows, 4..7: B rows
@@ -228,6 +228,15 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        // Stage kt+3 goes to buffer (kt-1)%4, last read (as stage kt-1) during
+        // stage kt-2; those reads were consumed by stage kt-1's MFMAs before
+        // every wave reached stage kt's barrier.
+        for (int kt = 0; kt < nk; kt += 4) {
+            stage(kt, 0, gb0, gb1);
+            if (kt + 1 < nk) stage(kt + 1, 1, gb1, gb0);
+            if (kt + 2 < nk) stage(kt + 2, 2, gb0, gb1);
+            if (kt + 3 < nk) stage(kt + 3, 3, gb1, gb0);
         }
     } else {
     v4i f0[8], f1[8];  // f[0..3] = A blocks, f[4..7] = B blocks
@@ -241,15 +250,17 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // instructions per stage then never queue up at the address unit at once.
     // Stage kt+3 goes to buffer (kt+3)%4 = (kt-1)%4, whose last reads (second
     // K step of stage kt-1) happened before the previous barrier.
-    for (int kt = 0; kt < nk; ++kt) {
+    // u = kt % 4 is passed as a constant (stages unrolled by four), so every
+    // LDS offset folds into the instruction's immediate.
+    auto stage = [&](int kt, int u) {
         const bool more = kt + 1 < nk, dma = kt + 3 < nk;
-        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((kt + 3) % kStages) * kStageBytes);
+        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
         // first K step: MFMAs on f0; reads of the second K step into f1; A part of stage kt+3
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int i = q >> 2, j = q & 3;
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f0[4 + j], f0[i], acc[i][j], 0, 0, 0);
-            if (q < 8) f1[kReadOrder[q]] = read_frag(kt, 1, kReadOrder[q]);
+            if (q < 8) f1[kReadOrder[q]] = read_frag(u, 1, kReadOrder[q]);
             else if (q < 12 && dma) dma16(pa[q - 8] + (size_t)(kt + 3) * BKS, st + 16 * (q - 8) * BKS);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -267,10 +278,16 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             if (q < 4) {
                 if (dma) dma16(pb[q] + (size_t)(kt + 3) * BKS, st + BM * BKS + 16 * q * BKS);
             } else if (q >= 8 && more) {
-                f0[kReadOrder[q - 8]] = read_frag(kt + 1, 0, kReadOrder[q - 8]);
+                f0[kReadOrder[q - 8]] = read_frag((u + 1) & 3, 0, kReadOrder[q - 8]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    for (int kt = 0; kt < nk; kt += 4) {
+        stage(kt, 0);
+        if (kt + 1 < nk) stage(kt + 1, 1);
+        if (kt + 2 < nk) stage(kt + 2, 2);
+        if (kt + 3 < nk) stage(kt + 3, 3);
     }
     }
 
