@@ -173,13 +173,17 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         s_bias[tid] = bias ? widen16<BF16>(bias[n]) : 0.0f;
     }
 
+    // Every stage issues the loads of stage kt+3, clamped to the last stage:
+    // past K they re-read it into a ring buffer no wave reads again.  So each
+    // stage waits on the same load count and the unrolled loop needs no
+    // branches (a loop whose stages run conditionally made the compiler merge
+    // register versions with hundreds of copies).  All loads are awaited
+    // before the epilogue reuses the ring.
     const int nk = K / BKS;
     issue(0);
-    if (nk > 1) issue(1);
-    if (nk > 2) issue(2);
-    if (nk > 2) wait_vmcnt<16>();
-    else if (nk > 1) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
+    issue(min(1, nk - 1));
+    issue(min(2, nk - 1));
+    wait_vmcnt<16>();
     stage_barrier();
 
     // Fragments are read in the order of first use by the MFMA sequence below
@@ -202,29 +206,25 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         for (int f = 0; f < 4; ++f) ga[f] = read_frag8(0, f);
 #pragma unroll
         for (int f = 0; f < 4; ++f) gb0[f] = read_frag8(0, 4 + f);
-        auto stage = [&](int kt, int u, const v8i* bc, v8i* bn) {
-            const bool more = kt + 1 < nk, dma = kt + 3 < nk;
-            if (more) {
-                // stage kt+1 must have landed; issued after it: stage kt+2 (8 loads, if any)
-                if (kt + 2 < nk) wait_vmcnt<8>();
-                else wait_vmcnt<0>();
-                stage_barrier();
-            }
+        auto stage = [&](int kt, int u, v8i (&bc)[4], v8i (&bn)[4]) {
+            // stage kt+1 must have landed; issued after it: stage kt+2 (8 loads)
+            wait_vmcnt<8>();
+            stage_barrier();
             const int un = (u + 1) & 3;
             const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
+            const size_t kd = (size_t)min(kt + 3, nk - 1) * BKS;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int i = q >> 2, j = q & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bc[j], ga[i], acc[i][j], 0, 0, 0,
                                                                             127, 0, 127);
-                if (more) {
-                    if (q < 4) bn[q] = read_frag8(un, 4 + q);
-                    if (j == 3) ga[i] = read_frag8(un, i);
-                }
-                if ((q & 1) == 0 && dma) {
+                // (at the last stage these read a stale buffer; unused)
+                if (q < 4) bn[q] = read_frag8(un, 4 + q);
+                if (j == 3) ga[i] = read_frag8(un, i);
+                if ((q & 1) == 0) {
                     const int d = q >> 1;  // 0..3: A rows, 4..7: B rows
-                    if (d < 4) dma16(pa[d] + (size_t)(kt + 3) * BKS, st + 16 * d * BKS);
-                    else dma16(pb[d - 4] + (size_t)(kt + 3) * BKS, st + BM * BKS + 16 * (d - 4) * BKS);
+                    if (d < 4) dma16(pa[d] + kd, st + 16 * d * BKS);
+                    else dma16(pb[d - 4] + kd, st + BM * BKS + 16 * (d - 4) * BKS);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -232,11 +232,19 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         // Stage kt+3 goes to buffer (kt-1)%4, last read (as stage kt-1) during
         // stage kt-2; those reads were consumed by stage kt-1's MFMAs before
         // every wave reached stage kt's barrier.
-        for (int kt = 0; kt < nk; kt += 4) {
+        int kt = 0;
+        for (; kt + 4 <= nk; kt += 4) {
             stage(kt, 0, gb0, gb1);
-            if (kt + 1 < nk) stage(kt + 1, 1, gb1, gb0);
-            if (kt + 2 < nk) stage(kt + 2, 2, gb0, gb1);
-            if (kt + 3 < nk) stage(kt + 3, 3, gb1, gb0);
+            stage(kt + 1, 1, gb1, gb0);
+            stage(kt + 2, 2, gb0, gb1);
+            stage(kt + 3, 3, gb1, gb0);
+        }
+        if (kt < nk) {
+            stage(kt, 0, gb0, gb1);
+            if (kt + 1 < nk) {
+                stage(kt + 1, 1, gb1, gb0);
+                if (kt + 2 < nk) stage(kt + 2, 2, gb0, gb1);
+            }
         }
     } else {
     v4i f0[8], f1[8];  // f[0..3] = A blocks, f[4..7] = B blocks
@@ -253,43 +261,48 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // u = kt % 4 is passed as a constant (stages unrolled by four), so every
     // LDS offset folds into the instruction's immediate.
     auto stage = [&](int kt, int u) {
-        const bool more = kt + 1 < nk, dma = kt + 3 < nk;
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
+        const size_t kd = (size_t)min(kt + 3, nk - 1) * BKS;
         // first K step: MFMAs on f0; reads of the second K step into f1; A part of stage kt+3
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int i = q >> 2, j = q & 3;
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f0[4 + j], f0[i], acc[i][j], 0, 0, 0);
             if (q < 8) f1[kReadOrder[q]] = read_frag(u, 1, kReadOrder[q]);
-            else if (q < 12 && dma) dma16(pa[q - 8] + (size_t)(kt + 3) * BKS, st + 16 * (q - 8) * BKS);
+            else if (q < 12) dma16(pa[q - 8] + kd, st + 16 * (q - 8) * BKS);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // stage kt+1 must have landed.  Issued after it: stage kt+2 (8 loads,
-        // if any) and the A part of stage kt+3 (4, if any).
-        if (kt + 3 < nk) wait_vmcnt<12>();
-        else if (kt + 2 < nk) wait_vmcnt<8>();
-        else wait_vmcnt<0>();
+        // stage kt+1 must have landed.  Issued after it: stage kt+2 (8 loads)
+        // and the A part of stage kt+3 (4).
+        wait_vmcnt<12>();
         stage_barrier();  // stage kt+1 visible to every wave
-        // second K step: MFMAs on f1; B part of stage kt+3; reads of stage kt+1 into f0
+        // second K step: MFMAs on f1; B part of stage kt+3; reads of stage kt+1
+        // into f0 (at the last stage a stale buffer; unused)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int i = q >> 2, j = q & 3;
             acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1[4 + j], f1[i], acc[i][j], 0, 0, 0);
-            if (q < 4) {
-                if (dma) dma16(pb[q] + (size_t)(kt + 3) * BKS, st + BM * BKS + 16 * q * BKS);
-            } else if (q >= 8 && more) {
-                f0[kReadOrder[q - 8]] = read_frag((u + 1) & 3, 0, kReadOrder[q - 8]);
-            }
+            if (q < 4) dma16(pb[q] + kd, st + BM * BKS + 16 * q * BKS);
+            else if (q >= 8) f0[kReadOrder[q - 8]] = read_frag((u + 1) & 3, 0, kReadOrder[q - 8]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    for (int kt = 0; kt < nk; kt += 4) {
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
         stage(kt, 0);
-        if (kt + 1 < nk) stage(kt + 1, 1);
-        if (kt + 2 < nk) stage(kt + 2, 2);
-        if (kt + 3 < nk) stage(kt + 3, 3);
+        stage(kt + 1, 1);
+        stage(kt + 2, 2);
+        stage(kt + 3, 3);
+    }
+    if (kt < nk) {
+        stage(kt, 0);
+        if (kt + 1 < nk) {
+            stage(kt + 1, 1);
+            if (kt + 2 < nk) stage(kt + 2, 2);
+        }
     }
     }
+    wait_vmcnt<0>();  // the clamped loads past K have landed too
 
     // ---- epilogue ----------------------------------------------------------
     // Block (i, j) is held transposed: register v of lane l is row
