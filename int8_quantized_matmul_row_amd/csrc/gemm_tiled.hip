@@ -1,4 +1,4 @@
-// Tiled LLM.int8() product for prefill shapes, bound by int8 MFMA throughput.
+// Tiled LLM.int8() product for prefill shapes, bound by MFMA throughput.
 //
 // "A Gentle Introduction to 8-bit Matrix Multiplication for transformers at
 // scale": section "LLM.int8() summary" (non-outliers in int8, outliers in
@@ -9,8 +9,8 @@
 //
 // Design (gfx950: 256 CUs in 8 XCDs, 160 KiB LDS per CU, 64 LDS banks):
 //  * Workgroup tile 256 x 256; 4 waves in a 2 x 2 grid, each wave owns a
-//    128 x 128 sub-tile = 4 x 4 v_mfma_i32_32x32x32_i8 blocks (256 int32
-//    accumulators per lane, in AGPRs).  One workgroup per CU.
+//    128 x 128 sub-tile = 4 x 4 blocks of 32 x 32 (256 accumulators per lane,
+//    in AGPRs).  One workgroup per CU.
 //  * K advances in 64-byte stages through a 4-deep ring of LDS buffers
 //    (A 256 x 64 + B 256 x 64 bytes each, 128 KiB in all).  Stages are filled
 //    by global_load_lds_dwordx4: each wave instruction moves 16 rows x 64 bytes
@@ -19,27 +19,28 @@
 //  * LDS rows are 64 bytes; 16-byte chunk c of row r sits in slot c ^ ((r>>2)&3),
 //    so a 16-lane phase of 16-byte fragment reads (16 consecutive rows, one
 //    chunk) touches all 64 banks once.
-//  * The fragments of the next K step are read while the MFMAs of the current
-//    one run; the stage barrier sits between the two MFMA halves of a stage.
+//  * A lane's operand for a block and stage is 32 bytes: chunks l/32 and
+//    2 + l/32 of its row, the same for both operands.  int8: two
+//    v_mfma_i32_32x32x32_i8 (the low halves are the stage's first 32 columns,
+//    the high halves the second 32).  FP8 (the E4M3 variant; format in
+//    common.h): one v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, unit
+//    scales), which sees one permutation of the 64 columns on both sides.
+//  * The A blocks are refilled with the next stage right after their last use
+//    in the current one; the B blocks (used by every MFMA of a stage) have a
+//    second register set filled early in the stage.  Loads, reads and MFMAs
+//    are interleaved in a fixed order (sched_barrier), and the loop has no
+//    branches: stages run in groups of four with constant ring slots, and
+//    loads past K are clamped.
 //  * Tile order: blocks are dispatched round-robin over the 8 XCDs; block b is
 //    remapped so that each XCD walks a contiguous range of a grouped raster
 //    (8 tile rows per group) and its tiles share CA/CB panels in its own L2.
-//  * Epilogue, fused: int32 -> fp32 times SCA[m]/127; the outlier columns
-//    (n_out read from device memory, no host sync) run as
-//    v_mfma_f32_32x32x16_{f16,bf16} of XO against the int8 weights gathered at
-//    idx (exact in 16-bit), into the same accumulators; then times SCB[n]/127,
-//    plus bias, rounded to 16-bit, staged in LDS and written with full 16-byte
-//    row-contiguous stores.
-//  * FP8 (the E4M3 variant; format in common.h): same tiles, ring and
-//    epilogue; one stage (64 columns) is one v_mfma_scale_f32_32x32x64_f8f6f4
-//    per block (E4M3 operands, unit scales, fp32 accumulators).  A lane's
-//    operand is its two 16-byte fragments of the stage (chunks l/32 and
-//    2 + l/32), the same for A and B, so the instruction sees one permutation
-//    of the 64 columns on both sides.  A fragments are refilled with stage
-//    kt+1 right after their last use in stage kt; B fragments (used by every
-//    MFMA of a stage) have a second register set filled early in the stage;
-//    one barrier per stage.  The epilogue divides by 448 and decodes the outlier weights'
-//    E4M3 codes (exact in fp16 and bf16).
+//  * Epilogue, fused: accumulators -> fp32 times SCA[m]/127 (FP8: /448); the
+//    outlier columns (n_out read from device memory, no host sync) run as
+//    v_mfma_f32_32x32x16_{f16,bf16} of XO against the codes of the weights
+//    gathered at idx (int8 values and E4M3 values are exact in 16-bit), into
+//    the same accumulators; then times SCB[n]/127 (/448), plus bias, rounded
+//    to 16-bit, staged in LDS and written with full 16-byte row-contiguous
+//    stores.
 #include "common.h"
 
 namespace llmint8 {
@@ -186,121 +187,75 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     wait_vmcnt<16>();
     stage_barrier();
 
-    // Fragments are read in the order of first use by the MFMA sequence below
-    // (block (i, j) = step q with i = q/4, j = q%4): A0, B0..B3, A1, A2, A3.
-    constexpr int kReadOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
-    if constexpr (FP8) {
-        // Fragment f is two 16-byte registers (chunks l/32 and 2 + l/32 of the
-        // stage).  MFMA q of a stage is block (i, j) = (q/4, q%4).  A block i is
-        // refilled with stage kt+1 in place, right after its last use (MFMA
-        // 4i+3); the B blocks, used until the stage's last MFMAs, have a second
-        // register set that takes stage kt+1 during the stage's first eight
-        // MFMAs.  Stages run in pairs so that the two B sets swap statically.
-        // u = kt % 4 is passed as a constant: with the ring slot known, every
-        // LDS offset folds into the instruction's immediate.
-        auto read_frag8 = [&](int u, int f) -> v8i {
-            return cat8(read_frag(u, 0, f), read_frag(u, 1, f));
-        };
-        v8i ga[4], gb0[4], gb1[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) ga[f] = read_frag8(0, f);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) gb0[f] = read_frag8(0, 4 + f);
-        auto stage = [&](int kt, int u, v8i (&bc)[4], v8i (&bn)[4]) {
-            // stage kt+1 must have landed; issued after it: stage kt+2 (8 loads)
-            wait_vmcnt<8>();
-            stage_barrier();
-            const int un = (u + 1) & 3;
-            const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
-            const size_t kd = (size_t)min(kt + 3, nk - 1) * BKS;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int i = q >> 2, j = q & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bc[j], ga[i], acc[i][j], 0, 0, 0,
-                                                                            127, 0, 127);
-                // (at the last stage these read a stale buffer; unused)
-                if (q < 4) bn[q] = read_frag8(un, 4 + q);
-                if (j == 3) ga[i] = read_frag8(un, i);
-                if ((q & 1) == 0) {
-                    const int d = q >> 1;  // 0..3: A rows, 4..7: B rows
-                    if (d < 4) dma16(pa[d] + kd, st + 16 * d * BKS);
-                    else dma16(pb[d - 4] + kd, st + BM * BKS + 16 * (d - 4) * BKS);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        // Stage kt+3 goes to buffer (kt-1)%4, last read (as stage kt-1) during
-        // stage kt-2; those reads were consumed by stage kt-1's MFMAs before
-        // every wave reached stage kt's barrier.
-        int kt = 0;
-        for (; kt + 4 <= nk; kt += 4) {
-            stage(kt, 0, gb0, gb1);
-            stage(kt + 1, 1, gb1, gb0);
-            stage(kt + 2, 2, gb0, gb1);
-            stage(kt + 3, 3, gb1, gb0);
+    // Fragment f (A block f < 4, B block f - 4) of a stage is 32 bytes per
+    // lane: chunks l/32 and 2 + l/32 of its row, the same for A and B.  FP8:
+    // one v_mfma_scale_f32_32x32x64_f8f6f4 per block and stage (the
+    // instruction sees one permutation of the 64 columns on both sides).
+    // int8: two v_mfma_i32_32x32x32_i8, on the low halves (the stage's first
+    // 32 columns) and on the high halves (the second 32).
+    auto mma = [&](const v8i& b, const v8i& a, acc_t c) -> acc_t {
+        if constexpr (FP8) {
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
+        } else {
+            c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_shufflevector(b, b, 0, 1, 2, 3),
+                                                       __builtin_shufflevector(a, a, 0, 1, 2, 3), c, 0, 0, 0);
+            return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_shufflevector(b, b, 4, 5, 6, 7),
+                                                          __builtin_shufflevector(a, a, 4, 5, 6, 7), c, 0, 0, 0);
         }
-        if (kt < nk) {
-            stage(kt, 0, gb0, gb1);
-            if (kt + 1 < nk) {
-                stage(kt + 1, 1, gb1, gb0);
-                if (kt + 2 < nk) stage(kt + 2, 2, gb0, gb1);
-            }
-        }
-    } else {
-    v4i f0[8], f1[8];  // f[0..3] = A blocks, f[4..7] = B blocks
+    };
+    // Stage pipeline: MFMA q of a stage is block (i, j) = (q/4, q%4).  A block
+    // i is refilled with stage kt+1 in place right after its last use (MFMA
+    // 4i+3); the B blocks, used until the stage's last MFMAs, have a second
+    // register set that takes stage kt+1 during the stage's first four MFMAs.
+    // Stages run in groups of four, so that the two B sets swap statically and
+    // the ring slot u = kt % 4 is a constant (every LDS offset folds into the
+    // instruction's immediate).  The order is pinned with sched_barrier.
+    auto read_frag8 = [&](int u, int f) -> v8i {
+        return cat8(read_frag(u, 0, f), read_frag(u, 1, f));
+    };
+    v8i ga[4], gb0[4], gb1[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) f0[kReadOrder[r]] = read_frag(0, 0, kReadOrder[r]);
-
-    // One stage = 2 K steps x 16 MFMAs per wave.  The order is pinned with
-    // sched_barrier so that every MFMA is followed by at most one LDS read or
-    // one LDS-DMA issue, and the loads of stage kt+3 are split over both halves
-    // (A rows in the first, B rows in the second): the four waves' 32 DMA
-    // instructions per stage then never queue up at the address unit at once.
-    // Stage kt+3 goes to buffer (kt+3)%4 = (kt-1)%4, whose last reads (second
-    // K step of stage kt-1) happened before the previous barrier.
-    // u = kt % 4 is passed as a constant (stages unrolled by four), so every
-    // LDS offset folds into the instruction's immediate.
-    auto stage = [&](int kt, int u) {
+    for (int f = 0; f < 4; ++f) ga[f] = read_frag8(0, f);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) gb0[f] = read_frag8(0, 4 + f);
+    auto stage = [&](int kt, int u, v8i (&bc)[4], v8i (&bn)[4]) {
+        // stage kt+1 must have landed; issued after it: stage kt+2 (8 loads)
+        wait_vmcnt<8>();
+        stage_barrier();
+        const int un = (u + 1) & 3;
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
         const size_t kd = (size_t)min(kt + 3, nk - 1) * BKS;
-        // first K step: MFMAs on f0; reads of the second K step into f1; A part of stage kt+3
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int i = q >> 2, j = q & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f0[4 + j], f0[i], acc[i][j], 0, 0, 0);
-            if (q < 8) f1[kReadOrder[q]] = read_frag(u, 1, kReadOrder[q]);
-            else if (q < 12) dma16(pa[q - 8] + kd, st + 16 * (q - 8) * BKS);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // stage kt+1 must have landed.  Issued after it: stage kt+2 (8 loads)
-        // and the A part of stage kt+3 (4).
-        wait_vmcnt<12>();
-        stage_barrier();  // stage kt+1 visible to every wave
-        // second K step: MFMAs on f1; B part of stage kt+3; reads of stage kt+1
-        // into f0 (at the last stage a stale buffer; unused)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int i = q >> 2, j = q & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1[4 + j], f1[i], acc[i][j], 0, 0, 0);
-            if (q < 4) dma16(pb[q] + kd, st + BM * BKS + 16 * q * BKS);
-            else if (q >= 8) f0[kReadOrder[q - 8]] = read_frag((u + 1) & 3, 0, kReadOrder[q - 8]);
+            acc[i][j] = mma(bc[j], ga[i], acc[i][j]);
+            // (at the last stage these read a stale buffer; unused)
+            if (q < 4) bn[q] = read_frag8(un, 4 + q);
+            if (j == 3) ga[i] = read_frag8(un, i);
+            if ((q & 1) == 0) {
+                const int d = q >> 1;  // 0..3: A rows, 4..7: B rows
+                if (d < 4) dma16(pa[d] + kd, st + 16 * d * BKS);
+                else dma16(pb[d - 4] + kd, st + BM * BKS + 16 * (d - 4) * BKS);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // Stage kt+3 goes to buffer (kt-1)%4, last read (as stage kt-1) during
+    // stage kt-2; those reads were consumed by stage kt-1's MFMAs before every
+    // wave reached stage kt's barrier.
     int kt = 0;
     for (; kt + 4 <= nk; kt += 4) {
-        stage(kt, 0);
-        stage(kt + 1, 1);
-        stage(kt + 2, 2);
-        stage(kt + 3, 3);
+        stage(kt, 0, gb0, gb1);
+        stage(kt + 1, 1, gb1, gb0);
+        stage(kt + 2, 2, gb0, gb1);
+        stage(kt + 3, 3, gb1, gb0);
     }
     if (kt < nk) {
-        stage(kt, 0);
+        stage(kt, 0, gb0, gb1);
         if (kt + 1 < nk) {
-            stage(kt + 1, 1);
-            if (kt + 2 < nk) stage(kt + 2, 2);
+            stage(kt + 1, 1, gb1, gb0);
+            if (kt + 2 < nk) stage(kt + 2, 2, gb0, gb1);
         }
-    }
     }
     wait_vmcnt<0>();  // the clamped loads past K have landed too
 
