@@ -57,11 +57,12 @@ KERNEL_NAMES = {"decode": "linear_decode_kernel", "fused": "linear_small_m_kerne
 
 def kernel_family(M, K, variant="int8"):
     """The kernel that carries the product in llmint8_linear (or
-    llmint8_linear_fp8, which has no fused kernel) for this shape."""
-    if variant == "fp8":
-        return "small_m" if M <= 16 else "tiled"
+    llmint8_linear_fp8, which has the fused decode kernel but not the other
+    fused small-M one) for this shape."""
     if 1 <= M <= 8 and M * K <= 32768 and K <= 8192:
         return "decode"
+    if variant == "fp8":
+        return "small_m" if M <= 16 else "tiled"
     if 1 <= M <= 16 and M * K <= 65536 and K <= 8192:
         return "fused"
     return "small_m" if M <= 16 else "tiled"

@@ -96,9 +96,11 @@ llmint8_status matmul_impl(int dtype, bool fp8, int64_t M, int64_t N, int64_t K,
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The FP8 forward has no fused small-M kernel: always quantize_act + matmul.
+// The FP8 forward has the fused decode kernel (M <= 8) but not the other
+// fused small-M kernel.
 size_t linear_workspace(int64_t M, int64_t N, int64_t K, bool fp8) {
     if (M == 0 || N == 0) return llmint8::quantize_act_workspace(M, K);
+    if (llmint8::linear_decode_supported((int)M, (int)K)) return 0;
     if (!fp8 && llmint8::linear_small_m_supported((int)M, (int)K)) return 0;
     const size_t act = llmint8::quantize_act_workspace(M, K);
     const size_t mm = llmint8::matmul_workspace(M, N, K);
@@ -130,10 +132,11 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
     if ((s = check_device()) != LLMINT8_OK) return s;
     const bool bf16 = dtype == LLMINT8_BF16;
     hipError_t e;
-    if (!fp8 && M > 0 && N > 0 && llmint8::linear_decode_supported((int)M, (int)K)) {
-        e = llmint8::launch_linear_decode(X, bf16, (int)M, (int)N, (int)K, threshold, CB, SCB,
+    if (M > 0 && N > 0 && llmint8::linear_decode_supported((int)M, (int)K)) {
+        e = llmint8::launch_linear_decode(X, bf16, fp8, (int)M, (int)N, (int)K, threshold, CB, SCB,
                                           bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,
-                                          C_i32, stream, ev_start, ev_stop);
+                                          fp8 ? nullptr : C_i32, fp8 ? C_f32 : nullptr, stream,
+                                          ev_start, ev_stop);
         return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
     }
     if (!fp8 && M > 0 && N > 0 && llmint8::linear_small_m_supported((int)M, (int)K)) {

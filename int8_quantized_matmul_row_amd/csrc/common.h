@@ -297,14 +297,15 @@ hipError_t launch_linear_small_m(const void* X, bool bf16, int M, int N, int K, 
                                  int32_t* C_i32, hipStream_t stream, hipEvent_t ev_start,
                                  hipEvent_t ev_stop);
 
-// Fused one-launch forward for decode batches (M <= 8, M*K <= 32768): compact
-// code, activations staged in LDS.  Preferred over launch_linear_small_m.
+// Fused one-launch forward for decode batches (M <= 8, M*K <= 32768), int8
+// or FP8 codes (the product to C_i32 or C_f32).  Preferred over
+// launch_linear_small_m.
 bool linear_decode_supported(int M, int K);
-hipError_t launch_linear_decode(const void* X, bool bf16, int M, int N, int K, float t,
+hipError_t launch_linear_decode(const void* X, bool bf16, bool fp8, int M, int N, int K, float t,
                                 const int8_t* CB, const float* SCB, const void* bias, void* Y,
                                 int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
-                                int32_t* C_i32, hipStream_t stream, hipEvent_t ev_start,
-                                hipEvent_t ev_stop);
+                                int32_t* C_i32, float* C_f32, hipStream_t stream,
+                                hipEvent_t ev_start, hipEvent_t ev_stop);
 
 // Kernel families used by launch_matmul.
 constexpr int kSmallM = 16;  // M <= kSmallM takes the streaming kernel

@@ -48,18 +48,19 @@ constexpr int kDecCaBytes = 32896;                 // >= M * (K + 16) for M * K 
 constexpr int kDecMaxK = 8192;
 constexpr int kDecGather = 8;                      // outlier weight bytes fetched early
 
-// CPT: 8-column chunks per thread (K <= 4096 -> 1, else 2); NB: output
-// channels per workgroup; SPW: 64-wide K steps per wave; FULL: M == 8.  Waves split as NB/16
+// FP8: E4M3 codes (the 8-bit floating-point variant; format in common.h)
+// instead of int8.  CPT: 8-column chunks per thread (K <= 4096 -> 1, else 2);
+// NB: output channels per workgroup; SPW: 64-wide K steps per wave; FULL: M == 8.  Waves split as NB/16
 // channel tiles x 8/(NB/16) K groups: wave w takes tile w % T and the
 // contiguous steps [g * SPW, g * SPW + SPW) of group g = w / T.
-template <bool BF16, int CPT, int NB, int SPW, bool FULL>
+template <bool BF16, bool FP8, int CPT, int NB, int SPW, bool FULL>
 __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     const uint16_t* __restrict__ X, int M, int N, int K, float t,
     const int8_t* __restrict__ CB, const float* __restrict__ SCB,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
     int8_t* __restrict__ CA_out, float* __restrict__ SCA_out, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ n_out_out, uint16_t* __restrict__ XO_out,
-    int32_t* __restrict__ C_i32) {
+    int32_t* __restrict__ C_i32, float* __restrict__ C_f32) {
     constexpr int T = NB / 16;
     constexpr int G = kDecWaves / T;
     __shared__ __attribute__((aligned(16))) uint16_t xl[(kDecXBytes + 1024) / 2];
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     __shared__ float sca[kDecMaxRows];
     __shared__ __attribute__((aligned(16))) float scl[kDecMaxRows];  // 127 / SCA (0 for an all-zero row)
     __shared__ int scan_lds[kDecWaves];
-    __shared__ int red[kDecWaves][4][64];
+    __shared__ int red[kDecWaves][4][64];          // int32 partial tiles, or fp32 bit patterns
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * NB;
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             for (int w = 0; w < kDecWaves; ++w) m = max(m, (rmax_w[w][tid >> 1] >> (16 * (tid & 1))) & 0xffffu);
             const float amax = widen16<BF16>((uint16_t)m);
             sca[tid] = amax;
-            scl[tid] = amax == 0.0f ? 0.0f : 127.0f / amax;
+            scl[tid] = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
         }
         uint32_t base = 0, total = 0;
 #pragma unroll
@@ -276,20 +277,27 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
                 for (int j = 0; j < CPT; ++j) {
                     const int c = tid + kDecThreads * j;
                     const v8u16 v = __builtin_bit_cast(v8u16, xr[j][r]);
-                    // non-outlier |x| <= SCA, so |x * scale| <= 127 and the low
-                    // byte is the code; outlier columns are masked to 0
-                    uint32_t q[8];
+                    uint32_t lo, hi;
+                    if constexpr (FP8) {
+                        lo = e4m3_pack4(widen16<BF16>(v[0]), widen16<BF16>(v[1]), widen16<BF16>(v[2]),
+                                        widen16<BF16>(v[3]), scale);
+                        hi = e4m3_pack4(widen16<BF16>(v[4]), widen16<BF16>(v[5]), widen16<BF16>(v[6]),
+                                        widen16<BF16>(v[7]), scale);
+                    } else {
+                        // non-outlier |x| <= SCA, so |x * scale| <= 127 and the low
+                        // byte is the code
+                        uint32_t q[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        if constexpr (BF16) q[e] = quantize_low_byte(widen16<true>(v[e]), scale);
-                        else q[e] = quantize_low_byte_f16(__builtin_bit_cast(_Float16, (uint16_t)v[e]), scale);
+                        for (int e = 0; e < 8; ++e) {
+                            if constexpr (BF16) q[e] = quantize_low_byte(widen16<true>(v[e]), scale);
+                            else q[e] = quantize_low_byte_f16(__builtin_bit_cast(_Float16, (uint16_t)v[e]), scale);
+                        }
+                        lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
+                                                   __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
+                        hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
+                                                   __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
                     }
-                    const uint32_t lo = __builtin_amdgcn_perm(
-                        __builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
-                        __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
-                    const uint32_t hi = __builtin_amdgcn_perm(
-                        __builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
-                        __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
+                    // outlier columns are masked to code 0
                     codes[j][r] = v2u{lo & keep_lo[j], hi & keep_hi[j]};
                     // a chunk past K (its registers hold chunk 0) parks its bytes in
                     // the row's 16-byte pad, which no MFMA reads
@@ -321,85 +329,117 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     }
     __syncthreads();
 
-    // ---- 6. int8 MFMA over this wave's K steps --------------------------------
+    // ---- 6. MFMA over this wave's K steps ---------------------------------------
     // A = CA rows (lane row r16 = token), B = CB rows (channel): accumulator
     // register v of lane l holds token 4*(l/16) + v, channel n0 + 16 tt + l%16.
+    // int8: one v_mfma_i32_16x16x64_i8 per step; FP8: two
+    // v_mfma_f32_16x16x32_fp8_fp8 on the 8-byte halves (the same split for
+    // both operands, so the sum covers the step's 64 columns once).
     {
         const bool a_ok = r16 < M;
         const int8_t* pa = ca + r16 * ca_stride + kg * 16;
-        v4i acc = {0, 0, 0, 0};
+        if constexpr (FP8) {
+            v4f acc = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int s = grp * SPW + i;
-            if (s < nsteps) {
-                const v4i a = a_ok ? *reinterpret_cast<const v4i*>(pa + s * 64) : v4i{0, 0, 0, 0};
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, breg[i], acc, 0, 0, 0);
+            for (int i = 0; i < SPW; ++i) {
+                const int s = grp * SPW + i;
+                if (s < nsteps) {
+                    const v4i a = a_ok ? *reinterpret_cast<const v4i*>(pa + s * 64) : v4i{0, 0, 0, 0};
+                    const v2l a2 = __builtin_bit_cast(v2l, a), b2 = __builtin_bit_cast(v2l, breg[i]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc, 0, 0, 0);
+                }
             }
-        }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[v];
+            for (int v = 0; v < 4; ++v) {
+                const float f = acc[v];  // by value: bit_cast of a vector element reads element 0
+                red[wave][v][lane] = __builtin_bit_cast(int, f);
+            }
+        } else {
+            v4i acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) {
+                const int s = grp * SPW + i;
+                if (s < nsteps) {
+                    const v4i a = a_ok ? *reinterpret_cast<const v4i*>(pa + s * 64) : v4i{0, 0, 0, 0};
+                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, breg[i], acc, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[v];
+        }
     }
     __syncthreads();
 
     // ---- 7. epilogue: one output per thread ------------------------------------
     if (!e_ok) return;
     const int et = e_n >> 4, l = (e_n & 15) + 16 * (e_m >> 2), v = e_m & 3;
-    int c32 = 0;
+    float y;
+    if constexpr (FP8) {
+        float c = 0.0f;  // the groups' partial sums, in a fixed order
 #pragma unroll
-    for (int g = 0; g < G; ++g) c32 += red[et + T * g][v][l];
-    if (C_i32) C_i32[(size_t)e_m * N + n_e] = c32;
-    float y = (float)c32 * (sca[e_m] / 127.0f);
+        for (int g = 0; g < G; ++g) c += __builtin_bit_cast(float, red[et + T * g][v][l]);
+        if (C_f32) C_f32[(size_t)e_m * N + n_e] = c;
+        y = c * (sca[e_m] / code_max<FP8>());
+    } else {
+        int c32 = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) c32 += red[et + T * g][v][l];
+        if (C_i32) C_i32[(size_t)e_m * N + n_e] = c32;
+        y = (float)c32 * (sca[e_m] / code_max<FP8>());
+    }
     const uint16_t* xrow = xl + (size_t)e_m * K;
 #pragma unroll
     for (int j = 0; j < kDecGather; ++j)
-        if (j < n_out) y += widen16<BF16>(xrow[idx_s[j]]) * (float)(int8_t)cbg[j];
+        if (j < n_out) y += widen16<BF16>(xrow[idx_s[j]]) * code_value<FP8>((int8_t)cbg[j]);
     for (int j = kDecGather; j < n_out; ++j) {
         const int k = idx_s[j];
-        y += widen16<BF16>(xrow[k]) * (float)CB[(size_t)n_e * K + k];
+        y += widen16<BF16>(xrow[k]) * code_value<FP8>(CB[(size_t)n_e * K + k]);
     }
     const float bv = bias ? widen16<BF16>(bias_raw) : 0.0f;
-    Y[(size_t)e_m * N + n_e] = narrow16<BF16>(y * (scb_raw / 127.0f) + bv);
+    Y[(size_t)e_m * N + n_e] = narrow16<BF16>(y * (scb_raw / code_max<FP8>()) + bv);
 }
 
-template <bool BF16, int CPT, int NB, int SPW, bool FULL>
+template <bool BF16, bool FP8, int CPT, int NB, int SPW, bool FULL>
 void launch_variant(hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop,
                     const uint16_t* x, int M, int N, int K, float t, const int8_t* CB,
                     const float* SCB, const uint16_t* b, uint16_t* y, int8_t* CA, float* SCA,
-                    int32_t* idx, int32_t* n_out, uint16_t* xo, int32_t* C_i32) {
-    auto fn = linear_decode_kernel<BF16, CPT, NB, SPW, FULL>;
+                    int32_t* idx, int32_t* n_out, uint16_t* xo, int32_t* C_i32, float* C_f32) {
+    auto fn = linear_decode_kernel<BF16, FP8, CPT, NB, SPW, FULL>;
     const dim3 grid((N + NB - 1) / NB);
     if (ev_start || ev_stop)
         hipExtLaunchKernelGGL(fn, grid, dim3(kDecThreads), 0, stream, ev_start, ev_stop, 0, x, M,
-                              N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32);
+                              N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32, C_f32);
     else
         fn<<<grid, kDecThreads, 0, stream>>>(x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out,
-                                             xo, C_i32);
+                                             xo, C_i32, C_f32);
 }
 
-#define DEC_ARGS stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32
+#define DEC_ARGS stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32, C_f32
 #define DEC_PARAMS                                                                              \
     hipStream_t stream, hipEvent_t e0, hipEvent_t e1, const uint16_t *x, int M, int N, int K,   \
         float t, const int8_t *CB, const float *SCB, const uint16_t *b, uint16_t *y,           \
-        int8_t *CA, float *SCA, int32_t *idx, int32_t *n_out, uint16_t *xo, int32_t *C_i32
+        int8_t *CA, float *SCA, int32_t *idx, int32_t *n_out, uint16_t *xo, int32_t *C_i32,     \
+        float *C_f32
 
 // steps per wave: K / 64 over the K groups, rounded up to a power of two
-template <bool BF16, int CPT, int NB, bool FULL>
+template <bool BF16, bool FP8, int CPT, int NB, bool FULL>
 void launch_steps(DEC_PARAMS) {
     constexpr int G = kDecWaves / (NB / 16);
     const int spw = (K / 64 + G - 1) / G;
-    if (spw <= 1) launch_variant<BF16, CPT, NB, 1, FULL>(DEC_ARGS);
-    else if (spw <= 2) launch_variant<BF16, CPT, NB, 2, FULL>(DEC_ARGS);
-    else if (spw <= 4) launch_variant<BF16, CPT, NB, 4, FULL>(DEC_ARGS);
-    else if (spw <= 8) launch_variant<BF16, CPT, NB, 8, FULL>(DEC_ARGS);
-    else launch_variant<BF16, CPT, NB, 16, FULL>(DEC_ARGS);
+    if (spw <= 1) launch_variant<BF16, FP8, CPT, NB, 1, FULL>(DEC_ARGS);
+    else if (spw <= 2) launch_variant<BF16, FP8, CPT, NB, 2, FULL>(DEC_ARGS);
+    else if (spw <= 4) launch_variant<BF16, FP8, CPT, NB, 4, FULL>(DEC_ARGS);
+    else if (spw <= 8) launch_variant<BF16, FP8, CPT, NB, 8, FULL>(DEC_ARGS);
+    else launch_variant<BF16, FP8, CPT, NB, 16, FULL>(DEC_ARGS);
 }
 
-template <bool BF16>
+template <bool BF16, bool FP8>
 void launch_dtype(DEC_PARAMS) {
     // K > 4096 implies M <= 4 (M * K <= 32768), so FULL needs CPT = 1
-    if (K > 4096) launch_steps<BF16, 2, 16, false>(DEC_ARGS);
-    else if (M == kDecMaxRows) launch_steps<BF16, 1, 16, true>(DEC_ARGS);
-    else launch_steps<BF16, 1, 16, false>(DEC_ARGS);
+    if (K > 4096) launch_steps<BF16, FP8, 2, 16, false>(DEC_ARGS);
+    else if (M == kDecMaxRows) launch_steps<BF16, FP8, 1, 16, true>(DEC_ARGS);
+    else launch_steps<BF16, FP8, 1, 16, false>(DEC_ARGS);
 }
 
 #undef DEC_ARGS
@@ -411,20 +451,22 @@ bool linear_decode_supported(int M, int K) {
     return M >= 1 && M <= kDecMaxRows && K <= kDecMaxK && (int64_t)M * K <= kDecXBytes / 2;
 }
 
-hipError_t launch_linear_decode(const void* X, bool bf16, int M, int N, int K, float t,
+hipError_t launch_linear_decode(const void* X, bool bf16, bool fp8, int M, int N, int K, float t,
                                 const int8_t* CB, const float* SCB, const void* bias, void* Y,
                                 int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
-                                int32_t* C_i32, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
+                                int32_t* C_i32, float* C_f32, hipStream_t stream, hipEvent_t e0,
+                                hipEvent_t e1) {
     const uint16_t* x = static_cast<const uint16_t*>(X);
     const uint16_t* b = static_cast<const uint16_t*>(bias);
     uint16_t* y = static_cast<uint16_t*>(Y);
     uint16_t* xo = static_cast<uint16_t*>(XO);
-    if (bf16)
-        launch_dtype<true>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo,
-                           C_i32);
-    else
-        launch_dtype<false>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo,
-                            C_i32);
+    if (bf16) {
+        if (fp8) launch_dtype<true, true>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32, C_f32);
+        else launch_dtype<true, false>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32, C_f32);
+    } else {
+        if (fp8) launch_dtype<false, true>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32, C_f32);
+        else launch_dtype<false, false>(stream, e0, e1, x, M, N, K, t, CB, SCB, b, y, CA, SCA, idx, n_out, xo, C_i32, C_f32);
+    }
     return hipGetLastError();
 }
 

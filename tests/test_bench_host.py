@@ -15,8 +15,9 @@ def test_kernel_family():
     assert bench.kernel_family(16, 4096) == "fused"
     assert bench.kernel_family(16, 8192) == "small_m"
     assert bench.kernel_family(2048, 4096) == "tiled"
-    # the FP8 forward has no fused kernel
-    assert bench.kernel_family(8, 4096, "fp8") == "small_m"
+    # the FP8 forward has the fused decode kernel, not the other fused one
+    assert bench.kernel_family(8, 4096, "fp8") == "decode"
+    assert bench.kernel_family(16, 4096, "fp8") == "small_m"
     assert bench.kernel_family(2048, 4096, "fp8") == "tiled"
 
 
