@@ -37,10 +37,12 @@
 //  * Epilogue, fused: accumulators -> fp32 times SCA[m]/127 (FP8: /448); the
 //    outlier columns (n_out read from device memory, no host sync) run as
 //    v_mfma_f32_32x32x16_{f16,bf16} of XO against the codes of the weights
-//    gathered at idx (int8 values and E4M3 values are exact in 16-bit), into
-//    the same accumulators; then times SCB[n]/127 (/448), plus bias, rounded
-//    to 16-bit, staged in LDS and written with full 16-byte row-contiguous
-//    stores.
+//    at idx (int8 values and E4M3 values are exact in 16-bit), into the same
+//    accumulators; then times SCB[n]/127 (/448), plus bias, rounded to
+//    16-bit, staged in LDS and written with full 16-byte row-contiguous
+//    stores.  The tile's scales, bias and the weight codes of its first 16
+//    outlier columns are loaded once, with the prologue's stage loads, and
+//    kept in LDS.
 #include "common.h"
 
 namespace llmint8 {
@@ -52,6 +54,7 @@ constexpr int kStages = 4;
 constexpr int kStageBytes = (BM + BN) * BKS;  // 32 KiB
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
+constexpr int kOutLds = 16;  // outlier columns whose weight codes are staged in LDS
 constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
 constexpr int kSmemBytes =
     kStages * kStageBytes > BM * kYStride ? kStages * kStageBytes : BM * kYStride;
@@ -114,7 +117,10 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32,
                        float* __restrict__ C_f32) {
     __shared__ __attribute__((aligned(16))) int8_t smem[kSmemBytes];
-    __shared__ float s_sb[BN], s_bias[BN];
+    __shared__ float s_sa[BM], s_sb[BN], s_bias[BN];
+    // weight codes of the tile's rows at the first kOutLds outlier columns, as
+    // 16-bit values (0 past n_out): row r, column e at s_wo[r * kOutLds + e]
+    __shared__ __attribute__((aligned(16))) uint16_t s_wo[BN * kOutLds];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -165,14 +171,26 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 
     // epilogue operands, fetched now so their latency hides under the K loop
     const int n_out = *n_out_ptr;
-    float sa_raw[4];
+    // The row and column scales, bias and outlier weight codes go to LDS
+    // after the prologue's wait: their loads are issued with its stage loads,
+    // so their latency hides under them.  Every load is unconditional, from a
+    // clamped address (a load under a branch is awaited where the branch
+    // rejoins).  Outlier gather: lane column e = tid % 16, rows tid/16 + 16 q;
+    // lanes past n_out read column 0 (discarded).
+    float sa_raw = SCA[min(m0 + tid, M - 1)];
+    const int n_sb = min(n0 + tid, N - 1);
+    float sb_raw = SCB[n_sb];
+    uint16_t bias_raw = *(bias ? bias + n_sb : XO);  // XO: any readable element
+    const int e_out = tid & (kOutLds - 1);
+    const bool e_valid = e_out < n_out;
+    int e_col = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa_raw[i] = SCA[min(m0 + wm * 128 + 32 * i + (lane & 31), M - 1)];
-    {
-        const int n = min(n0 + tid, N - 1);
-        s_sb[tid] = SCB[n] / code_max<FP8>();
-        s_bias[tid] = bias ? widen16<BF16>(bias[n]) : 0.0f;
+    for (int u = 0; u < kOutLds; ++u) {  // uniform reads; idx holds K >= 64 entries
+        int c = idx[u];
+        asm volatile("" : "+s"(c));  // all sixteen read, then selected without branches
+        e_col = u == e_out ? c : e_col;
     }
+    if (!e_valid) e_col = 0;
 
     // Every stage issues the loads of stage kt+3, clamped to the last stage:
     // past K they re-read it into a ring buffer no wave reads again.  So each
@@ -182,9 +200,26 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // before the epilogue reuses the ring.
     const int nk = K / BKS;
     issue(0);
+    int32_t wo_raw[kOutLds];
+#pragma unroll
+    for (int q = 0; q < kOutLds; ++q)
+        wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + 16 * q, N - 1) * K + e_col];
     issue(min(1, nk - 1));
     issue(min(2, nk - 1));
-    wait_vmcnt<16>();
+    wait_vmcnt<16>();  // stage 0 and everything issued before stage 1
+    // the values are used from here on only (the compiler would otherwise
+    // hoist their conversions above the stage loads, and wait there)
+    asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw));
+#pragma unroll
+    for (int q = 0; q < kOutLds; ++q) asm volatile("" : "+v"(wo_raw[q]));
+    s_sa[tid] = sa_raw;
+    s_sb[tid] = sb_raw / code_max<FP8>();
+    s_bias[tid] = bias ? widen16<BF16>(bias_raw) : 0.0f;
+    const uint32_t e_mask = e_valid ? 0xFFFFu : 0u;  // a mask, not a select: no branches
+#pragma unroll
+    for (int q = 0; q < kOutLds; ++q)
+        s_wo[((tid >> 4) + 16 * q) * kOutLds + e_out] =
+            (uint16_t)(narrow16<BF16>(code_value<FP8>((int8_t)wo_raw[q])) & e_mask);
     stage_barrier();
 
     // Fragment f (A block f < 4, B block f - 4) of a stage is 32 bytes per
@@ -287,32 +322,13 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                     }
                 }
         }
-        // outlier k-block 0 operands, requested before the conversion below so
-        // that their latency overlaps it: all loads unconditional from clamped
-        // addresses (a load under a branch is awaited where the branch rejoins)
+        // outlier k-block 0: the XO row is requested before the conversion
+        // below so that its latency overlaps it (unconditional, from a clamped
+        // address: a load under a branch is awaited where the branch rejoins;
+        // in bounds for n_pad = 0 too, XO holds M * K >= 16 elements)
         const bool have_out = n_out > 0;
-        v8u16 xraw;
-        int8_t wb[4][8];
-        bool kv[8];
-        {
-            // in bounds for n_pad = 0 too: XO holds M * K >= 16 elements
-            xraw = *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + 8 * kh);
-            int kc[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int jj = 8 * kh + e;
-                kv[e] = jj < n_out;
-                const int col = idx[jj];  // idx holds K >= 64 entries; beyond n_out unused
-                kc[e] = kv[e] ? col : 0;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr, N - 1) * K;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) wb[j][e] = cb[kc[e]];
-            }
-        }
-        const float sa = sa_raw[i] / code_max<FP8>();
+        const v8u16 xraw = *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + 8 * kh);
+        const float sa = s_sa[m_lane + 32 * i] / code_max<FP8>();
         v16f f[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -325,14 +341,12 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             const vec_t xa = __builtin_bit_cast(vec_t, xraw);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v8u16 raw;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    raw[e] = kv[e] ? narrow16<BF16>(code_value<FP8>(wb[j][e])) : (uint16_t)0;
+                const v8u16 raw = *reinterpret_cast<const v8u16*>(
+                    s_wo + (wn * 128 + 32 * j + rr) * kOutLds + 8 * kh);
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
-        for (int j0 = 16; j0 < n_out; j0 += 16) {
+        for (int j0 = kOutLds; j0 < n_out; j0 += 16) {
             // further outlier k-blocks (more than 16 outlier columns)
             const vec_t xa = __builtin_bit_cast(
                 vec_t, *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + j0 + 8 * kh));
