@@ -45,12 +45,21 @@ __device__ __forceinline__ uint16_t narrow16(float f) {
 // pattern read as an unsigned integer, so maxima and threshold tests can run on
 // packed u16 pairs and give exactly the fp32 results.
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t abs2(uint32_t v) { return v & 0x7fff7fffu; }
 
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
                                                                   __builtin_bit_cast(u16x2, b)));
+}
+
+// Packed 16-bit difference (wrapping) and arithmetic shift of each half.
+__device__ __forceinline__ uint32_t sub_i16x2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, a) - __builtin_bit_cast(i16x2, b));
+}
+__device__ __forceinline__ uint32_t ashr16x2(uint32_t a, int s) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, a) >> (int16_t)s);
 }
 
 // Smallest finite-or-infinite 16-bit magnitude pattern h with value(h) >= t, so

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     __shared__ int scan_lds[kDecWaves];
     __shared__ int red[kDecWaves][4][64];          // int32 partial tiles, or fp32 bit patterns
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar arithmetic
     const int n0 = blockIdx.x * NB;
     const int nchunk = K >> 3, nsteps = K >> 6;
     const int ca_stride = K + 16;  // 16 rows at one offset hit distinct banks
@@ -131,15 +132,20 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         const uint32_t off = (uint32_t)(c < nchunk ? c : 0) * 16;
 #pragma unroll
         for (int r = 0; r < kDecMaxRows; ++r)
-            xr[j][r] = r < M ? lds_load<v4i>(xl, (uint32_t)(r * K * 2) + off) : v4i{0, 0, 0, 0};
+            xr[j][r] = FULL || r < M ? lds_load<v4i>(xl, (uint32_t)(r * K * 2) + off) : v4i{0, 0, 0, 0};
     }
     issue_weights(0);
 
     // ---- 3. outlier mask: column max over the M rows, 8 bits per chunk --------
     // Magnitudes are compared as 16-bit patterns (packed pairs); for finite
     // values this orders exactly like the fp32 values.
+    // keep16: 0xffff in the 16-bit halves of non-outlier columns.  Both
+    // magnitude patterns are at most 0x7fff, so cm - tb as a signed 16-bit
+    // difference is negative exactly when the column stays (cm < tb).
     const uint32_t tb = threshold_bits<BF16>(t);
+    const uint32_t tb2 = tb | (tb << 16);
     uint32_t mbits[CPT];
+    uint32_t keep16[CPT][4];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         uint32_t cm[4] = {0, 0, 0, 0};
@@ -147,12 +153,13 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         for (int r = 0; r < kDecMaxRows; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) cm[i] = max_u16x2(cm[i], abs2((uint32_t)xr[j][r][i]));
-        uint32_t bits = 0;
+        uint32_t w = 0;  // outlier flag of column 2i in bit 2i, of column 2i+1 in bit 16+2i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            bits |= ((cm[i] & 0xffffu) >= tb ? 1u : 0u) << (2 * i);
-            bits |= ((cm[i] >> 16) >= tb ? 1u : 0u) << (2 * i + 1);
+            keep16[j][i] = ashr16x2(sub_i16x2(cm[i], tb2), 15);
+            w |= (~keep16[j][i] & 0x00010001u) << (2 * i);
         }
+        const uint32_t bits = (w & 0x55u) | ((w >> 15) & 0xaau);
         mbits[j] = tid + kDecThreads * j < nchunk ? bits : 0u;
     }
     issue_weights(1);
@@ -163,13 +170,10 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         uint32_t rm[kDecMaxRows / 2] = {0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const bool ok = tid + kDecThreads * j < nchunk;  // chunks past K count for nothing
+            // a chunk past K holds chunk 0 again, which changes no maximum
             uint32_t keep[4];  // 0x7fff in the 16-bit halves of non-outlier columns
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                keep[i] = !ok ? 0u
-                              : ((((mbits[j] >> (2 * i)) & 1u) ? 0u : 0x7fffu) |
-                                 (((mbits[j] >> (2 * i + 1)) & 1u) ? 0u : 0x7fff0000u));
+            for (int i = 0; i < 4; ++i) keep[i] = keep16[j][i] & 0x7fff7fffu;
 #pragma unroll
             for (int r = 0; r < kDecMaxRows; ++r) {
                 uint32_t m2 = 0;
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         const int tot0 = (int)(total & 0xffffu);
         rank[0] = (int)(ex & 0xffffu);
         if constexpr (CPT > 1) rank[1] = tot0 + (int)(ex >> 16);
-        n_out = tot0 + (int)(total >> 16);
+        n_out = __builtin_amdgcn_readfirstlane(tot0 + (int)(total >> 16));  // the same in every lane
     }
     // the ascending outlier list
 #pragma unroll
@@ -244,7 +248,8 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     {
         const int8_t* cbrow = CB + (size_t)n_c * K;
 #pragma unroll
-        for (int j = 0; j < kDecGather; ++j) cbg[j] = cbrow[j < n_out ? (int)idx_s[j] : 0];
+        for (int j = 0; j < kDecGather; ++j)  // the column is the same in every lane
+            cbg[j] = cbrow[__builtin_amdgcn_readfirstlane(j < n_out ? (int)idx_s[j] : 0)];
     }
 
     // ---- 5. int8 activations into LDS, from the registers ----------------------
@@ -254,18 +259,16 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     {
         uint32_t keep_lo[CPT], keep_hi[CPT];  // 0xff per non-outlier byte
         bool export_ca[CPT];                  // this workgroup's share of the CA output
+        // workgroup b exports the chunks [b * per, b * per + per)
+        const int per = (nchunk + (int)gridDim.x - 1) / (int)gridDim.x;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const uint32_t bits = mbits[j];
-            keep_lo[j] = 0;
-            keep_hi[j] = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                keep_lo[j] |= ((bits >> e) & 1u) ? 0u : (0xffu << (8 * e));
-                keep_hi[j] |= ((bits >> (e + 4)) & 1u) ? 0u : (0xffu << (8 * e));
-            }
+            // byte e of keep_lo: a byte of column e's 16-bit keep mask (columns
+            // 2i and 2i+1 are the halves of keep16 word i)
+            keep_lo[j] = __builtin_amdgcn_perm(keep16[j][1], keep16[j][0], 0x06040200u);
+            keep_hi[j] = __builtin_amdgcn_perm(keep16[j][3], keep16[j][2], 0x06040200u);
             const int c = tid + kDecThreads * j;
-            export_ca[j] = c < nchunk && c % gridDim.x == blockIdx.x;
+            export_ca[j] = c < nchunk && (unsigned)(c - (int)blockIdx.x * per) < (unsigned)per;
         }
         const v4f sc0 = lds_load<v4f>(scl, 0), sc1 = lds_load<v4f>(scl, 16);
         v2u codes[CPT][kDecMaxRows];
@@ -312,7 +315,8 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
                 const int c = tid + kDecThreads * j;
 #pragma unroll
                 for (int r = 0; r < kDecMaxRows; ++r)
-                    if (FULL || r < M) *reinterpret_cast<v2u*>(CA_out + (size_t)r * K + c * 8) = codes[j][r];
+                    if (FULL || r < M)  // M * K <= 32768: 32-bit offsets
+                        *reinterpret_cast<v2u*>(CA_out + (uint32_t)(r * K + c * 8)) = codes[j][r];
             }
         }
     }
@@ -320,10 +324,9 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     if (blockIdx.x == 0) {
         const int n_pad = (n_out + 31) & ~31;
         for (int j = tid; j < n_out; j += kDecThreads) idx_out[j] = idx_s[j];
-        for (int p = tid; p < M * n_pad; p += kDecThreads) {
-            const int r = p / n_pad, j = p - r * n_pad;
-            XO_out[p] = j < n_out ? xl[(size_t)r * K + idx_s[j]] : (uint16_t)0;
-        }
+        for (int r = 0; r < M; ++r)
+            for (int j = tid; j < n_pad; j += kDecThreads)
+                XO_out[r * n_pad + j] = j < n_out ? xl[r * K + idx_s[j]] : (uint16_t)0;
         if (tid == 0) *n_out_out = n_out;
         if (tid < M) SCA_out[tid] = sca[tid];
     }
@@ -335,17 +338,21 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     // int8: one v_mfma_i32_16x16x64_i8 per step; FP8: two
     // v_mfma_f32_16x16x32_fp8_fp8 on the 8-byte halves (the same split for
     // both operands, so the sum covers the step's 64 columns once).
+    // All A operands are read first, unconditionally: token rows past M read
+    // row M-1 (their accumulator rows are never used) and steps past K read
+    // the last step (their MFMAs are skipped by a uniform test).
     {
-        const bool a_ok = r16 < M;
-        const int8_t* pa = ca + r16 * ca_stride + kg * 16;
+        const int8_t* pa = ca + min(r16, M - 1) * ca_stride + kg * 16;
+        v4i areg[SPW];
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+            areg[i] = *reinterpret_cast<const v4i*>(pa + min(grp * SPW + i, nsteps - 1) * 64);
         if constexpr (FP8) {
             v4f acc = {0, 0, 0, 0};
 #pragma unroll
             for (int i = 0; i < SPW; ++i) {
-                const int s = grp * SPW + i;
-                if (s < nsteps) {
-                    const v4i a = a_ok ? *reinterpret_cast<const v4i*>(pa + s * 64) : v4i{0, 0, 0, 0};
-                    const v2l a2 = __builtin_bit_cast(v2l, a), b2 = __builtin_bit_cast(v2l, breg[i]);
+                if (grp * SPW + i < nsteps) {
+                    const v2l a2 = __builtin_bit_cast(v2l, areg[i]), b2 = __builtin_bit_cast(v2l, breg[i]);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc, 0, 0, 0);
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc, 0, 0, 0);
                 }
@@ -356,17 +363,14 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
                 red[wave][v][lane] = __builtin_bit_cast(int, f);
             }
         } else {
-            v4i acc = {0, 0, 0, 0};
+            // two independent chains (even and odd steps); integer sums are exact
+            v4i acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                const int s = grp * SPW + i;
-                if (s < nsteps) {
-                    const v4i a = a_ok ? *reinterpret_cast<const v4i*>(pa + s * 64) : v4i{0, 0, 0, 0};
-                    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, breg[i], acc, 0, 0, 0);
-                }
-            }
+            for (int i = 0; i < SPW; ++i)
+                if (grp * SPW + i < nsteps)
+                    acc[i & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(areg[i], breg[i], acc[i & 1], 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[v];
+            for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[0][v] + acc[1][v];
         }
     }
     __syncthreads();
