@@ -128,13 +128,32 @@ __device__ __forceinline__ constexpr float code_max() {
     return FP8 ? 448.0f : 127.0f;
 }
 
-// four codes, value a in the lowest byte
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float scale) {
-#pragma clang fp contract(off)
-    const float pa = a * scale, pb = b * scale, pc = c * scale, pd = d * scale;
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(pa, pb, 0, false);
+// four codes, value a in the lowest byte.  The first conversion's untouched
+// upper half is overwritten by the second, so its "old" operand can be any
+// register (here pa's own bits: no register has to be zeroed).
+__device__ __forceinline__ uint32_t e4m3_pack4_products(float pa, float pb, float pc, float pd) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(pa, pb, __builtin_bit_cast(int, pa), false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(pc, pd, w, true);
     return (uint32_t)w;
+}
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float scale) {
+#pragma clang fp contract(off)
+    return e4m3_pack4_products(a * scale, b * scale, c * scale, d * scale);
+}
+// The same codes from 16-bit values: fma(x, scale, -0) is the fp32 product of
+// the exactly widened x, signed zeros included (-0 + -0 = -0, +0 + -0 = +0),
+// in one v_fma_mix_f32 that widens x itself.  The -0 is passed in a register
+// the compiler cannot see through (it would rewrite the fma as a multiply,
+// which takes a separate widening instruction).
+__device__ __forceinline__ float opaque_neg_zero() {
+    uint32_t b = 0x80000000u;
+    asm volatile("" : "+s"(b));
+    return __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ uint32_t e4m3_pack4_f16(_Float16 a, _Float16 b, _Float16 c, _Float16 d, float scale,
+                                                   float nz) {
+    return e4m3_pack4_products(__builtin_fmaf((float)a, scale, nz), __builtin_fmaf((float)b, scale, nz),
+                               __builtin_fmaf((float)c, scale, nz), __builtin_fmaf((float)d, scale, nz));
 }
 
 // value of a code byte: the int8 value, or the E4M3 value (exact in fp32)

@@ -271,6 +271,7 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             export_ca[j] = c < nchunk && (unsigned)(c - (int)blockIdx.x * per) < (unsigned)per;
         }
         const v4f sc0 = lds_load<v4f>(scl, 0), sc1 = lds_load<v4f>(scl, 16);
+        const float nz = opaque_neg_zero();
         v2u codes[CPT][kDecMaxRows];
 #pragma unroll
         for (int r = 0; r < kDecMaxRows; ++r) {
@@ -281,7 +282,13 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
                     const int c = tid + kDecThreads * j;
                     const v8u16 v = __builtin_bit_cast(v8u16, xr[j][r]);
                     uint32_t lo, hi;
-                    if constexpr (FP8) {
+                    if constexpr (FP8 && !BF16) {
+                        _Float16 h[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) h[e] = __builtin_bit_cast(_Float16, (uint16_t)v[e]);
+                        lo = e4m3_pack4_f16(h[0], h[1], h[2], h[3], scale, nz);
+                        hi = e4m3_pack4_f16(h[4], h[5], h[6], h[7], scale, nz);
+                    } else if constexpr (FP8) {
                         lo = e4m3_pack4(widen16<BF16>(v[0]), widen16<BF16>(v[1]), widen16<BF16>(v[2]),
                                         widen16<BF16>(v[3]), scale);
                         hi = e4m3_pack4(widen16<BF16>(v[4]), widen16<BF16>(v[5]), widen16<BF16>(v[6]),

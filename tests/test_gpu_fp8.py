@@ -224,6 +224,35 @@ def test_fp8_exact_inputs(seed, dt):
     check_y(bits_of(Y), ref, dt, f"fp8 exact seed={seed}")
 
 
+# ---- the fused decode kernel on the same exact inputs, with signed zeros --------
+# Row 5's non-outlier entries are all +-0 (SCA = 0, scale 0); elsewhere -0 and
+# +0 occur among the drawn values.  The codes keep the sign of a zero product
+# (0x80 for -0), and Y is the closed form.
+@pytest.mark.parametrize("seed,dt", [(0, F16), (1, BF16)])
+def test_fp8_decode_exact_signed_zeros(orc, seed, dt):
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    import bruteforce
+    X, W, b, cols = pins.fp8_exact_case(seed, dt, M=8, N=64, K=512, n_out=3)
+    rest = np.setdiff1d(np.arange(512), cols)
+    X[5, rest] = np.where(np.arange(rest.size) % 3 == 0, 0x8000, 0).astype(X.dtype)
+    assert (X[:, rest] == 0x8000).sum() > 150
+    dev = torch.device("cuda:0")
+    CB, SCB = pkg.quantize_weight_fp8(to_torch(W, dt, dev))
+    Y, q = pkg.linear_fp8(to_torch(X, dt, dev), CB, SCB, bias=to_torch(b, dt, dev), threshold=6.0)
+    torch.cuda.synchronize()
+    ref = orc.forward_fp8(X, W, dt, 6.0, bias=b)
+    assert np.array_equal(q.idx[:int(q.n_out.item())].cpu().numpy(), cols)
+    assert np.array_equal(q.SCA.cpu().numpy(), ref["SCA"]) and ref["SCA"][5] == 0.0
+    ca = q.CA.cpu().numpy()
+    assert np.array_equal(ca, ref["CA"])
+    assert (ca.view(np.uint8)[5, rest] == 0x80).sum() == (X[5, rest] == 0x8000).sum()
+    x = bruteforce.widen(X, dt).astype(np.float64)
+    w = bruteforce.widen(W, dt).astype(np.float64)
+    check_y(bits_of(Y), x @ w.T + bruteforce.widen(b, dt).astype(np.float64), dt,
+            f"fp8 decode exact seed={seed}")
+
+
 # ---- the full decode and prefill shapes, in the one-call launch ----------------
 @pytest.mark.parametrize("name,nrows", [("decode", None), ("prefill", 6)])
 def test_fp8_full_size(orc, name, nrows):
