@@ -18,13 +18,15 @@
 //  * small M (M <= 16 and M*K <= 128K): one launch of M workgroups.  Each
 //    workgroup reads all of X (tiny, L2 resident) to build the outlier mask in
 //    LDS, ranks the outliers with a block scan, then quantizes its own row.
-//  * otherwise three launches, all reading X with 16-byte coalesced loads:
-//      A  column max of each (row group, 512-column slab) -> partial [G, K]
-//      B  max over the G partials, compare with the threshold -> one mask
-//         byte per 8 columns, its rank inside a 256-column group, group counts
-//      C  one wave per row: absmax over non-outlier columns, quantize, write
-//         CA; scatter the row's outlier values into XO by rank; workgroup 0
-//         also writes idx and n_out.
+//  * otherwise two launches, both reading X with 16-byte coalesced loads:
+//      A  per (row group, 256-column slab): column maxima of the magnitudes,
+//         thresholded -> one outlier mask per row group (a bit per column);
+//      C  every workgroup ORs the G group masks and ranks the outliers
+//         (popcount prefixes per 32 columns); then one wave per row: absmax
+//         over non-outlier columns, quantize, write CA; scatter the row's
+//         outlier values into XO by rank; workgroup 0 also writes idx and
+//         n_out.
+//    X is read twice in all (A, then C), CA written once.
 #include "common.h"
 
 namespace llmint8 {
@@ -33,7 +35,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaskBytesMax = 133120 / 8;  // K <= 133120
-constexpr int kRankGroup = 32;             // mask bytes (256 columns) per rank group
+constexpr int kMaskWordsMax = 133120 / 32;
+constexpr int kSlabChunks = 8;             // 8-column chunks per slab of kernel A (K % 64 == 0)
+constexpr int kRowLanes = kThreads / kSlabChunks;
 constexpr int kSmallMaxM = 16;
 constexpr int kSmallMaxElems = 1 << 17;
 
@@ -166,168 +170,214 @@ __global__ __launch_bounds__(kThreads) void act_quant_small(
 }
 
 // ---------------------------------------------------------------------------
-// Large-M path, kernel A: partial column max over a group of rows.
-// grid = (ceil(K/512), G); wave w of the block takes rows row0+w, row0+w+4, ...
+// Large-M path, kernel A: for one group of rows and one 64-column slab, the
+// column maxima of the magnitudes (as 16-bit patterns, which order like the
+// values), thresholded: bit e of byte c of the group's mask is set when column
+// 8c+e reaches t in one of the group's rows.  grid = (slabs, groups); thread
+// (row lane rl = tid/8, chunk lane cl = tid%8) reads rows r0+rl, r0+rl+32, ...
+// of its 8-column chunk with 16-byte loads, 8 of them in flight (a wave
+// instruction reads 8 rows x 128 bytes).  Narrow slabs keep the number of
+// row groups, which kernel C combines, small.
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void act_colmax_partial(const uint16_t* __restrict__ X,
-                                                               int M, int K, int rows_per_group,
-                                                               float* __restrict__ partial) {
-    __shared__ float red[3][kWave][8];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c = blockIdx.x * kWave + lane;  // 8-column piece
-    const int nchunk = K >> 3;
-    const int r0 = blockIdx.y * rows_per_group;
-    const int r1 = min(r0 + rows_per_group, M);
-    float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < nchunk) {
-#pragma unroll 4
-        for (int r = r0 + wave; r < r1; r += 4) {
-            v8u16 v = *reinterpret_cast<const v8u16*>(X + (size_t)r * K + (size_t)c * 8);
+__global__ __launch_bounds__(kThreads) void act_colmask_partial(const uint16_t* __restrict__ X, int M,
+                                                                int K, int rows_per_group, float t,
+                                                                uint32_t* __restrict__ mask_g) {
+    __shared__ uint32_t red[kRowLanes][kSlabChunks][4];
+    __shared__ __attribute__((aligned(4))) uint8_t mbytes[kSlabChunks];
+    const int tid = threadIdx.x, cl = tid % kSlabChunks, rl = tid / kSlabChunks;
+    const int nwords = K >> 5;
+    const int c = blockIdx.x * kSlabChunks + cl;  // < K/8: K % 64 == 0
+    const int r0 = blockIdx.y * rows_per_group, r1 = min(r0 + rows_per_group, M);
+    uint32_t cm[4] = {0, 0, 0, 0};
+    const uint16_t* p = X + (size_t)c * 8;
+#pragma unroll 8
+    for (int r = r0 + rl; r < r1; r += kRowLanes) {
+        const v4i v = *reinterpret_cast<const v4i*>(p + (size_t)r * K);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) cm[e] = fmaxf(cm[e], fabsf(widen16<BF16>(v[e])));
-        }
+        for (int i = 0; i < 4; ++i) cm[i] = max_u16x2(cm[i], abs2((uint32_t)v[i]));
     }
-    if (wave > 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave - 1][lane][e] = cm[e];
+    for (int i = 0; i < 4; ++i) red[rl][cl][i] = cm[i];
+    __syncthreads();
+    if (tid < kSlabChunks) {
+#pragma unroll
+        for (int q = 1; q < kRowLanes; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cm[i] = max_u16x2(cm[i], red[q][cl][i]);
+        const uint32_t tb = threshold_bits<BF16>(t);
+        uint32_t bits = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bits |= ((cm[i] & 0xffffu) >= tb ? 1u : 0u) << (2 * i);
+            bits |= ((cm[i] >> 16) >= tb ? 1u : 0u) << (2 * i + 1);
+        }
+        mbytes[cl] = (uint8_t)bits;
     }
     __syncthreads();
-    if (wave == 0 && c < nchunk) {
-#pragma unroll
-        for (int w = 0; w < 3; ++w)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cm[e] = fmaxf(cm[e], red[w][lane][e]);
-        float* dst = partial + (size_t)blockIdx.y * K + (size_t)c * 8;
-        *reinterpret_cast<v4f*>(dst) = v4f{cm[0], cm[1], cm[2], cm[3]};
-        *reinterpret_cast<v4f*>(dst + 4) = v4f{cm[4], cm[5], cm[6], cm[7]};
+    if (tid < kSlabChunks / 4) {
+        const int w = blockIdx.x * (kSlabChunks / 4) + tid;  // < nwords: K % 64 == 0
+        mask_g[(size_t)blockIdx.y * nwords + w] = reinterpret_cast<const uint32_t*>(mbytes)[tid];
     }
 }
 
-// Kernel B: threshold the column max; one mask byte per 8 columns, ranked
-// inside groups of kRankGroup bytes.  256 threads = 32 mask bytes x 8 lanes,
-// the 8 lanes of a byte split the G partial rows.
-__global__ __launch_bounds__(kThreads) void act_outlier_mask(const float* __restrict__ partial,
-                                                             int G, int K, float t,
-                                                             uint8_t* __restrict__ mask,
-                                                             int32_t* __restrict__ rank8,
-                                                             int32_t* __restrict__ group_count) {
-    __shared__ int cnt_lds[kRankGroup];
-    const int sub = threadIdx.x & 7;
-    const int local = threadIdx.x >> 3;  // 0..31
-    const int c = blockIdx.x * kRankGroup + local;
-    const int nchunk = K >> 3;
-    float cm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (c < nchunk) {
-        for (int g = sub; g < G; g += 8) {
-            const float* src = partial + (size_t)g * K + (size_t)c * 8;
-            v4f a = *reinterpret_cast<const v4f*>(src);
-            v4f b = *reinterpret_cast<const v4f*>(src + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                cm[e] = fmaxf(cm[e], a[e]);
-                cm[e + 4] = fmaxf(cm[e + 4], b[e]);
-            }
-        }
-    }
-    // max over the 8 lanes of each mask byte: xor 1, xor 2 (quad_perm), then
-    // the half-row mirror (lane i <-> 7 - i within 8 lanes)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float v = cm[e];
-        v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0xB1>(0, __builtin_bit_cast(int, v))));
-        v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x4E>(0, __builtin_bit_cast(int, v))));
-        v = fmaxf(v, __builtin_bit_cast(float, dpp_i<0x141>(0, __builtin_bit_cast(int, v))));
-        cm[e] = v;
-    }
-    uint32_t bits = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bits |= (cm[e] >= t ? 1u : 0u) << e;
-    if (c >= nchunk) bits = 0;
-    if (sub == 0) {
-        cnt_lds[local] = __popc(bits);
-        if (c < nchunk) mask[c] = (uint8_t)bits;
-    }
-    __syncthreads();
-    if (sub == 0 && c < nchunk) {
-        int before = 0;
-        for (int q = 0; q < local; ++q) before += cnt_lds[q];
-        rank8[c] = before;
-    }
-    if (threadIdx.x == 0) {
-        int s = 0;
-        for (int q = 0; q < kRankGroup; ++q) s += cnt_lds[q];
-        group_count[blockIdx.x] = s;
-    }
+// 0xffff in the 16-bit halves of word i (columns 2i, 2i+1 of a chunk) whose
+// mask bit is clear.
+__device__ __forceinline__ uint32_t keep_halves(uint32_t bits, int i) {
+    return (((bits >> (2 * i)) & 1u) ? 0u : 0xffffu) | (((bits >> (2 * i + 1)) & 1u) ? 0u : 0xffff0000u);
 }
 
-// Kernel C: one wave per row.  Group offsets are rebuilt per workgroup from
-// the group counts (at most K/256 of them).
+// Codes of 8 values none of which is an outlier (|x| <= absmax, so
+// |x * scale| <= 127 (448) up to rounding).  int8: the fp32 product plus
+// 1.5 * 2^23 holds rint(product) in its low byte; E4M3: v_cvt_pk_fp8_f32.
+// From fp16 the product is one v_fma_mix_f32 (see common.h).
+template <bool BF16, bool FP8>
+__device__ __forceinline__ uint2 codes8(v4i x, float scale, float nz) {
+    const v8u16 v = __builtin_bit_cast(v8u16, x);
+    uint32_t lo, hi;
+    if constexpr (FP8 && !BF16) {
+        _Float16 h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = __builtin_bit_cast(_Float16, (uint16_t)v[e]);
+        lo = e4m3_pack4_f16(h[0], h[1], h[2], h[3], scale, nz);
+        hi = e4m3_pack4_f16(h[4], h[5], h[6], h[7], scale, nz);
+    } else if constexpr (FP8) {
+        lo = e4m3_pack4(widen16<true>(v[0]), widen16<true>(v[1]), widen16<true>(v[2]), widen16<true>(v[3]), scale);
+        hi = e4m3_pack4(widen16<true>(v[4]), widen16<true>(v[5]), widen16<true>(v[6]), widen16<true>(v[7]), scale);
+    } else {
+        uint32_t q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (BF16) q[e] = quantize_low_byte(widen16<true>(v[e]), scale);
+            else q[e] = quantize_low_byte_f16(__builtin_bit_cast(_Float16, (uint16_t)v[e]), scale);
+        }
+        lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(q[3], q[2], 0x0c0c0400u),
+                                   __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u), 0x05040100u);
+        hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(q[7], q[6], 0x0c0c0400u),
+                                   __builtin_amdgcn_perm(q[5], q[4], 0x0c0c0400u), 0x05040100u);
+    }
+    return make_uint2(lo, hi);
+}
+
+// Kernel C: the mask is the OR of the G group masks (one word = 32 columns);
+// exclusive popcount prefixes per word rank the outliers.  Then one wave per
+// row: the row is read in batches of 8 chunks per lane (4096 columns), all
+// loads of a batch in flight; absmax over the non-outlier columns, codes, and
+// the outlier values scattered into XO by rank.  A row of at most 4096
+// columns is read once (its batch stays in registers); longer rows are read
+// again for the codes.
 template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) void act_quant_rows(
-    const uint16_t* __restrict__ X, int M, int K, const uint8_t* __restrict__ mask_g,
-    const int32_t* __restrict__ rank8, const int32_t* __restrict__ group_count, int n_groups,
+    const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g, int G,
     int8_t* __restrict__ CA, float* __restrict__ SCA, int32_t* __restrict__ idx,
     int32_t* __restrict__ n_out, uint16_t* __restrict__ XO) {
-    __shared__ uint8_t mask[kMaskBytesMax];
-    __shared__ int goff[kMaskBytesMax / kRankGroup + 1];
+    __shared__ uint32_t mw[kMaskWordsMax];
+    __shared__ int wpre[kMaskWordsMax];
     __shared__ int scan_lds[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nchunk = K >> 3;
-    for (int c = tid; c < nchunk; c += kThreads) mask[c] = mask_g[c];
-    // group offsets: exclusive scan of group_count, in runs of `per` groups per thread
-    const int per = (n_groups + kThreads - 1) / kThreads;
-    const int g0 = min(tid * per, n_groups), g1 = min(g0 + per, n_groups);
+    const int nchunk = K >> 3, nwords = K >> 5;
+    constexpr int B = 8;  // chunks per lane per batch
+    const int nbatch = (nchunk + B * kWave - 1) / (B * kWave);
+    v4i xv[B];
+    auto load_batch = [&](const uint16_t* xrow, int b) {
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            // from a clamped address (no branch, so no wait here); chunks past
+            // K count as all-outlier below and are never stored
+            const int c = (b * B + j) * kWave + lane;
+            xv[j] = *reinterpret_cast<const v4i*>(xrow + (size_t)min(c, nchunk - 1) * 8);
+        }
+    };
+    // the first row's first batch is requested before the mask, so that the
+    // two latencies overlap
+    const int m_first = blockIdx.x * 4 + wave;
+    if (m_first < M) load_batch(X + (size_t)m_first * K, 0);
+    // the mask and the exclusive prefix of its popcounts; thread t owns a
+    // contiguous run of words
+    const int per = (nwords + kThreads - 1) / kThreads;
+    const int w0 = min(tid * per, nwords), w1 = min(w0 + per, nwords);
     int s = 0;
-    for (int g = g0; g < g1; ++g) s += group_count[g];
+    for (int w = w0; w < w1; ++w) {
+        uint32_t v = 0;
+#pragma unroll 8
+        for (int g = 0; g < G; ++g) v |= mask_g[(size_t)g * nwords + w];
+        mw[w] = v;
+        s += __popc(v);
+    }
     int total;
     int off = block_exclusive_scan(s, scan_lds, &total);
-    for (int g = g0; g < g1; ++g) {
-        goff[g] = off;
-        off += group_count[g];
+    for (int w = w0; w < w1; ++w) {
+        wpre[w] = off;
+        off += __popc(mw[w]);
     }
     __syncthreads();
     const int n_pad = (total + 31) & ~31;
 
     if (blockIdx.x == 0) {
         if (tid == 0) *n_out = total;
-        for (int c = tid; c < nchunk; c += kThreads) {
-            uint32_t bits = mask[c];
-            int r = goff[c / kRankGroup] + (bits ? rank8[c] : 0);
-            while (bits) {
-                const int e = __builtin_ctz(bits);
-                bits &= bits - 1;
-                idx[r++] = c * 8 + e;
+        for (int w = tid; w < nwords; w += kThreads) {
+            uint32_t b = mw[w];
+            int r = wpre[w];
+            while (b) {
+                idx[r++] = w * 32 + __builtin_ctz(b);
+                b &= b - 1;
             }
         }
     }
 
-    for (int m = blockIdx.x * 4 + wave; m < M; m += gridDim.x * 4) {
+    for (int m = m_first; m < M; m += gridDim.x * 4) {
         const uint16_t* xrow = X + (size_t)m * K;
-        float amax = 0.0f;
-#pragma unroll 4
-        for (int c = lane; c < nchunk; c += kWave) {
-            v8u16 v = *reinterpret_cast<const v8u16*>(xrow + (size_t)c * 8);
-            const uint32_t bits = mask[c];
+        auto chunk_bits = [&](int c) -> uint32_t {
+            return c < nchunk ? (mw[c >> 2] >> (8 * (c & 3))) & 0xffu : 0xffu;
+        };
+        // Outlier columns (and chunks past K) are zeroed in the registers, in
+        // the rare chunks that have any, so the maxima and the codes need no
+        // further mask: a zero gives code 0 (+0 in E4M3).
+        auto mask_batch = [&](int b) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (!((bits >> e) & 1u)) amax = fmaxf(amax, fabsf(widen16<BF16>(v[e])));
+            for (int j = 0; j < B; ++j) {
+                const uint32_t bits = chunk_bits((b * B + j) * kWave + lane);
+                if (bits) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xv[j][i] = (int)((uint32_t)xv[j][i] & keep_halves(bits, i));
+                }
+            }
+        };
+        uint32_t am2 = 0;  // packed magnitude maxima
+        for (int b = 0; b < nbatch; ++b) {
+            if (b > 0 || m != m_first) load_batch(xrow, b);
+            mask_batch(b);
+#pragma unroll
+            for (int j = 0; j < B; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) am2 = max_u16x2(am2, abs2((uint32_t)xv[j][i]));
         }
-        amax = wave_max(amax);
+        const uint32_t am = wave_max_u32(max(am2 & 0xffffu, am2 >> 16));
+        const float amax = widen16<BF16>((uint16_t)am);
         if (lane == 0) SCA[m] = amax;
         const float scale = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
+        const float nz = opaque_neg_zero();
         int8_t* carow = CA + (size_t)m * K;
         uint16_t* xo = XO + (size_t)m * n_pad;
-#pragma unroll 4
-        for (int c = lane; c < nchunk; c += kWave) {
-            v8u16 v = *reinterpret_cast<const v8u16*>(xrow + (size_t)c * 8);
-            uint32_t bits = mask[c];
-            *reinterpret_cast<uint2*>(carow + (size_t)c * 8) = quantize8<BF16, FP8>(v, bits, scale);
-            if (bits) {
-                int r = goff[c / kRankGroup] + rank8[c];
-                while (bits) {
-                    const int e = __builtin_ctz(bits);
-                    bits &= bits - 1;
-                    xo[r++] = v[e];
+        for (int b = 0; b < nbatch; ++b) {
+            if (nbatch > 1) {
+                load_batch(xrow, b);
+                mask_batch(b);
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const int c = (b * B + j) * kWave + lane;
+                if (c < nchunk) {
+                    *reinterpret_cast<uint2*>(carow + (size_t)c * 8) = codes8<BF16, FP8>(xv[j], scale, nz);
+                    uint32_t bits = chunk_bits(c);
+                    if (bits) {  // the outlier values, read again (their registers were zeroed)
+                        const uint32_t word = mw[c >> 2];
+                        int r = wpre[c >> 2] + __popc(word & ((1u << (8 * (c & 3))) - 1u));
+                        while (bits) {
+                            const int e = __builtin_ctz(bits);
+                            bits &= bits - 1;
+                            xo[r++] = xrow[c * 8 + e];
+                        }
+                    }
                 }
             }
         }
@@ -339,11 +389,10 @@ __global__ void write_zero_count(int32_t* n_out) { *n_out = 0; }
 
 struct ActPlan {
     bool small;
-    int slabs;            // ceil(K / 512)
-    int groups;           // G row groups for the partial column max
+    int slabs;            // K/64: 64-column slabs of kernel A
+    int groups;           // G row groups of kernel A, each writing a mask of K/8 bytes
     int rows_per_group;
-    int n_rank_groups;    // ceil(K/8 / 32)
-    size_t off_mask, off_rank, off_count, bytes;
+    size_t bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -352,21 +401,17 @@ ActPlan plan_act(int64_t M, int64_t K) {
     ActPlan p{};
     p.small = M <= kSmallMaxM && M * K <= kSmallMaxElems;
     const int64_t nchunk = K / 8;
-    p.slabs = (int)((nchunk + kWave - 1) / kWave);
-    // about 1024 workgroups for kernel A, at least 8 rows per group
-    int64_t g = (1024 + p.slabs - 1) / p.slabs;
-    int64_t gmax = (M + 7) / 8;
+    p.slabs = (int)(nchunk / kSlabChunks);  // K % 64 == 0
+    // about 512 workgroups for kernel A; few row groups (kernel C combines
+    // their masks: 8 or fewer for K >= 4096), each of at least 32 rows
+    int64_t g = (512 + p.slabs - 1) / p.slabs;
+    const int64_t gmax = (M + 31) / 32;
     if (g > gmax) g = gmax;
-    if (g < 1) g = 1;
     if (g > 64) g = 64;
+    if (g < 1) g = 1;
     p.rows_per_group = (int)((M + g - 1) / g);
     p.groups = (int)((M + p.rows_per_group - 1) / p.rows_per_group);
-    p.n_rank_groups = (int)((nchunk + kRankGroup - 1) / kRankGroup);
-    p.off_mask = align256((size_t)p.groups * K * sizeof(float));
-    p.off_rank = p.off_mask + align256((size_t)nchunk);
-    p.off_count = p.off_rank + align256((size_t)nchunk * sizeof(int32_t));
-    p.bytes = p.off_count + align256((size_t)p.n_rank_groups * sizeof(int32_t));
-    if (p.small) p.bytes = 0;
+    p.bytes = p.small ? 0 : align256((size_t)p.groups * (size_t)(K / 8));
     return p;
 }
 
@@ -394,26 +439,19 @@ hipError_t launch_quantize_act(const void* Xv, bool bf16, bool fp8, int M, int K
         fn<<<M, kThreads, 0, stream>>>(X, M, K, t, CA, SCA, idx, n_out, XO);
         return hipGetLastError();
     }
-    char* base = static_cast<char*>(ws);
-    float* partial = reinterpret_cast<float*>(base);
-    uint8_t* mask = reinterpret_cast<uint8_t*>(base + p.off_mask);
-    int32_t* rank8 = reinterpret_cast<int32_t*>(base + p.off_rank);
-    int32_t* gcount = reinterpret_cast<int32_t*>(base + p.off_count);
+    uint32_t* mask_g = static_cast<uint32_t*>(ws);
     dim3 ga(p.slabs, p.groups);
     if (bf16)
-        act_colmax_partial<true><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, partial);
+        act_colmask_partial<true><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, t, mask_g);
     else
-        act_colmax_partial<false><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, partial);
-    act_outlier_mask<<<p.n_rank_groups, kThreads, 0, stream>>>(partial, p.groups, K, t, mask,
-                                                               rank8, gcount);
+        act_colmask_partial<false><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, t, mask_g);
     int blocks = (M + 3) / 4;
     if (blocks > 65536) blocks = 65536;
-    void (*fn)(const uint16_t*, int, int, const uint8_t*, const int32_t*, const int32_t*, int,
-               int8_t*, float*, int32_t*, int32_t*, uint16_t*) =
+    void (*fn)(const uint16_t*, int, int, const uint32_t*, int, int8_t*, float*, int32_t*, int32_t*,
+               uint16_t*) =
         bf16 ? (fp8 ? act_quant_rows<true, true> : act_quant_rows<true, false>)
              : (fp8 ? act_quant_rows<false, true> : act_quant_rows<false, false>);
-    fn<<<blocks, kThreads, 0, stream>>>(X, M, K, mask, rank8, gcount, p.n_rank_groups, CA, SCA, idx,
-                                        n_out, XO);
+    fn<<<blocks, kThreads, 0, stream>>>(X, M, K, mask_g, p.groups, CA, SCA, idx, n_out, XO);
     return hipGetLastError();
 }
 
