@@ -101,6 +101,21 @@ struct TileAcc<true> {
     typedef v16f type;
 };
 
+// Two fp32 values -> packed 16-bit pair (a in the low half), each rounded to
+// nearest even: one v_cvt_pk_{f16,bf16}_f32.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack16x2(float a, float b) {
+    if constexpr (BF16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const bf16x2_t v = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        const f16x2_t v = {(_Float16)a, (_Float16)b};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
 __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
@@ -372,12 +387,11 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int nl = n_lane + 32 * j + 8 * a4;
-                uint32_t h[4];
+                float y[4];
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    h[b] = narrow16<BF16>(f[j][4 * a4 + b] * s_sb[nl + b] + s_bias[nl + b]);
+                for (int b = 0; b < 4; ++b) y[b] = f[j][4 * a4 + b] * s_sb[nl + b] + s_bias[nl + b];
                 *reinterpret_cast<uint2*>(ys + (m_lane + 32 * i) * (kYStride / 2) + nl) =
-                    make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                    make_uint2(pack16x2<BF16>(y[0], y[1]), pack16x2<BF16>(y[2], y[3]));
             }
     }
     __syncthreads();
