@@ -181,6 +181,52 @@ def calibrate_copy(torch, dev, nbytes, launches):
                       "bytes_written_per_launch": nbytes, "launches": launches}), flush=True)
 
 
+def measured_ceiling(torch, pkg, dev, bound, fp8):
+    """The ceiling measured on this device beside the published peak.  HBM:
+    a plain 1 GiB device-to-device copy (its read and its write counted).
+    MFMA: the library's sustained-rate loop (llmint8_peak_mfma) on random
+    codes, every CU busy.  Median of 5 timed launches after 2 warm-ups."""
+    stream = torch.cuda.current_stream()
+    times = []
+    if bound == "hbm":
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for i in range(7):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                times.append(e0.elapsed_time(e1) * 1e-3)
+        t = sorted(times)[len(times) // 2]
+        del src, dst
+        return {"value": round(2 * nbytes / t / 1e9, 1), "unit": "GB/s",
+                "how": "device-to-device copy of 1 GiB, read + write bytes / time"}
+    g = torch.Generator(device="cpu").manual_seed(7)
+    codes = torch.randint(-128, 128, (262144,), dtype=torch.int8, generator=g)
+    if fp8:  # finite E4M3 codes only (0x7f and 0xff are NaN)
+        codes[(codes == 127) | (codes == -1)] = 1
+    operands = codes.to(dev)
+    blocks, iters = 1024, 512
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    for i in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pkg.llmint8_peak_mfma(1 if fp8 else 0, operands.data_ptr(), operands.numel(), sink.data_ptr(),
+                              sink.numel() * 4, blocks, iters, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            times.append(e0.elapsed_time(e1) * 1e-3)
+    t = sorted(times)[len(times) // 2]
+    ops = blocks * 16 * iters * (131072 if fp8 else 65536)
+    return {"value": round(ops / t / 1e12, 1), "unit": "TFLOP/s" if fp8 else "TOP/s",
+            "how": ("v_mfma_scale_f32_32x32x64_f8f6f4" if fp8 else "v_mfma_i32_32x32x32_i8")
+                   + " back to back on random codes, 1024 workgroups x 4 waves"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -345,6 +391,9 @@ def main():
         achieved = 2.0 * M * N * K / (k_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s" if fp8 else "TOP/s", "frac": round(achieved / peak, 4)}
+    ceiling = measured_ceiling(torch, pkg, dev, roof["bound"], fp8)
+    ceiling["frac"] = round(roof["achieved"] / ceiling["value"], 4)
+    roof["measured_peak"] = ceiling
     roof["traffic"] = load_traffic(args.config, fam, args.variant)
     roof["kernel"] = KERNEL_NAMES[fam]
     roof["kernel_ms"] = round(k_ms, 5)

@@ -271,6 +271,24 @@ llmint8_status llmint8_linear_fp8_profiled(const void* X, int dtype, int64_t M, 
                                            hipStream_t stream, hipEvent_t start,
                                            hipEvent_t stop);
 
+/* Diagnostic for the roofline report, not a step of the method: the device's
+ * sustained matrix-core rate, the measured ceiling reported beside the
+ * published peak.  Launches `blocks` workgroups of 256 threads; every wave
+ * runs 4 * iters back-to-back MFMAs on four independent accumulators --
+ * fp8 = 0: v_mfma_i32_32x32x32_i8 (65536 operations each); fp8 = 1:
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 codes (131072 each) -- so the
+ * launch performs blocks * 16 * iters * (65536 or 131072) operations.
+ * operands: device, at least 262144 bytes of codes read once per wave (the
+ * power drawn, and so the clock, depends on them: pass random codes, finite
+ * ones for E4M3).  sink: device, at least blocks * 1024 bytes, one word per
+ * thread (written so that nothing is optimised away).  Time the launch with
+ * events on `stream`.  Errors: LLMINT8_ERR_INVALID_ARGUMENT for NULL or
+ * misaligned pointers, buffers too small, blocks or iters below 1;
+ * LLMINT8_ERR_UNSUPPORTED when the device is not gfx950. */
+llmint8_status llmint8_peak_mfma(int fp8, const int8_t* operands, size_t operand_bytes,
+                                 int32_t* sink, size_t sink_bytes, int blocks, int iters,
+                                 hipStream_t stream);
+
 /* Static English text for a status code. */
 const char* llmint8_status_string(llmint8_status s);
 

@@ -51,6 +51,7 @@ EXPORTS = (
     "llmint8_linear_fp8_workspace_size",
     "llmint8_linear_fp8",
     "llmint8_linear_fp8_profiled",
+    "llmint8_peak_mfma",
     "llmint8_status_string",
     "llmint8_last_hip_error",
 )
@@ -113,6 +114,8 @@ def lib() -> ctypes.CDLL:
               "llmint8_quantize_act_fp8", "llmint8_matmul_fp8", "llmint8_matmul_fp8_profiled",
               "llmint8_linear_fp8", "llmint8_linear_fp8_profiled"):
         getattr(L, f).restype = _INT
+    L.llmint8_peak_mfma.argtypes = [_INT, _P, ctypes.c_size_t, _P, ctypes.c_size_t, _INT, _INT, _P]
+    L.llmint8_peak_mfma.restype = _INT
     L.llmint8_status_string.argtypes = [_INT]
     L.llmint8_status_string.restype = ctypes.c_char_p
     L.llmint8_last_hip_error.argtypes = []
@@ -243,6 +246,11 @@ def llmint8_linear_fp8_profiled(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, 
                                              SCB, bias, Y, CA, SCA, outlier_idx, n_outliers,
                                              X_outlier, C_f32, workspace, workspace_bytes,
                                              stream, start, stop))
+
+
+def llmint8_peak_mfma(fp8, operands, operand_bytes, sink, sink_bytes, blocks, iters, stream=0):
+    _check("llmint8_peak_mfma",
+           lib().llmint8_peak_mfma(fp8, operands, operand_bytes, sink, sink_bytes, blocks, iters, stream))
 
 
 def llmint8_status_string(status: int) -> str:

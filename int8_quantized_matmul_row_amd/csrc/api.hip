@@ -227,6 +227,12 @@ llmint8_status quantize_act_impl(const void* X, int dtype, bool fp8, int64_t M, 
 
 }  // namespace
 
+namespace llmint8 {
+// peak_probe.hip
+hipError_t launch_mfma_peak(bool fp8, const int8_t* operands, int iters, int32_t* sink, int blocks,
+                            hipStream_t stream);
+}  // namespace llmint8
+
 extern "C" {
 
 llmint8_status llmint8_quantize_weight(const void* W, int dtype, int64_t N, int64_t K, int8_t* CB,
@@ -388,6 +394,18 @@ llmint8_status llmint8_linear_fp8_profiled(const void* X, int dtype, int64_t M, 
     return linear_impl(X, dtype, true, M, N, K, threshold, reinterpret_cast<const int8_t*>(CB), SCB,
                        bias, Y, reinterpret_cast<int8_t*>(CA), SCA, outlier_idx, n_outliers,
                        X_outlier, nullptr, C_f32, workspace, workspace_bytes, stream, start, stop);
+}
+
+llmint8_status llmint8_peak_mfma(int fp8, const int8_t* operands, size_t operand_bytes,
+                                 int32_t* sink, size_t sink_bytes, int blocks, int iters,
+                                 hipStream_t stream) {
+    if ((fp8 != 0 && fp8 != 1) || bad_ptr(operands) || bad_ptr(sink) || blocks < 1 || iters < 1)
+        return LLMINT8_ERR_INVALID_ARGUMENT;
+    if (operand_bytes < 262144 || sink_bytes / 1024 < (size_t)blocks) return LLMINT8_ERR_INVALID_ARGUMENT;
+    llmint8_status s = check_device();
+    if (s != LLMINT8_OK) return s;
+    hipError_t e = llmint8::launch_mfma_peak(fp8 == 1, operands, iters, sink, blocks, stream);
+    return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
 }
 
 const char* llmint8_status_string(llmint8_status s) {

@@ -127,3 +127,22 @@ def test_fp8_entry_points_validation():
         pkg.llmint8_quantize_act_workspace_size(2048, 4096) > 0
     assert pkg.llmint8_linear_fp8_workspace_size(8, 4096, 4096) == 0
     assert pkg.llmint8_linear_fp8_workspace_size(8, 4096, 100) == 0
+
+
+def test_peak_mfma_rejects_bad_arguments_before_any_hip_call():
+    L = pkg.lib()
+    ok = dict(fp8=0, operands=A, operand_bytes=262144, sink=A, sink_bytes=1024 * 4, blocks=4, iters=1)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.llmint8_peak_mfma(a["fp8"], a["operands"], a["operand_bytes"], a["sink"],
+                                   a["sink_bytes"], a["blocks"], a["iters"], None)
+
+    assert call(fp8=2) == INVALID
+    assert call(operands=None) == INVALID
+    assert call(operands=A + 4) == INVALID          # misaligned
+    assert call(sink=None) == INVALID
+    assert call(operand_bytes=262143) == INVALID
+    assert call(sink_bytes=4 * 1024 - 1) == INVALID  # one word per thread of 4 blocks
+    assert call(blocks=0) == INVALID
+    assert call(iters=0) == INVALID
