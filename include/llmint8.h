@@ -118,7 +118,9 @@ llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t
                                     int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of optional device workspace llmint8_matmul can use for M x N x K. */
+/* Bytes of optional device workspace llmint8_matmul can use for M x N x K:
+ * for M > 16, 64 * ceil(N / 32) * min(K rounded up to 32, 512) (room for the
+ * weight codes at 512 outlier columns), else 0.  0 for invalid sizes. */
 size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -133,8 +135,16 @@ size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
  *   Y      [M,N] 16-bit out (round to nearest even from fp32).
  *   C_i32  [M,N] int32 out or NULL: when given, the same kernels also store the
  *          exact int8 accumulators (for parity checks).
- *   workspace  optional scratch (NULL / 0 bytes is always valid; a workspace of
- *          llmint8_matmul_workspace_size bytes lets long-K shapes split K).
+ *   workspace  optional scratch, 16-byte aligned; NULL / 0 bytes is always
+ *          valid.  For M > 16 and more than 16 outlier columns, the weight
+ *          codes at the outlier columns are first gathered into it (one
+ *          extra kernel), which makes the outlier part of the product several
+ *          times faster.  W bytes hold 32 * floor(W / (64 * ceil(N / 32) * 32))
+ *          columns (at most K): llmint8_matmul_workspace_size bytes hold 512,
+ *          64 * ceil(N / 32) * K rounded up to 32 hold every column.  With
+ *          more outlier columns than that (n_outliers is read on the device)
+ *          the product gathers the codes itself, as without a workspace.
+ *          The contents need no initialization and are not kept.
  */
 llmint8_status llmint8_matmul(int dtype, int64_t M, int64_t N, int64_t K,
                               const int8_t* CA, const float* SCA, const int32_t* outlier_idx,
@@ -170,7 +180,9 @@ size_t llmint8_linear_workspace_size(int64_t M, int64_t N, int64_t K);
  * K <= 8192, the forward is one fused kernel (each workgroup re-derives the
  * tiny activation quantization while its weight slab streams in); otherwise it
  * is the quantize_act launches followed by the matmul kernel.
- * workspace: llmint8_linear_workspace_size bytes.
+ * workspace: at least llmint8_linear_workspace_size bytes, 16-byte aligned:
+ * llmint8_quantize_act's workspace rounded up to 256 bytes, then the rest
+ * used as llmint8_matmul's (more bytes hold more outlier columns).
  */
 llmint8_status llmint8_linear(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
                               float threshold, const int8_t* CB, const float* SCB,

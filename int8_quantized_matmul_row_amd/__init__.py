@@ -380,9 +380,20 @@ def outlier_columns(q: QuantizedAct):
     return q.idx[:n].cpu()
 
 
+def matmul_workspace(M, N, K, device):
+    """(buffer, bytes) of the optional product workspace (the weight codes at
+    the outlier columns, gathered once per call when there are more than 16)."""
+    torch = _torch()
+    n = llmint8_matmul_workspace_size(M, N, K)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+
+
 def matmul(q: QuantizedAct, CB, SCB, bias=None, out=None, C_i32=None, stream=None,
            workspace=None, events=None):
-    """Y [M,N] = dequant(CA CB^T) + outlier part + bias, in X's dtype."""
+    """Y [M,N] = dequant(CA CB^T) + outlier part + bias, in X's dtype.
+
+    workspace: (buffer, bytes); None allocates llmint8_matmul_workspace_size
+    bytes, (None, 0) runs without one."""
     torch = _torch()
     M, K = q.CA.shape
     N = CB.shape[0]
@@ -390,7 +401,7 @@ def matmul(q: QuantizedAct, CB, SCB, bias=None, out=None, C_i32=None, stream=Non
         raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
     dt_t = torch.float16 if q.dtype == F16 else torch.bfloat16
     Y = out if out is not None else torch.empty((M, N), dtype=dt_t, device=q.CA.device)
-    ws, nbytes = (None, 0) if workspace is None else workspace
+    ws, nbytes = workspace if workspace is not None else matmul_workspace(M, N, K, q.CA.device)
     args = (q.dtype, M, N, K, _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO),
             _ptr(CB), _ptr(SCB), _ptr(bias), _ptr(Y), _ptr(C_i32), _ptr(ws), nbytes,
             _stream(stream))
@@ -462,7 +473,8 @@ def quantize_act_fp8(X, threshold: float = 6.0, stream=None, out: Optional[Quant
 
 def matmul_fp8(q: QuantizedAct, CB, SCB, bias=None, out=None, C_f32=None, stream=None,
                workspace=None, events=None):
-    """The FP8 product Y [M,N] from quantize_act_fp8 / quantize_weight_fp8 outputs."""
+    """The FP8 product Y [M,N] from quantize_act_fp8 / quantize_weight_fp8 outputs
+    (workspace as in matmul)."""
     torch = _torch()
     M, K = q.CA.shape
     N = CB.shape[0]
@@ -470,7 +482,7 @@ def matmul_fp8(q: QuantizedAct, CB, SCB, bias=None, out=None, C_f32=None, stream
         raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
     dt_t = torch.float16 if q.dtype == F16 else torch.bfloat16
     Y = out if out is not None else torch.empty((M, N), dtype=dt_t, device=q.CA.device)
-    ws, nbytes = (None, 0) if workspace is None else workspace
+    ws, nbytes = workspace if workspace is not None else matmul_workspace(M, N, K, q.CA.device)
     args = (q.dtype, M, N, K, _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO),
             _ptr(CB), _ptr(SCB), _ptr(bias), _ptr(Y), _ptr(C_f32), _ptr(ws), nbytes,
             _stream(stream))

@@ -145,8 +145,25 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
                                            C_i32, stream, ev_start, ev_stop);
         return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
     }
+    // the product's share of the workspace follows the activation kernels'
+    const size_t act_ws = align256(llmint8::quantize_act_workspace(M, K));
+    void* mm_ws = workspace && workspace_bytes > act_ws ? static_cast<char*>(workspace) + act_ws : nullptr;
+    const size_t mm_bytes = mm_ws ? workspace_bytes - act_ws : 0;
+    // For the tiled product, the activation kernel also gathers the weight
+    // codes at the outlier columns when the workspace holds no more columns
+    // than it can list (it knows the columns first); no extra launch.
+    llmint8::CodeGather gather;
+    if (M > llmint8::kSmallM && N > 0 && mm_ws) {
+        const int cap = llmint8::gemm_tiled_code_cap((int)N, (int)K, mm_bytes);
+        if (cap > 0 && cap <= llmint8::kActGatherCols) {
+            gather.CB = CB;
+            gather.N = (int)N;
+            gather.cap = cap;
+            gather.out = static_cast<uint16_t*>(mm_ws);
+        }
+    }
     e = llmint8::launch_quantize_act(X, bf16, fp8, (int)M, (int)K, threshold, CA, SCA, outlier_idx,
-                                     n_outliers, X_outlier, workspace, stream);
+                                     n_outliers, X_outlier, workspace, stream, &gather);
     if (e != hipSuccess) return hip_fail(e);
     if (M == 0 || N == 0) return LLMINT8_OK;
     llmint8::MatmulArgs a;
@@ -166,9 +183,9 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
     a.bias = static_cast<const uint16_t*>(bias);
     a.Y = static_cast<uint16_t*>(Y);
     a.C_i32 = fp8 ? nullptr : C_i32;
-    const size_t act_ws = align256(llmint8::quantize_act_workspace(M, K));
-    a.ws = workspace && workspace_bytes > act_ws ? static_cast<char*>(workspace) + act_ws : nullptr;
-    a.ws_bytes = a.ws ? workspace_bytes - act_ws : 0;
+    a.ws = mm_ws;
+    a.ws_bytes = mm_bytes;
+    a.codes_gathered = gather.out != nullptr;
     e = llmint8::launch_matmul(a, stream, ev_start, ev_stop);
     return e == hipSuccess ? LLMINT8_OK : hip_fail(e);
 }
@@ -177,7 +194,9 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
 
 namespace llmint8 {
 
-size_t matmul_workspace(int64_t, int64_t, int64_t) { return 0; }
+size_t matmul_workspace(int64_t M, int64_t N, int64_t K) {
+    return M <= kSmallM ? 0 : gemm_tiled_workspace(N, K);
+}
 
 hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                          hipEvent_t ev_stop) {

@@ -165,6 +165,44 @@ __device__ __forceinline__ float code_value(int8_t b) {
         return (float)b;
 }
 
+// ---- weight codes at the outlier columns, gathered for the tiled product ---
+// Element (n, c), weight row n and outlier column c, sits at 16-bit offset
+// gathered_block(n / 32, c / 16, cap) + (n % 32) * 16 + c % 16: 1 KiB blocks
+// of 32 rows x 16 columns, cap / 16 of them per 32 rows (cap a multiple of 32
+// and n_out <= cap).  It holds the value of CB[n][col(c)] in 16-bit (exact:
+// int8 codes and E4M3 values), 0 for c >= n_out and for rows n >= N.  Columns
+// below kGatherFirst are not written (the product stages those in LDS).
+constexpr int kGatherFirst = 16;
+
+__device__ __forceinline__ size_t gathered_block(int rb, int b, int cap) {
+    return ((size_t)rb * (cap / 16) + b) * 512;
+}
+
+// A workgroup of 256 threads writes row blocks rb0, rb0 + stride, ...: per
+// pass, thread t writes 8 columns of one row, block column t / 64 (then every
+// fourth), row (t % 64) / 2, half t % 2.  col(c) is the c-th outlier column.
+template <bool BF16, bool FP8, typename Col>
+__device__ __forceinline__ void gather_code_blocks(int N, int K, int cap, int n_out, Col col,
+                                                   const int8_t* __restrict__ CB,
+                                                   uint16_t* __restrict__ out, int rb0, int stride) {
+    const int nb = ((n_out + 31) & ~31) / 16, row_blocks = (N + 31) / 32;
+    const int q = threadIdx.x & 63, r = q >> 1, h = q & 1;
+    for (int rb = rb0; rb < row_blocks; rb += stride) {
+        const int n = rb * 32 + r;
+        const int8_t* row = CB + (size_t)min(n, N - 1) * K;
+        for (int b = kGatherFirst / 16 + (int)(threadIdx.x >> 6); b < nb; b += 4) {
+            v8u16 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 16 * b + 8 * h + e;
+                const int8_t code = row[col(min(c, n_out - 1))];
+                v[e] = c < n_out && n < N ? narrow16<BF16>(code_value<FP8>(code)) : (uint16_t)0;
+            }
+            *reinterpret_cast<v8u16*>(out + gathered_block(rb, b, cap) + r * 16 + 8 * h) = v;
+        }
+    }
+}
+
 // ---- cross-lane reductions and scans with DPP (no LDS round trips) --------
 // DPP controls of the gfx9 family: quad_perm, row_shr:n (0x110 + n), row_mirror
 // (0x140), row_half_mirror (0x141), row_bcast:15 (0x142), row_bcast:31 (0x143).
@@ -287,10 +325,20 @@ size_t quantize_tensor_workspace();
 hipError_t launch_quantize_tensor(const void* A, bool bf16, int64_t rows, int64_t cols, int8_t* Q,
                                   float* scale, void* ws, hipStream_t stream);
 
+// Weight codes the activation kernel gathers (layout above) for the tiled
+// product that follows it, at most kActGatherCols columns; out == nullptr:
+// none.  The launcher clears out when it did not gather.
+constexpr int kActGatherCols = 512;
+struct CodeGather {
+    const int8_t* CB = nullptr;
+    int N = 0, cap = 0;
+    uint16_t* out = nullptr;
+};
+
 size_t quantize_act_workspace(int64_t M, int64_t K);
 hipError_t launch_quantize_act(const void* X, bool bf16, bool fp8, int M, int K, float threshold,
                                int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XO,
-                               void* ws, hipStream_t stream);
+                               void* ws, hipStream_t stream, CodeGather* gather = nullptr);
 
 // CA / CB hold int8 codes, or E4M3 code bytes when fp8 is set; the product is
 // exported to C_i32 (int8) or C_f32 (fp8, the fp32 accumulation) when given.
@@ -311,9 +359,13 @@ struct MatmulArgs {
     float* C_f32;
     void* ws;
     size_t ws_bytes;
+    bool codes_gathered = false;  // the activation kernel filled the workspace's codes
 };
 
 size_t matmul_workspace(int64_t M, int64_t N, int64_t K);
+size_t gemm_tiled_workspace(int64_t N, int64_t K);
+// outlier columns whose codes ws_bytes of workspace hold for the tiled product
+int gemm_tiled_code_cap(int N, int K, size_t ws_bytes);
 hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 

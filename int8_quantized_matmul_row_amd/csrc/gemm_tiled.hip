@@ -43,6 +43,12 @@
 //    stores.  The tile's scales, bias and the weight codes of its first 16
 //    outlier columns are loaded once, with the prologue's stage loads, and
 //    kept in LDS.
+//  * More than 16 outlier columns: given a workspace, a gather kernel first
+//    writes the weight codes at the outlier columns, as 16-bit values, in
+//    1 KiB blocks of 32 rows x 16 columns, so that the epilogue reads each
+//    MFMA operand with one 16-byte load per lane instead of eight byte
+//    gathers from rows K bytes apart.  Without one (or past its capacity)
+//    the epilogue gathers the bytes itself.
 #include "common.h"
 
 namespace llmint8 {
@@ -55,6 +61,8 @@ constexpr int kStageBytes = (BM + BN) * BKS;  // 32 KiB
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 constexpr int kOutLds = 16;  // outlier columns whose weight codes are staged in LDS
+constexpr int kGatherThreads = 256;
+static_assert(kOutLds == kGatherFirst, "the gathered codes start where the LDS ones end");
 constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
 constexpr int kSmemBytes =
     kStages * kStageBytes > BM * kYStride ? kStages * kStageBytes : BM * kYStride;
@@ -122,6 +130,18 @@ __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
 
 }  // namespace
 
+// The weight codes at outlier columns kOutLds and on, for the epilogue
+// (layout with gathered_block), when the activation kernel has not written them.
+template <bool BF16, bool FP8>
+__global__ __launch_bounds__(kGatherThreads) void gather_outlier_codes(
+    int N, int K, int cap, const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
+    const int8_t* __restrict__ CB, uint16_t* __restrict__ wo_all) {
+    const int n_out = *n_out_ptr;
+    if (n_out <= kOutLds || n_out > cap) return;  // the epilogue does not read it
+    gather_code_blocks<BF16, FP8>(N, K, cap, n_out, [&](int c) { return idx[c]; }, CB, wo_all,
+                                  blockIdx.x, gridDim.x);
+}
+
 template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
@@ -130,7 +150,8 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const uint16_t* __restrict__ XO, const int8_t* __restrict__ CB,
                        const float* __restrict__ SCB, const uint16_t* __restrict__ bias,
                        uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32,
-                       float* __restrict__ C_f32) {
+                       float* __restrict__ C_f32, const uint16_t* __restrict__ wo_all,
+                       int wo_cap) {
     __shared__ __attribute__((aligned(16))) int8_t smem[kSmemBytes];
     __shared__ float s_sa[BM], s_sb[BN], s_bias[BN];
     // weight codes of the tile's rows at the first kOutLds outlier columns, as
@@ -322,6 +343,17 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
     typedef typename Vec16<BF16>::type vec_t;
     const int n_pad = (n_out + 31) & ~31;
+    // this lane's row of block column 0 in the gathered codes, per j (rows of
+    // blocks past N clamp to the last block: their results are not stored)
+    const bool gathered = wo_all != nullptr && n_out <= wo_cap;
+    const uint16_t* wo_blocks[4] = {};
+    if (gathered) {
+        const int row_blocks = (N + 31) / 32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            wo_blocks[j] = wo_all + gathered_block(min((n0 + wn * 128 + 32 * j) / 32, row_blocks - 1), 0, wo_cap) +
+                           rr * 16 + 8 * kh;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = m0 + m_lane + 32 * i;
@@ -361,24 +393,67 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
-        for (int j0 = kOutLds; j0 < n_out; j0 += 16) {
-            // further outlier k-blocks (more than 16 outlier columns)
-            const vec_t xa = __builtin_bit_cast(
-                vec_t, *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + j0 + 8 * kh));
-            int kcol[8];
+        // further outlier k-blocks (more than 16 outlier columns)
+        if (gathered) {
+            // the codes gathered beforehand: block (row block, j0 / 16), row rr,
+            // columns 8 kh .. 8 kh + 7.  Four k-blocks per round, all their
+            // loads issued first (one wave per SIMD: the latency of one round
+            // of loads is not hidden by anything else); blocks past n_out
+            // re-read the last one and skip their MFMAs.
+            const int j_last = (n_out - 1) & ~15;
+            const uint16_t* xo_row = XO + (size_t)min(m, M - 1) * n_pad + 8 * kh;
+            for (int j0 = kOutLds; j0 < n_out; j0 += 64) {
+                v8u16 xraw4[4], raw[4][4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int jj = j0 + 8 * kh + e;
-                kcol[e] = jj < n_out ? idx[jj] : -1;
+                for (int u = 0; u < 4; ++u) {
+                    const int jb = min(j0 + 16 * u, j_last);
+                    xraw4[u] = *reinterpret_cast<const v8u16*>(xo_row + jb);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        raw[u][j] = *reinterpret_cast<const v8u16*>(wo_blocks[j] + 32 * jb);
+                }
+                // every load is issued before the first wait (the compiler
+                // would otherwise sink each one into the branch that uses it)
+                asm volatile(""
+                             : "+v"(xraw4[0]), "+v"(xraw4[1]), "+v"(xraw4[2]), "+v"(xraw4[3]),
+                               "+v"(raw[0][0]), "+v"(raw[0][1]), "+v"(raw[0][2]), "+v"(raw[0][3]),
+                               "+v"(raw[1][0]), "+v"(raw[1][1]), "+v"(raw[1][2]), "+v"(raw[1][3]),
+                               "+v"(raw[2][0]), "+v"(raw[2][1]), "+v"(raw[2][2]), "+v"(raw[2][3]),
+                               "+v"(raw[3][0]), "+v"(raw[3][1]), "+v"(raw[3][2]), "+v"(raw[3][3]));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (j0 + 16 * u < n_out) {
+                        const vec_t xa = __builtin_bit_cast(vec_t, xraw4[u]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw[u][j]), xa, f[j]);
+                    }
+                }
             }
+        } else {
+            for (int j0 = kOutLds; j0 < n_out; j0 += 16) {
+                const vec_t xa = __builtin_bit_cast(
+                    vec_t, *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + j0 + 8 * kh));
+                // columns past n_out read the last outlier column (no branch
+                // around a load) and are masked to 0
+                int kcol[8];
+                uint32_t keep = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr, N - 1) * K;
-                v8u16 raw;
+                for (int e = 0; e < 8; ++e) {
+                    const int jj = j0 + 8 * kh + e;
+                    kcol[e] = idx[min(jj, n_out - 1)];
+                    keep |= (jj < n_out ? 1u : 0u) << e;
+                }
 #pragma unroll
-                for (int e = 0; e < 8; ++e)  // exact in fp16 and bf16
-                    raw[e] = kcol[e] >= 0 ? narrow16<BF16>(code_value<FP8>(cb[kcol[e]])) : (uint16_t)0;
-                f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
+                for (int j = 0; j < 4; ++j) {
+                    const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr, N - 1) * K;
+                    v8u16 raw;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)  // exact in fp16 and bf16
+                        raw[e] = (uint16_t)(narrow16<BF16>(code_value<FP8>(cb[kcol[e]])) &
+                                            (0u - ((keep >> e) & 1u)));
+                    f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
+                }
             }
         }
 
@@ -412,22 +487,51 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     }
 }
 
+// Bytes of gathered outlier codes for an N x K weight holding `cap` outlier
+// columns (a multiple of 32).
+static size_t gathered_codes_bytes(int64_t N, int64_t cap) { return (size_t)((N + 31) / 32) * 64 * cap; }
+
+size_t gemm_tiled_workspace(int64_t N, int64_t K) {
+    if (N == 0 || K <= kOutLds) return 0;
+    const int64_t k32 = (K + 31) & ~(int64_t)31;
+    return gathered_codes_bytes(N, k32 < kActGatherCols ? k32 : kActGatherCols);
+}
+
+// as many multiples of 32 as fit, at most K rounded up
+int gemm_tiled_code_cap(int N, int K, size_t ws_bytes) {
+    if (K <= kOutLds || N <= 0) return 0;
+    const size_t fit = ws_bytes / gathered_codes_bytes(N, 32), k_blocks = (size_t)((K + 31) & ~31) / 32;
+    return (int)(fit < k_blocks ? fit : k_blocks) * 32;
+}
+
 hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                              hipEvent_t ev_stop) {
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int cap = a.ws ? gemm_tiled_code_cap(a.N, a.K, a.ws_bytes) : 0;
+    uint16_t* wo_all = cap > 0 ? static_cast<uint16_t*>(a.ws) : nullptr;
+    if (wo_all && !a.codes_gathered) {
+        void (*g)(int, int, int, const int32_t*, const int32_t*, const int8_t*, uint16_t*) =
+            a.bf16 ? (a.fp8 ? gather_outlier_codes<true, true> : gather_outlier_codes<true, false>)
+                   : (a.fp8 ? gather_outlier_codes<false, true> : gather_outlier_codes<false, false>);
+        const int row_blocks = (a.N + 31) / 32, blocks = row_blocks < 512 ? row_blocks : 512;
+        g<<<blocks, kGatherThreads, 0, stream>>>(a.N, a.K, cap, a.idx, a.n_out, a.CB, wo_all);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     dim3 grid(tiles_m * tiles_n), block(kThreads);
     void (*fn)(int, int, int, int, int, const int8_t*, const float*, const int32_t*,
                const int32_t*, const uint16_t*, const int8_t*, const float*, const uint16_t*,
-               uint16_t*, int32_t*, float*) =
+               uint16_t*, int32_t*, float*, const uint16_t*, int) =
         a.bf16 ? (a.fp8 ? gemm_tiled_kernel<true, true> : gemm_tiled_kernel<true, false>)
                : (a.fp8 ? gemm_tiled_kernel<false, true> : gemm_tiled_kernel<false, false>);
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(fn, grid, block, 0, stream, ev_start, ev_stop, 0, a.M, a.N, a.K,
                               tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB,
-                              a.bias, a.Y, a.C_i32, a.C_f32);
+                              a.bias, a.Y, a.C_i32, a.C_f32, wo_all, cap);
     } else {
         fn<<<grid, block, 0, stream>>>(a.M, a.N, a.K, tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out,
-                                       a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32, a.C_f32);
+                                       a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32, a.C_f32, wo_all,
+                                       cap);
     }
     return hipGetLastError();
 }

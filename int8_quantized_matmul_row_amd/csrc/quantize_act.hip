@@ -269,7 +269,7 @@ template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) void act_quant_rows(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g, int G,
     int8_t* __restrict__ CA, float* __restrict__ SCA, int32_t* __restrict__ idx,
-    int32_t* __restrict__ n_out, uint16_t* __restrict__ XO) {
+    int32_t* __restrict__ n_out, uint16_t* __restrict__ XO, CodeGather gather) {
     __shared__ uint32_t mw[kMaskWordsMax];
     __shared__ int wpre[kMaskWordsMax];
     __shared__ int scan_lds[4];
@@ -383,6 +383,23 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
         }
         for (int j = total + lane; j < n_pad; j += kWave) xo[j] = 0;
     }
+
+    // the weight codes at the outlier columns for the product that follows
+    // (when asked for): this workgroup's share of the weight's row blocks
+    if (gather.out != nullptr && total > kGatherFirst && total <= gather.cap) {
+        __shared__ int s_cols[kActGatherCols];
+        for (int w = tid; w < nwords; w += kThreads) {
+            uint32_t b = mw[w];
+            int r = wpre[w];
+            while (b) {
+                s_cols[r++] = w * 32 + __builtin_ctz(b);
+                b &= b - 1;
+            }
+        }
+        __syncthreads();
+        gather_code_blocks<BF16, FP8>(gather.N, K, gather.cap, total, [&](int c) { return s_cols[c]; },
+                                      gather.CB, gather.out, blockIdx.x, gridDim.x);
+    }
 }
 
 __global__ void write_zero_count(int32_t* n_out) { *n_out = 0; }
@@ -424,9 +441,15 @@ size_t quantize_act_workspace(int64_t M, int64_t K) {
 
 hipError_t launch_quantize_act(const void* Xv, bool bf16, bool fp8, int M, int K, float t,
                                int8_t* CA, float* SCA, int32_t* idx, int32_t* n_out, void* XOv,
-                               void* ws, hipStream_t stream) {
+                               void* ws, hipStream_t stream, CodeGather* gather) {
     const uint16_t* X = static_cast<const uint16_t*>(Xv);
     uint16_t* XO = static_cast<uint16_t*>(XOv);
+    CodeGather g;
+    if (gather != nullptr) {
+        g = *gather;
+        if (g.cap > kActGatherCols) g.out = nullptr;
+        gather->out = nullptr;  // set again below when act_quant_rows gathers
+    }
     if (M == 0) {
         write_zero_count<<<1, 1, 0, stream>>>(n_out);
         return hipGetLastError();
@@ -448,10 +471,11 @@ hipError_t launch_quantize_act(const void* Xv, bool bf16, bool fp8, int M, int K
     int blocks = (M + 3) / 4;
     if (blocks > 65536) blocks = 65536;
     void (*fn)(const uint16_t*, int, int, const uint32_t*, int, int8_t*, float*, int32_t*, int32_t*,
-               uint16_t*) =
+               uint16_t*, CodeGather) =
         bf16 ? (fp8 ? act_quant_rows<true, true> : act_quant_rows<true, false>)
              : (fp8 ? act_quant_rows<false, true> : act_quant_rows<false, false>);
-    fn<<<blocks, kThreads, 0, stream>>>(X, M, K, mask_g, p.groups, CA, SCA, idx, n_out, XO);
+    fn<<<blocks, kThreads, 0, stream>>>(X, M, K, mask_g, p.groups, CA, SCA, idx, n_out, XO, g);
+    if (gather != nullptr) gather->out = g.out;
     return hipGetLastError();
 }
 

@@ -77,7 +77,16 @@ def test_workspace_sizes():
     assert pkg.llmint8_quantize_act_workspace_size(8, 4096) == 0      # one-launch path
     assert pkg.llmint8_quantize_act_workspace_size(2048, 4096) > 0
     assert pkg.llmint8_quantize_act_workspace_size(64, 100) == 0       # unsupported K
-    assert pkg.llmint8_matmul_workspace_size(8, 4096, 4096) >= 0
+    # the tiled product's gathered outlier codes: 16-bit, 32-row blocks, up to
+    # 512 columns (fewer when K is smaller); nothing for the small-M kernel
+    assert pkg.llmint8_matmul_workspace_size(8, 4096, 4096) == 0
+    assert pkg.llmint8_matmul_workspace_size(16, 4096, 4096) == 0
+    assert pkg.llmint8_matmul_workspace_size(17, 4096, 4096) == 4096 * 2 * 512
+    assert pkg.llmint8_matmul_workspace_size(2048, 16384, 4096) == 16 << 20
+    assert pkg.llmint8_matmul_workspace_size(300, 33, 128) == 64 * 2 * 128
+    assert pkg.llmint8_matmul_workspace_size(300, 33, 96) == 0           # unsupported K
+    assert pkg.llmint8_linear_workspace_size(2048, 16384, 4096) >= \
+        pkg.llmint8_quantize_act_workspace_size(2048, 4096) + (16 << 20)
 
 
 def mm(dtype=0, M=32, N=64, K=128, CA=A, SCA=A, idx=A, n=A, XO=A, CB=A, SCB=A, bias=None, Y=A,

@@ -86,6 +86,76 @@ def test_threshold_inf_no_outliers(orc, M, N, K):
     assert g["n_out"] == 0
 
 
+# ---- more than 16 outlier columns: codes gathered into the workspace --------
+MANY = [
+    # M, N, K, dtype, planted outlier columns, threshold (None: the default)
+    (257, 769, 448, BF16, 40, None),
+    (64, 33, 576, F16, 150, None),
+    (300, 100, 1024, F16, 0, 0.0),   # every column: 1024 > the default capacity
+]
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
+@pytest.mark.parametrize("M,N,K,dt,nout,t", MANY,
+                         ids=[f"{r[0]}x{r[1]}x{r[2]}-{r[4]}" for r in MANY])
+def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8):
+    """The tiled product gives the same bits whether the epilogue reads the
+    outlier weight codes from the gathered blocks (default and full-capacity
+    workspaces) or gathers them itself (no workspace, or one too small)."""
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    from gpu_helpers import to_torch
+    wl = synth.make_random(M, N, K, dt, seed=5 * M + N, n_outlier_cols=nout, bias_sigma=0.01)
+    t = wl.threshold if t is None else t
+    dev = torch.device("cuda:0")
+    X, W = to_torch(wl.X, dt, dev), to_torch(wl.W, dt, dev)
+    bias = to_torch(wl.bias, dt, dev)
+    if fp8:
+        CB, SCB = pkg.quantize_weight_fp8(W)
+        q = pkg.quantize_act_fp8(X, t)
+        mm = pkg.matmul_fp8
+    else:
+        CB, SCB = pkg.quantize_weight(W)
+        q = pkg.quantize_act(X, t)
+        mm = pkg.matmul
+    n_out = int(q.n_out.item())
+    log(f"[parity] gathered outlier codes {M}x{N}x{K} fp8={fp8} n_out={n_out}")
+    assert n_out > 16
+    default_bytes = pkg.llmint8_matmul_workspace_size(M, N, K)
+    full_bytes = (N + 31) // 32 * 64 * ((K + 31) // 32 * 32)
+    small_bytes = (N + 31) // 32 * 64 * 16   # holds no 32-column group
+    runs = {}
+    for name, nbytes in [("none", 0), ("small", small_bytes), ("default", default_bytes),
+                         ("full", full_bytes)]:
+        ws = torch.full((max(nbytes, 1),), 0x5A, dtype=torch.uint8, device=dev)  # stale bytes
+        Y = mm(q, CB, SCB, bias=bias, workspace=(ws if nbytes else None, nbytes))
+        runs[name] = Y.view(torch.int16).cpu()
+    for name in ("small", "default", "full"):
+        assert torch.equal(runs[name], runs["none"]), name
+    # the one-call forward: codes gathered by the activation kernel (default
+    # workspace), or by the product's own gather kernel (a workspace holding
+    # more columns than the activation kernel lists)
+    lin = pkg.linear_fp8 if fp8 else pkg.linear
+    lin_size = (pkg.llmint8_linear_fp8_workspace_size if fp8 else pkg.llmint8_linear_workspace_size)
+    base = lin_size(M, N, K)
+    for extra in (0, full_bytes - default_bytes):
+        ws = torch.full((base + extra,), 0x5A, dtype=torch.uint8, device=dev)
+        Y, _ = lin(X, CB, SCB, bias=bias, threshold=t, workspace=(ws, base + extra))
+        assert torch.equal(Y.view(torch.int16).cpu(), runs["none"]), extra
+    # and a second call with fewer outlier columns into the same (stale) workspace
+    if t != 0.0:
+        X2 = X.clone()
+        X2[:, q.idx[:n_out // 2].long()] = 0   # half the outlier columns drop out
+        q2 = (pkg.quantize_act_fp8 if fp8 else pkg.quantize_act)(X2, t)
+        assert 16 < int(q2.n_out.item()) < n_out
+        ws = torch.empty((default_bytes,), dtype=torch.uint8, device=dev)
+        Y1 = mm(q, CB, SCB, bias=bias, workspace=(ws, default_bytes))
+        Y2 = mm(q2, CB, SCB, bias=bias, workspace=(ws, default_bytes))
+        Y2_none = mm(q2, CB, SCB, bias=bias, workspace=(None, 0))
+        assert torch.equal(Y1.view(torch.int16).cpu(), runs["none"])
+        assert torch.equal(Y2.view(torch.int16).cpu(), Y2_none.view(torch.int16).cpu())
+
+
 @pytest.mark.parametrize("M", [5, 48])
 def test_threshold_boundary_and_zero_rows(orc, M):
     wl = synth.make_random(M, 70, 128, F16, seed=23)
@@ -210,6 +280,9 @@ LINEAR = [
     (3, 64, 192, BF16, 1, False, 6.0),        # one slice, a wave with no step
     (16, 77, 2112, BF16, 2, True, 2.5),       # ~90 outlier columns per slice
     (8, 4096, 1024, F16, 1, True, 6.0),       # four slices of 256 columns
+    (257, 769, 448, BF16, 40, True, 6.0),     # tiled; the activation kernel gathers codes
+    (64, 33, 576, F16, 150, True, 6.0),
+    (300, 100, 1024, F16, 2, True, 0.0),      # more outlier columns than the workspace holds
 ]
 
 
