@@ -360,11 +360,11 @@ def main():
     n_kt = min(steps, 512)
     evs = [(hip.event(), hip.event()) for _ in range(n_kt)]
     mm_prof = pkg.llmint8_matmul_fp8_profiled if fp8 else pkg.llmint8_matmul_profiled
-    # The product's workspace takes the weight codes at the outlier columns
-    # past the first 16 (gathered by a kernel ahead of the GEMM).  With 16 or
-    # fewer the GEMM never reads it, so it runs without one and no gather
-    # launch sits between the GEMMs timed here.
-    mm_ws = pkg.matmul_workspace(M, N, K, dev) if n_out > 16 else (None, 0)
+    # The product's own workspace, as llmint8_matmul takes it: split-K partial
+    # tiles and the weight codes at the outlier columns past the first 16,
+    # with a small kernel ahead of the GEMM that zeroes the split counters and
+    # gathers the codes.
+    mm_ws = pkg.matmul_workspace(M, N, K, dev)
 
     def gemm_only(i, ev):
         CB, SCB = weights[i % n_copies]

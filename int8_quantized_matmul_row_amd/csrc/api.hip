@@ -154,12 +154,12 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
     // than it can list (it knows the columns first); no extra launch.
     llmint8::CodeGather gather;
     if (M > llmint8::kSmallM && N > 0 && mm_ws) {
-        const int cap = llmint8::gemm_tiled_code_cap((int)N, (int)K, mm_bytes);
-        if (cap > 0 && cap <= llmint8::kActGatherCols) {
+        const llmint8::TiledLayout L = llmint8::tiled_layout((int)M, (int)N, (int)K, mm_ws, mm_bytes);
+        if (L.codes != nullptr && L.cap <= llmint8::kActGatherCols) {
             gather.CB = CB;
             gather.N = (int)N;
-            gather.cap = cap;
-            gather.out = static_cast<uint16_t*>(mm_ws);
+            gather.cap = L.cap;
+            gather.out = L.codes;
         }
     }
     e = llmint8::launch_quantize_act(X, bf16, fp8, (int)M, (int)K, threshold, CA, SCA, outlier_idx,
@@ -195,7 +195,7 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
 namespace llmint8 {
 
 size_t matmul_workspace(int64_t M, int64_t N, int64_t K) {
-    return M <= kSmallM ? 0 : gemm_tiled_workspace(N, K);
+    return M <= kSmallM ? 0 : gemm_tiled_workspace(M, N, K);
 }
 
 hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,

@@ -363,9 +363,18 @@ struct MatmulArgs {
 };
 
 size_t matmul_workspace(int64_t M, int64_t N, int64_t K);
-size_t gemm_tiled_workspace(int64_t N, int64_t K);
-// outlier columns whose codes ws_bytes of workspace hold for the tiled product
-int gemm_tiled_code_cap(int N, int K, size_t ws_bytes);
+size_t gemm_tiled_workspace(int64_t M, int64_t N, int64_t K);
+// How the tiled product uses a workspace: split-K arrival counters and
+// partial tiles (split > 1), then the gathered outlier codes (cap columns).
+struct TiledLayout {
+    int split = 1;
+    uint32_t* counters = nullptr;
+    int n_counters = 0;
+    int32_t* part = nullptr;
+    uint16_t* codes = nullptr;
+    int cap = 0;
+};
+TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes);
 hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                          hipEvent_t ev_stop);
 

@@ -43,6 +43,12 @@
 //    stores.  The tile's scales, bias and the weight codes of its first 16
 //    outlier columns are loaded once, with the prologue's stage loads, and
 //    kept in LDS.
+//  * Few tiles (under half the CUs, e.g. M = 512 against a 57344-long K):
+//    given a workspace, K is split over up to 8 workgroups per tile.  Each
+//    stores its int32 (FP8: fp32) accumulators there and counts itself in
+//    with an atomic; the last to arrive adds the partial sums in split order
+//    (the same result whichever arrives last; exact for int8) and runs the
+//    epilogue.  The counters are zeroed by a kernel ahead of the GEMM.
 //  * More than 16 outlier columns: given a workspace, a gather kernel first
 //    writes the weight codes at the outlier columns, as 16-bit values, in
 //    1 KiB blocks of 32 rows x 16 columns, so that the epilogue reads each
@@ -62,6 +68,9 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = 8;
 constexpr int kOutLds = 16;  // outlier columns whose weight codes are staged in LDS
 constexpr int kGatherThreads = 256;
+constexpr int kCUs = 256;             // compute units of the device (gfx950)
+constexpr int kMaxSplit = 8;          // workgroups per tile when K is split
+constexpr int kMinSplitStages = 16;   // K stages per split, at least
 static_assert(kOutLds == kGatherFirst, "the gathered codes start where the LDS ones end");
 constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
 constexpr int kSmemBytes =
@@ -108,6 +117,14 @@ template <>
 struct TileAcc<true> {
     typedef v16f type;
 };
+template <bool FP8>
+struct Part4 {
+    typedef v4i type;
+};
+template <>
+struct Part4<true> {
+    typedef v4f type;
+};
 
 // Two fp32 values -> packed 16-bit pair (a in the low half), each rounded to
 // nearest even: one v_cvt_pk_{f16,bf16}_f32.
@@ -130,19 +147,25 @@ __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
 
 }  // namespace
 
-// The weight codes at outlier columns kOutLds and on, for the epilogue
-// (layout with gathered_block), when the activation kernel has not written them.
+// Ahead of the GEMM: workgroup 0 zeroes the split-K arrival counters (if
+// any), and the weight codes at outlier columns kOutLds and on are gathered
+// for the epilogue (layout with gathered_block) when the activation kernel
+// has not written them (wo_all != nullptr).
 template <bool BF16, bool FP8>
-__global__ __launch_bounds__(kGatherThreads) void gather_outlier_codes(
+__global__ __launch_bounds__(kGatherThreads) void gemm_prep(
     int N, int K, int cap, const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
-    const int8_t* __restrict__ CB, uint16_t* __restrict__ wo_all) {
+    const int8_t* __restrict__ CB, uint16_t* __restrict__ wo_all, uint32_t* __restrict__ counters,
+    int n_counters) {
+    if (blockIdx.x == 0)
+        for (int t = threadIdx.x; t < n_counters; t += kGatherThreads) counters[t] = 0;
+    if (wo_all == nullptr) return;
     const int n_out = *n_out_ptr;
     if (n_out <= kOutLds || n_out > cap) return;  // the epilogue does not read it
     gather_code_blocks<BF16, FP8>(N, K, cap, n_out, [&](int c) { return idx[c]; }, CB, wo_all,
                                   blockIdx.x, gridDim.x);
 }
 
-template <bool BF16, bool FP8>
+template <bool BF16, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const int8_t* __restrict__ CA, const float* __restrict__ SCA,
@@ -151,7 +174,8 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const float* __restrict__ SCB, const uint16_t* __restrict__ bias,
                        uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32,
                        float* __restrict__ C_f32, const uint16_t* __restrict__ wo_all,
-                       int wo_cap) {
+                       int wo_cap, int split, uint32_t* __restrict__ counters,
+                       int32_t* __restrict__ part) {
     __shared__ __attribute__((aligned(16))) int8_t smem[kSmemBytes];
     __shared__ float s_sa[BM], s_sb[BN], s_bias[BN];
     // weight codes of the tile's rows at the first kOutLds outlier columns, as
@@ -160,9 +184,15 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    // SPLIT: workgroup b takes split ks = b % split of tile b / split, K
+    // stages [ks nk / split, (ks + 1) nk / split); otherwise split is 1
+    if constexpr (!SPLIT) split = 1;
+    const int tile = blockIdx.x / split, ks = blockIdx.x - tile * split;
     int tm, tn;
-    map_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    map_tile(tile, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    const int nk_all = K / BKS;
+    const int kt_begin = ks * nk_all / split, nk = (ks + 1) * nk_all / split - kt_begin;
 
     // ---- stage loads: wave w fills rows [64w, 64w + 64) of A and of B, 16 rows
     // per instruction; lane p lands in row 16 q + p/4, slot p%4, and so fetches
@@ -174,8 +204,8 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 64 * wave + 16 * i + (lane >> 2);
-        pa[i] = CA + (size_t)min(m0 + r, M - 1) * K + dchunk;
-        pb[i] = CB + (size_t)min(n0 + r, N - 1) * K + dchunk;
+        pa[i] = CA + (size_t)min(m0 + r, M - 1) * K + (size_t)kt_begin * BKS + dchunk;
+        pb[i] = CB + (size_t)min(n0 + r, N - 1) * K + (size_t)kt_begin * BKS + dchunk;
     }
     const uint32_t lds_base = lds_address(smem) + 64 * wave * BKS;  // this wave's rows
     auto issue = [&](int kt) {
@@ -234,7 +264,6 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // branches (a loop whose stages run conditionally made the compiler merge
     // register versions with hundreds of copies).  All loads are awaited
     // before the epilogue reuses the ring.
-    const int nk = K / BKS;
     issue(0);
     int32_t wo_raw[kOutLds];
 #pragma unroll
@@ -329,6 +358,57 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         }
     }
     wait_vmcnt<0>();  // the clamped loads past K have landed too
+
+    // ---- split K: the partial sums meet in the workspace ---------------------
+    // Stored in register order: 16 bytes (registers 4c..4c+3 of a block) per
+    // lane, a wave's 64 lanes contiguous, so every access is a full 1 KiB.
+    if constexpr (SPLIT) {
+        __shared__ int s_last;
+        constexpr int kWaveWords = 16 * 16 * 64;  // 16 blocks x 16 registers x 64 lanes
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    // whole vectors through bit casts (a bit cast of one vector
+                    // element reads element 0)
+                    const v16i bits = __builtin_bit_cast(v16i, acc[i][j]);
+                    const v4i w = {bits[4 * c], bits[4 * c + 1], bits[4 * c + 2], bits[4 * c + 3]};
+                    *reinterpret_cast<v4i*>(part + (((size_t)tile * split + ks) * 4 + wave) * kWaveWords +
+                                            ((i * 4 + j) * 4 + c) * 256 + lane * 4) = w;
+                }
+        __threadfence();  // the stores are visible device-wide before the count
+        __syncthreads();
+        if (tid == 0) s_last = atomicAdd(counters + tile, 1u) == (unsigned)(split - 1);
+        __syncthreads();
+        if (!s_last) return;  // another workgroup finishes this tile
+        __threadfence();
+        // sum in split order, this workgroup's own part read back too (the
+        // same result whichever workgroup arrives last)
+        const int32_t* p0 = part + (size_t)tile * split * (4 * kWaveWords) + wave * kWaveWords + lane * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc_t t;
+#pragma unroll
+                for (int sp = 0; sp < kMaxSplit; ++sp) {
+                    if (sp < split) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const auto x = __builtin_bit_cast(typename Part4<FP8>::type,
+                                                              *reinterpret_cast<const v4i*>(
+                                                                  p0 + (size_t)sp * (4 * kWaveWords) +
+                                                                  ((i * 4 + j) * 4 + c) * 256));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) t[4 * c + e] = sp == 0 ? x[e] : t[4 * c + e] + x[e];
+                        }
+                    }
+                }
+                acc[i][j] = t;
+            }
+    }
 
     // ---- epilogue ----------------------------------------------------------
     // Block (i, j) is held transposed: register v of lane l is row
@@ -491,47 +571,95 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 // columns (a multiple of 32).
 static size_t gathered_codes_bytes(int64_t N, int64_t cap) { return (size_t)((N + 31) / 32) * 64 * cap; }
 
-size_t gemm_tiled_workspace(int64_t N, int64_t K) {
-    if (N == 0 || K <= kOutLds) return 0;
-    const int64_t k32 = (K + 31) & ~(int64_t)31;
-    return gathered_codes_bytes(N, k32 < kActGatherCols ? k32 : kActGatherCols);
+// Workgroups per tile: split K when the tiles fill under half the CUs, into
+// as many parts as keep one workgroup per CU, each at least kMinSplitStages
+// stages long.
+static int split_of(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (tiles * 2 > kCUs) return 1;
+    int64_t s = kCUs / tiles;
+    if (s > K / BKS / kMinSplitStages) s = K / BKS / kMinSplitStages;
+    if (s > kMaxSplit) s = kMaxSplit;
+    return s < 1 ? 1 : (int)s;
 }
 
-// as many multiples of 32 as fit, at most K rounded up
-int gemm_tiled_code_cap(int N, int K, size_t ws_bytes) {
-    if (K <= kOutLds || N <= 0) return 0;
-    const size_t fit = ws_bytes / gathered_codes_bytes(N, 32), k_blocks = (size_t)((K + 31) & ~31) / 32;
-    return (int)(fit < k_blocks ? fit : k_blocks) * 32;
+// arrival counters (padded to 256 bytes), then split x tiles partial tiles
+static size_t split_bytes(int64_t M, int64_t N, int64_t K) {
+    const int split = split_of(M, N, K);
+    if (split <= 1) return 0;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return (((size_t)tiles * 4 + 255) & ~(size_t)255) + (size_t)split * tiles * BM * BN * 4;
+}
+
+size_t gemm_tiled_workspace(int64_t M, int64_t N, int64_t K) {
+    size_t b = split_bytes(M, N, K);
+    if (N > 0 && K > kOutLds) {
+        const int64_t k32 = (K + 31) & ~(int64_t)31;
+        b += gathered_codes_bytes(N, k32 < kActGatherCols ? k32 : kActGatherCols);
+    }
+    return b;
+}
+
+// The split region first, when the workspace holds it; the gathered codes
+// take the rest: as many multiples of 32 columns as fit, at most K rounded up.
+TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes) {
+    TiledLayout L;
+    if (ws == nullptr || M <= 0 || N <= 0) return L;
+    char* p = static_cast<char*>(ws);
+    const size_t sb = split_bytes(M, N, K);
+    if (sb > 0 && ws_bytes >= sb) {
+        const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        L.split = split_of(M, N, K);
+        L.counters = reinterpret_cast<uint32_t*>(p);
+        L.n_counters = tiles;
+        L.part = reinterpret_cast<int32_t*>(p + (((size_t)tiles * 4 + 255) & ~(size_t)255));
+        p += sb;
+        ws_bytes -= sb;
+    }
+    if (K > kOutLds) {
+        const size_t fit = ws_bytes / gathered_codes_bytes(N, 32), k_blocks = (size_t)((K + 31) & ~31) / 32;
+        L.cap = (int)(fit < k_blocks ? fit : k_blocks) * 32;
+        if (L.cap > 0) L.codes = reinterpret_cast<uint16_t*>(p);
+    }
+    return L;
 }
 
 hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                              hipEvent_t ev_stop) {
     const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-    const int cap = a.ws ? gemm_tiled_code_cap(a.N, a.K, a.ws_bytes) : 0;
-    uint16_t* wo_all = cap > 0 ? static_cast<uint16_t*>(a.ws) : nullptr;
-    if (wo_all && !a.codes_gathered) {
-        void (*g)(int, int, int, const int32_t*, const int32_t*, const int8_t*, uint16_t*) =
-            a.bf16 ? (a.fp8 ? gather_outlier_codes<true, true> : gather_outlier_codes<true, false>)
-                   : (a.fp8 ? gather_outlier_codes<false, true> : gather_outlier_codes<false, false>);
-        const int row_blocks = (a.N + 31) / 32, blocks = row_blocks < 512 ? row_blocks : 512;
-        g<<<blocks, kGatherThreads, 0, stream>>>(a.N, a.K, cap, a.idx, a.n_out, a.CB, wo_all);
+    const TiledLayout L = tiled_layout(a.M, a.N, a.K, a.ws, a.ws_bytes);
+    uint16_t* gather_to = a.codes_gathered ? nullptr : L.codes;
+    if (gather_to != nullptr || L.split > 1) {
+        void (*g)(int, int, int, const int32_t*, const int32_t*, const int8_t*, uint16_t*, uint32_t*, int) =
+            a.bf16 ? (a.fp8 ? gemm_prep<true, true> : gemm_prep<true, false>)
+                   : (a.fp8 ? gemm_prep<false, true> : gemm_prep<false, false>);
+        const int row_blocks = (a.N + 31) / 32;
+        const int blocks = gather_to == nullptr ? 1 : row_blocks < 512 ? row_blocks : 512;
+        g<<<blocks, kGatherThreads, 0, stream>>>(a.N, a.K, L.cap, a.idx, a.n_out, a.CB, gather_to,
+                                                 L.counters, L.split > 1 ? L.n_counters : 0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 grid(tiles_m * tiles_n), block(kThreads);
-    void (*fn)(int, int, int, int, int, const int8_t*, const float*, const int32_t*,
-               const int32_t*, const uint16_t*, const int8_t*, const float*, const uint16_t*,
-               uint16_t*, int32_t*, float*, const uint16_t*, int) =
-        a.bf16 ? (a.fp8 ? gemm_tiled_kernel<true, true> : gemm_tiled_kernel<true, false>)
-               : (a.fp8 ? gemm_tiled_kernel<false, true> : gemm_tiled_kernel<false, false>);
+    dim3 grid(tiles_m * tiles_n * L.split), block(kThreads);
+    typedef void (*kernel_t)(int, int, int, int, int, const int8_t*, const float*, const int32_t*,
+                             const int32_t*, const uint16_t*, const int8_t*, const float*,
+                             const uint16_t*, uint16_t*, int32_t*, float*, const uint16_t*, int, int,
+                             uint32_t*, int32_t*);
+    const kernel_t fn =
+        L.split > 1
+            ? (a.bf16 ? (a.fp8 ? gemm_tiled_kernel<true, true, true> : gemm_tiled_kernel<true, false, true>)
+                      : (a.fp8 ? gemm_tiled_kernel<false, true, true> : gemm_tiled_kernel<false, false, true>))
+            : (a.bf16 ? (a.fp8 ? gemm_tiled_kernel<true, true, false> : gemm_tiled_kernel<true, false, false>)
+                      : (a.fp8 ? gemm_tiled_kernel<false, true, false> : gemm_tiled_kernel<false, false, false>));
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(fn, grid, block, 0, stream, ev_start, ev_stop, 0, a.M, a.N, a.K,
                               tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB,
-                              a.bias, a.Y, a.C_i32, a.C_f32, wo_all, cap);
+                              a.bias, a.Y, a.C_i32, a.C_f32, L.codes, L.cap, L.split, L.counters,
+                              L.part);
     } else {
         fn<<<grid, block, 0, stream>>>(a.M, a.N, a.K, tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out,
-                                       a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32, a.C_f32, wo_all,
-                                       cap);
+                                       a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32, a.C_f32, L.codes,
+                                       L.cap, L.split, L.counters, L.part);
     }
     return hipGetLastError();
 }

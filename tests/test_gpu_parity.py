@@ -156,6 +156,63 @@ def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8):
         assert torch.equal(Y2.view(torch.int16).cpu(), Y2_none.view(torch.int16).cpu())
 
 
+# ---- K split over several workgroups per tile (few tiles, long K) -----------
+SPLIT = [
+    # M, N, K, dtype, planted outlier columns
+    (300, 700, 4096, F16, 40),    # 6 tiles, K split in 4; codes gathered too
+    (40, 64, 57344, BF16, 3),     # 1 tile, split in 8
+    (520, 300, 2048, BF16, 0),    # 6 tiles, split in 2; three tile rows
+]
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
+@pytest.mark.parametrize("M,N,K,dt,nout", SPLIT, ids=[f"{r[0]}x{r[1]}x{r[2]}" for r in SPLIT])
+def test_split_k_matches_unsplit(M, N, K, dt, nout, fp8):
+    """The split product (default workspace) against the unsplit one (no
+    workspace): int8 accumulators and Y bit for bit; FP8 accumulators within
+    fp32 reassociation error, Y within one 16-bit step.  Two split runs give
+    the same bits."""
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    from gpu_helpers import to_torch
+    wl = synth.make_random(M, N, K, dt, seed=7 * M + K, n_outlier_cols=nout, bias_sigma=0.01)
+    dev = torch.device("cuda:0")
+    X, W = to_torch(wl.X, dt, dev), to_torch(wl.W, dt, dev)
+    bias = to_torch(wl.bias, dt, dev)
+    if fp8:
+        CB, SCB = pkg.quantize_weight_fp8(W)
+        q = pkg.quantize_act_fp8(X, wl.threshold)
+    else:
+        CB, SCB = pkg.quantize_weight(W)
+        q = pkg.quantize_act(X, wl.threshold)
+    log(f"[parity] split K {M}x{N}x{K} fp8={fp8} n_out={int(q.n_out.item())}")
+    cdt = torch.float32 if fp8 else torch.int32
+
+    def run(workspace):
+        C = torch.empty((M, N), dtype=cdt, device=dev)
+        if fp8:
+            Y = pkg.matmul_fp8(q, CB, SCB, bias=bias, C_f32=C, workspace=workspace)
+        else:
+            Y = pkg.matmul(q, CB, SCB, bias=bias, C_i32=C, workspace=workspace)
+        return Y.view(torch.int16).cpu(), C.cpu()
+
+    Y0, C0 = run((None, 0))
+    Y1, C1 = run(None)
+    Y2, C2 = run(None)
+    assert torch.equal(Y1, Y2) and torch.equal(C1, C2)
+    if not fp8:
+        assert torch.equal(C1, C0)
+        assert torch.equal(Y1, Y0)
+    else:
+        scale = C0.abs().max().item()
+        assert (C1 - C0).abs().max().item() <= 1e-5 * scale
+        # at most one 16-bit rounding step apart (plus a hair near zero)
+        ft = torch.float16 if dt == F16 else torch.bfloat16
+        y0, y1 = Y0.view(ft).float(), Y1.view(ft).float()
+        step = 2.0 ** (-10 if dt == F16 else -7)
+        assert ((y1 - y0).abs() <= step * y0.abs() + 1e-6 * y0.abs().max()).all()
+
+
 @pytest.mark.parametrize("M", [5, 48])
 def test_threshold_boundary_and_zero_rows(orc, M):
     wl = synth.make_random(M, 70, 128, F16, seed=23)
