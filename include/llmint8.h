@@ -118,9 +118,14 @@ llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t
                                     int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of optional device workspace llmint8_matmul can use for M x N x K:
- * for M > 16, 64 * ceil(N / 32) * min(K rounded up to 32, 512) (room for the
- * weight codes at 512 outlier columns), else 0.  0 for invalid sizes. */
+/* Bytes of optional device workspace llmint8_matmul can use for M x N x K
+ * (0 for M <= 16 and for invalid sizes).  For M > 16 it is the sum of:
+ *   - split K, when T = ceil(M/256) * ceil(N/256) tiles fill at most half
+ *     of the 256 CUs (T <= 128): S = min(floor(256/T), floor(K/1024), 8) workgroups per
+ *     tile (if S >= 2), needing 4T bytes of counters rounded up to 256, then
+ *     S * T * 256 KiB of partial tiles;
+ *   - 64 * ceil(N / 32) * min(K rounded up to 32, 512) bytes: the weight
+ *     codes at 512 outlier columns. */
 size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -136,15 +141,21 @@ size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
  *   C_i32  [M,N] int32 out or NULL: when given, the same kernels also store the
  *          exact int8 accumulators (for parity checks).
  *   workspace  optional scratch, 16-byte aligned; NULL / 0 bytes is always
- *          valid.  For M > 16 and more than 16 outlier columns, the weight
- *          codes at the outlier columns are first gathered into it (one
- *          extra kernel), which makes the outlier part of the product several
- *          times faster.  W bytes hold 32 * floor(W / (64 * ceil(N / 32) * 32))
- *          columns (at most K): llmint8_matmul_workspace_size bytes hold 512,
- *          64 * ceil(N / 32) * K rounded up to 32 hold every column.  With
- *          more outlier columns than that (n_outliers is read on the device)
- *          the product gathers the codes itself, as without a workspace.
- *          The contents need no initialization and are not kept.
+ *          valid.  For M > 16 it is used in this order:
+ *          - the split-K region (sizes at llmint8_matmul_workspace_size),
+ *            when the shape splits and the workspace holds it: the product
+ *            then spreads K over several workgroups per tile;
+ *          - the rest, R bytes, for the weight codes at the outlier columns
+ *            beyond the first 16, gathered once per call (a small kernel
+ *            ahead of the GEMM), which makes the outlier part of the product
+ *            several times faster.  R bytes hold
+ *            32 * floor(R / (64 * ceil(N / 32) * 32)) columns, at most K:
+ *            512 at the default size, every column with
+ *            64 * ceil(N / 32) * (K rounded up to 32) bytes.  With more
+ *            outlier columns than that (n_outliers is read on the device)
+ *            the product gathers the codes itself, as without a workspace.
+ *          The contents need no initialization and are not kept.  Calls
+ *          that share a workspace must not overlap.
  */
 llmint8_status llmint8_matmul(int dtype, int64_t M, int64_t N, int64_t K,
                               const int8_t* CA, const float* SCA, const int32_t* outlier_idx,

@@ -43,7 +43,7 @@
 //    stores.  The tile's scales, bias and the weight codes of its first 16
 //    outlier columns are loaded once, with the prologue's stage loads, and
 //    kept in LDS.
-//  * Few tiles (under half the CUs, e.g. M = 512 against a 57344-long K):
+//  * Few tiles (at most half the CUs, e.g. M = 512 against a 57344-long K):
 //    given a workspace, K is split over up to 8 workgroups per tile.  Each
 //    stores its int32 (FP8: fp32) accumulators there and counts itself in
 //    with an atomic; the last to arrive adds the partial sums in split order
@@ -571,7 +571,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 // columns (a multiple of 32).
 static size_t gathered_codes_bytes(int64_t N, int64_t cap) { return (size_t)((N + 31) / 32) * 64 * cap; }
 
-// Workgroups per tile: split K when the tiles fill under half the CUs, into
+// Workgroups per tile: split K when the tiles fill at most half the CUs, into
 // as many parts as keep one workgroup per CU, each at least kMinSplitStages
 // stages long.
 static int split_of(int64_t M, int64_t N, int64_t K) {
