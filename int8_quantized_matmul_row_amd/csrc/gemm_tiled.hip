@@ -182,7 +182,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // 16-bit values (0 past n_out): row r, column e at s_wo[r * kOutLds + e]
     __shared__ __attribute__((aligned(16))) uint16_t s_wo[BN * kOutLds];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     // SPLIT: workgroup b takes split ks = b % split of tile b / split, K
     // stages [ks nk / split, (ks + 1) nk / split); otherwise split is 1
@@ -417,8 +417,12 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // columns of one output row.  One 32-row block at a time: dequantize, add
     // the outlier product, scale, bias, round, and stage 8-byte pieces in LDS.
     __syncthreads();  // every wave is done reading the stage buffers
-    const int kh = lane >> 5;
-    const int m_lane = wm * 128 + rr;              // + 32 i
+    // the lane index again, from v_mbcnt (opaque, so that it is not kept in a
+    // register across the K loop)
+    int lane_e;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+    const int kh = lane_e >> 5, rr_e = lane_e & 31, tid_e = wave * 64 + lane_e;
+    const int m_lane = wm * 128 + rr_e;              // + 32 i
     const int n_lane = wn * 128 + 4 * kh;          // + 32 j + 8 (v/4) + v%4
     uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
     typedef typename Vec16<BF16>::type vec_t;
@@ -432,7 +436,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             wo_blocks[j] = wo_all + gathered_block(min((n0 + wn * 128 + 32 * j) / 32, row_blocks - 1), 0, wo_cap) +
-                           rr * 16 + 8 * kh;
+                           rr_e * 16 + 8 * kh;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -469,13 +473,13 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const v8u16 raw = *reinterpret_cast<const v8u16*>(
-                    s_wo + (wn * 128 + 32 * j + rr) * kOutLds + 8 * kh);
+                    s_wo + (wn * 128 + 32 * j + rr_e) * kOutLds + 8 * kh);
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
         // further outlier k-blocks (more than 16 outlier columns)
         if (gathered) {
-            // the codes gathered beforehand: block (row block, j0 / 16), row rr,
+            // the codes gathered beforehand: block (row block, j0 / 16), row l % 32,
             // columns 8 kh .. 8 kh + 7.  Four k-blocks per round, all their
             // loads issued first (one wave per SIMD: the latency of one round
             // of loads is not hidden by anything else); blocks past n_out
@@ -514,23 +518,57 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             for (int j0 = kOutLds; j0 < n_out; j0 += 16) {
                 const vec_t xa = __builtin_bit_cast(
                     vec_t, *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + j0 + 8 * kh));
-                // columns past n_out read the last outlier column (no branch
-                // around a load) and are masked to 0
-                int kcol[8];
-                uint32_t keep = 0;
+                // The block's 16 columns are read as uniform (scalar) values;
+                // lanes with kh = 1 take the second 8.  Adjacent columns from a
+                // multiple of 8 on (every block when t = 0 makes every column
+                // an outlier) are one 8-byte load per row; otherwise one byte
+                // load each, columns past n_out reading the last outlier
+                // column (no branch around a load) and masked to 0.
+                const int first = idx[j0], last = idx[min(j0 + 15, n_out - 1)];
+                int b[4][8];
+                uint32_t keep = 0xffu;
+                if (j0 + 16 <= n_out && last - first == 15 && (first & 7) == 0) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int jj = j0 + 8 * kh + e;
-                    kcol[e] = idx[min(jj, n_out - 1)];
-                    keep |= (jj < n_out ? 1u : 0u) << e;
+                    for (int j = 0; j < 4; ++j) {
+                        const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr_e, N - 1) * K;
+                        const uint2 w8 = *reinterpret_cast<const uint2*>(cb + first + 8 * kh);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) b[j][e] = (int)((e < 4 ? w8.x : w8.y) >> (8 * (e & 3)));
+                    }
+                } else {
+                    int kcol[8];
+                    keep = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        int c0 = idx[min(j0 + e, n_out - 1)], c1 = idx[min(j0 + 8 + e, n_out - 1)];
+                        asm volatile("" : "+s"(c0), "+s"(c1));
+                        kcol[e] = kh ? c1 : c0;
+                        keep |= (j0 + 8 * kh + e < n_out ? 1u : 0u) << e;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr_e, N - 1) * K;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) b[j][e] = cb[kcol[e]];
+                    }
+                    // all 32 byte loads in flight before the first wait
+                    asm volatile(""
+                                 : "+v"(b[0][0]), "+v"(b[0][1]), "+v"(b[0][2]), "+v"(b[0][3]),
+                                   "+v"(b[0][4]), "+v"(b[0][5]), "+v"(b[0][6]), "+v"(b[0][7]),
+                                   "+v"(b[1][0]), "+v"(b[1][1]), "+v"(b[1][2]), "+v"(b[1][3]),
+                                   "+v"(b[1][4]), "+v"(b[1][5]), "+v"(b[1][6]), "+v"(b[1][7]));
+                    asm volatile(""
+                                 : "+v"(b[2][0]), "+v"(b[2][1]), "+v"(b[2][2]), "+v"(b[2][3]),
+                                   "+v"(b[2][4]), "+v"(b[2][5]), "+v"(b[2][6]), "+v"(b[2][7]),
+                                   "+v"(b[3][0]), "+v"(b[3][1]), "+v"(b[3][2]), "+v"(b[3][3]),
+                                   "+v"(b[3][4]), "+v"(b[3][5]), "+v"(b[3][6]), "+v"(b[3][7]));
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr, N - 1) * K;
                     v8u16 raw;
 #pragma unroll
                     for (int e = 0; e < 8; ++e)  // exact in fp16 and bf16
-                        raw[e] = (uint16_t)(narrow16<BF16>(code_value<FP8>(cb[kcol[e]])) &
+                        raw[e] = (uint16_t)(narrow16<BF16>(code_value<FP8>((int8_t)b[j][e])) &
                                             (0u - ((keep >> e) & 1u)));
                     f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
                 }
@@ -553,14 +591,14 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     const int rows = min(BM, M - m0), cols = min(BN, N - n0);
     if ((N & 7) == 0) {
         // 32 lanes per 512-byte row, 8 rows per pass of the workgroup
-        const int c8 = (tid & 31) * 8;
-        for (int r = tid >> 5; r < rows; r += kThreads / 32) {
+        const int c8 = (tid_e & 31) * 8;
+        for (int r = tid_e >> 5; r < rows; r += kThreads / 32) {
             if (c8 < cols)
                 *reinterpret_cast<v4i*>(Y + (size_t)(m0 + r) * N + n0 + c8) =
                     *reinterpret_cast<const v4i*>(smem + r * kYStride + c8 * 2);
         }
     } else {
-        for (int e = tid; e < rows * BN; e += kThreads) {
+        for (int e = tid_e; e < rows * BN; e += kThreads) {
             const int r = e / BN, c = e - r * BN;
             if (c < cols) Y[(size_t)(m0 + r) * N + n0 + c] = ys[r * (kYStride / 2) + c];
         }
