@@ -8,9 +8,11 @@
 // vectors), section "Usage" (recovered weight CB * SCB / 127).
 //
 // Design (gfx950: 256 CUs in 8 XCDs, 160 KiB LDS per CU, 64 LDS banks):
-//  * Workgroup tile 256 x 256; 4 waves in a 2 x 2 grid, each wave owns a
-//    128 x 128 sub-tile = 4 x 4 blocks of 32 x 32 (256 accumulators per lane,
-//    in AGPRs).  One workgroup per CU.
+//  * Workgroup tile 256 x 256; 8 waves in a 2 x 4 grid, each wave owns a
+//    128 x 64 sub-tile = 4 x 2 blocks of 32 x 32 (128 accumulators per lane,
+//    in AGPRs).  One workgroup per CU, two waves per SIMD, so that one wave's
+//    MFMAs run while the other waits (1-2% faster than 4 waves of 128 x 128
+//    with twice the accumulators; the layout is a compile-time choice).
 //  * K advances in 64-byte stages through a 4-deep ring of LDS buffers
 //    (A 256 x 64 + B 256 x 64 bytes each, 128 KiB in all).  Stages are filled
 //    by global_load_lds_dwordx4: each wave instruction moves 16 rows x 64 bytes
@@ -64,7 +66,12 @@ namespace {
 constexpr int BM = 256, BN = 256, BKS = 64;
 constexpr int kStages = 4;
 constexpr int kStageBytes = (BM + BN) * BKS;  // 32 KiB
-constexpr int kThreads = 256;
+constexpr int kWavesN = 4;                  // waves along N (2 along M)
+constexpr int kWaves = 2 * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int JB = 8 / kWavesN;             // 32-column blocks per wave
+constexpr int kWaveN = 32 * JB;             // columns per wave
+constexpr int kDmaRows = BM / kWaves / 16;  // stage-load instructions per operand and wave
 constexpr int kGroupM = 8;
 constexpr int kOutLds = 16;  // outlier columns whose weight codes are staged in LDS
 constexpr int kGatherThreads = 256;
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(kGatherThreads) void gemm_prep(
 }
 
 template <bool BF16, bool FP8, bool SPLIT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const int8_t* __restrict__ CA, const float* __restrict__ SCA,
                        const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
@@ -183,7 +190,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     __shared__ __attribute__((aligned(16))) uint16_t s_wo[BN * kOutLds];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
     // SPLIT: workgroup b takes split ks = b % split of tile b / split, K
     // stages [ks nk / split, (ks + 1) nk / split); otherwise split is 1
     if constexpr (!SPLIT) split = 1;
@@ -199,28 +206,28 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // the logical chunk (p%4) ^ ((p/16)&3).  Rows past M / N re-read the last
     // valid row (their results are never stored).
     const int dchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
-    const int8_t* pa[4];
-    const int8_t* pb[4];
+    const int8_t* pa[kDmaRows];
+    const int8_t* pb[kDmaRows];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wave + 16 * i + (lane >> 2);
+    for (int i = 0; i < kDmaRows; ++i) {
+        const int r = 16 * kDmaRows * wave + 16 * i + (lane >> 2);
         pa[i] = CA + (size_t)min(m0 + r, M - 1) * K + (size_t)kt_begin * BKS + dchunk;
         pb[i] = CB + (size_t)min(n0 + r, N - 1) * K + (size_t)kt_begin * BKS + dchunk;
     }
-    const uint32_t lds_base = lds_address(smem) + 64 * wave * BKS;  // this wave's rows
+    const uint32_t lds_base = lds_address(smem) + 16 * kDmaRows * wave * BKS;  // this wave's rows
     auto issue = [&](int kt) {
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (kt % kStages) * kStageBytes);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(pa[i] + (size_t)kt * BKS, st + 16 * i * BKS);
+        for (int i = 0; i < kDmaRows; ++i) dma16(pa[i] + (size_t)kt * BKS, st + 16 * i * BKS);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(pb[i] + (size_t)kt * BKS, st + BM * BKS + 16 * i * BKS);
+        for (int i = 0; i < kDmaRows; ++i) dma16(pb[i] + (size_t)kt * BKS, st + BM * BKS + 16 * i * BKS);
     };
 
     // ---- fragments: lane l reads row (l & 31) of each 32-row block, chunk
     // 2 ks + l/32 of the stage.  Fragment f < 4 is A block f, f >= 4 is B block
     // f - 4.
     const int rr = lane & 31;
-    const int a_off = wm * 128 * BKS, b_off = BM * BKS + wn * 128 * BKS;
+    const int a_off = wm * 128 * BKS, b_off = BM * BKS + wn * kWaveN * BKS;
     auto read_frag = [&](int kt, int ks, int f) -> v4i {
         const int slot = ((2 * ks + (lane >> 5)) ^ ((rr >> 2) & 3)) * 16;
         const int off = (kt % kStages) * kStageBytes + slot +
@@ -229,11 +236,11 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     };
 
     typedef typename TileAcc<FP8>::type acc_t;
-    acc_t acc[4][4];
+    acc_t acc[4][JB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{};
+        for (int j = 0; j < JB; ++j) acc[i][j] = acc_t{};
 
     // epilogue operands, fetched now so their latency hides under the K loop
     const int n_out = *n_out_ptr;
@@ -243,8 +250,9 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // clamped address (a load under a branch is awaited where the branch
     // rejoins).  Outlier gather: lane column e = tid % 16, rows tid/16 + 16 q;
     // lanes past n_out read column 0 (discarded).
-    float sa_raw = SCA[min(m0 + tid, M - 1)];
-    const int n_sb = min(n0 + tid, N - 1);
+    const int t8 = kThreads > 256 ? (tid & 255) : tid;  // threads 256 and on repeat 0..255
+    float sa_raw = SCA[min(m0 + t8, M - 1)];
+    const int n_sb = min(n0 + t8, N - 1);
     float sb_raw = SCB[n_sb];
     uint16_t bias_raw = *(bias ? bias + n_sb : XO);  // XO: any readable element
     const int e_out = tid & (kOutLds - 1);
@@ -265,25 +273,28 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // register versions with hundreds of copies).  All loads are awaited
     // before the epilogue reuses the ring.
     issue(0);
-    int32_t wo_raw[kOutLds];
+    constexpr int kWoPasses = BN * kOutLds / kThreads;  // rows tid/16 + (kThreads/16) q
+    int32_t wo_raw[kWoPasses];
 #pragma unroll
-    for (int q = 0; q < kOutLds; ++q)
-        wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + 16 * q, N - 1) * K + e_col];
+    for (int q = 0; q < kWoPasses; ++q)
+        wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + (kThreads / 16) * q, N - 1) * K + e_col];
     issue(min(1, nk - 1));
     issue(min(2, nk - 1));
-    wait_vmcnt<16>();  // stage 0 and everything issued before stage 1
+    wait_vmcnt<4 * kDmaRows>();  // stage 0 and everything issued before stage 1
     // the values are used from here on only (the compiler would otherwise
     // hoist their conversions above the stage loads, and wait there)
     asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw));
 #pragma unroll
-    for (int q = 0; q < kOutLds; ++q) asm volatile("" : "+v"(wo_raw[q]));
-    s_sa[tid] = sa_raw;
-    s_sb[tid] = sb_raw / code_max<FP8>();
-    s_bias[tid] = bias ? widen16<BF16>(bias_raw) : 0.0f;
+    for (int q = 0; q < kWoPasses; ++q) asm volatile("" : "+v"(wo_raw[q]));
+    if (kThreads == 256 || tid < 256) {
+        s_sa[tid] = sa_raw;
+        s_sb[tid] = sb_raw / code_max<FP8>();
+        s_bias[tid] = bias ? widen16<BF16>(bias_raw) : 0.0f;
+    }
     const uint32_t e_mask = e_valid ? 0xFFFFu : 0u;  // a mask, not a select: no branches
 #pragma unroll
-    for (int q = 0; q < kOutLds; ++q)
-        s_wo[((tid >> 4) + 16 * q) * kOutLds + e_out] =
+    for (int q = 0; q < kWoPasses; ++q)
+        s_wo[((tid >> 4) + (kThreads / 16) * q) * kOutLds + e_out] =
             (uint16_t)(narrow16<BF16>(code_value<FP8>((int8_t)wo_raw[q])) & e_mask);
     stage_barrier();
 
@@ -303,39 +314,40 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                                                           __builtin_shufflevector(a, a, 4, 5, 6, 7), c, 0, 0, 0);
         }
     };
-    // Stage pipeline: MFMA q of a stage is block (i, j) = (q/4, q%4).  A block
-    // i is refilled with stage kt+1 in place right after its last use (MFMA
-    // 4i+3); the B blocks, used until the stage's last MFMAs, have a second
-    // register set that takes stage kt+1 during the stage's first four MFMAs.
+    // Stage pipeline: MFMA q of a stage is block (i, j) = (q/JB, q%JB).  A
+    // block i is refilled with stage kt+1 in place right after its last use
+    // (MFMA JB i + JB-1); the B blocks, used until the stage's last MFMAs, have
+    // a second register set that takes stage kt+1 during its first JB MFMAs.
+    // The wave's stage loads go out with the even MFMAs.
     // Stages run in groups of four, so that the two B sets swap statically and
     // the ring slot u = kt % 4 is a constant (every LDS offset folds into the
     // instruction's immediate).  The order is pinned with sched_barrier.
     auto read_frag8 = [&](int u, int f) -> v8i {
         return cat8(read_frag(u, 0, f), read_frag(u, 1, f));
     };
-    v8i ga[4], gb0[4], gb1[4];
+    v8i ga[4], gb0[JB], gb1[JB];
 #pragma unroll
     for (int f = 0; f < 4; ++f) ga[f] = read_frag8(0, f);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) gb0[f] = read_frag8(0, 4 + f);
-    auto stage = [&](int kt, int u, v8i (&bc)[4], v8i (&bn)[4]) {
-        // stage kt+1 must have landed; issued after it: stage kt+2 (8 loads)
-        wait_vmcnt<8>();
+    for (int f = 0; f < JB; ++f) gb0[f] = read_frag8(0, 4 + f);
+    auto stage = [&](int kt, int u, v8i (&bc)[JB], v8i (&bn)[JB]) {
+        // stage kt+1 must have landed; issued after it: stage kt+2
+        wait_vmcnt<2 * kDmaRows>();
         stage_barrier();
         const int un = (u + 1) & 3;
         const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
         const size_t kd = (size_t)min(kt + 3, nk - 1) * BKS;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int i = q >> 2, j = q & 3;
+        for (int q = 0; q < 4 * JB; ++q) {
+            const int i = q / JB, j = q % JB;
             acc[i][j] = mma(bc[j], ga[i], acc[i][j]);
             // (at the last stage these read a stale buffer; unused)
-            if (q < 4) bn[q] = read_frag8(un, 4 + q);
-            if (j == 3) ga[i] = read_frag8(un, i);
-            if ((q & 1) == 0) {
-                const int d = q >> 1;  // 0..3: A rows, 4..7: B rows
-                if (d < 4) dma16(pa[d] + kd, st + 16 * d * BKS);
-                else dma16(pb[d - 4] + kd, st + BM * BKS + 16 * (d - 4) * BKS);
+            if (q < JB) bn[q] = read_frag8(un, 4 + q);
+            if (j == JB - 1) ga[i] = read_frag8(un, i);
+            if ((q & 1) == 0 && (q >> 1) < 2 * kDmaRows) {
+                const int d = q >> 1;  // A rows, then B rows
+                if (d < kDmaRows) dma16(pa[d] + kd, st + 16 * d * BKS);
+                else dma16(pb[d - kDmaRows] + kd, st + BM * BKS + 16 * (d - kDmaRows) * BKS);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -364,19 +376,19 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // lane, a wave's 64 lanes contiguous, so every access is a full 1 KiB.
     if constexpr (SPLIT) {
         __shared__ int s_last;
-        constexpr int kWaveWords = 16 * 16 * 64;  // 16 blocks x 16 registers x 64 lanes
+        constexpr int kWaveWords = 4 * JB * 16 * 64;  // blocks x 16 registers x 64 lanes
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JB; ++j)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     // whole vectors through bit casts (a bit cast of one vector
                     // element reads element 0)
                     const v16i bits = __builtin_bit_cast(v16i, acc[i][j]);
                     const v4i w = {bits[4 * c], bits[4 * c + 1], bits[4 * c + 2], bits[4 * c + 3]};
-                    *reinterpret_cast<v4i*>(part + (((size_t)tile * split + ks) * 4 + wave) * kWaveWords +
-                                            ((i * 4 + j) * 4 + c) * 256 + lane * 4) = w;
+                    *reinterpret_cast<v4i*>(part + (((size_t)tile * split + ks) * kWaves + wave) * kWaveWords +
+                                            ((i * JB + j) * 4 + c) * 256 + lane * 4) = w;
                 }
         __threadfence();  // the stores are visible device-wide before the count
         __syncthreads();
@@ -386,11 +398,11 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         __threadfence();
         // sum in split order, this workgroup's own part read back too (the
         // same result whichever workgroup arrives last)
-        const int32_t* p0 = part + (size_t)tile * split * (4 * kWaveWords) + wave * kWaveWords + lane * 4;
+        const int32_t* p0 = part + (size_t)tile * split * (kWaves * kWaveWords) + wave * kWaveWords + lane * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JB; ++j) {
                 acc_t t;
 #pragma unroll
                 for (int sp = 0; sp < kMaxSplit; ++sp) {
@@ -399,8 +411,8 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                         for (int c = 0; c < 4; ++c) {
                             const auto x = __builtin_bit_cast(typename Part4<FP8>::type,
                                                               *reinterpret_cast<const v4i*>(
-                                                                  p0 + (size_t)sp * (4 * kWaveWords) +
-                                                                  ((i * 4 + j) * 4 + c) * 256));
+                                                                  p0 + (size_t)sp * (kWaves * kWaveWords) +
+                                                                  ((i * JB + j) * 4 + c) * 256));
 #pragma unroll
                             for (int e = 0; e < 4; ++e) t[4 * c + e] = sp == 0 ? x[e] : t[4 * c + e] + x[e];
                         }
@@ -423,19 +435,19 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
     const int kh = lane_e >> 5, rr_e = lane_e & 31, tid_e = wave * 64 + lane_e;
     const int m_lane = wm * 128 + rr_e;              // + 32 i
-    const int n_lane = wn * 128 + 4 * kh;          // + 32 j + 8 (v/4) + v%4
+    const int n_lane = wn * kWaveN + 4 * kh;       // + 32 j + 8 (v/4) + v%4
     uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
     typedef typename Vec16<BF16>::type vec_t;
     const int n_pad = (n_out + 31) & ~31;
     // this lane's row of block column 0 in the gathered codes, per j (rows of
     // blocks past N clamp to the last block: their results are not stored)
     const bool gathered = wo_all != nullptr && n_out <= wo_cap;
-    const uint16_t* wo_blocks[4] = {};
+    const uint16_t* wo_blocks[JB] = {};
     if (gathered) {
         const int row_blocks = (N + 31) / 32;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            wo_blocks[j] = wo_all + gathered_block(min((n0 + wn * 128 + 32 * j) / 32, row_blocks - 1), 0, wo_cap) +
+        for (int j = 0; j < JB; ++j)
+            wo_blocks[j] = wo_all + gathered_block(min((n0 + wn * kWaveN + 32 * j) / 32, row_blocks - 1), 0, wo_cap) +
                            rr_e * 16 + 8 * kh;
     }
 #pragma unroll
@@ -443,7 +455,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         const int m = m0 + m_lane + 32 * i;
         if (FP8 ? C_f32 != nullptr : C_i32 != nullptr) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JB; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int n = n0 + n_lane + 32 * j + 8 * (v >> 2) + (v & 3);
@@ -460,9 +472,9 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         const bool have_out = n_out > 0;
         const v8u16 xraw = *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + 8 * kh);
         const float sa = s_sa[m_lane + 32 * i] / code_max<FP8>();
-        v16f f[4];
+        v16f f[JB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JB; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) f[j][v] = (float)acc[i][j][v] * sa;
 
@@ -471,9 +483,9 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             // E4M3 values are exact in fp16 and bf16
             const vec_t xa = __builtin_bit_cast(vec_t, xraw);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JB; ++j) {
                 const v8u16 raw = *reinterpret_cast<const v8u16*>(
-                    s_wo + (wn * 128 + 32 * j + rr_e) * kOutLds + 8 * kh);
+                    s_wo + (wn * kWaveN + 32 * j + rr_e) * kOutLds + 8 * kh);
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
@@ -487,29 +499,35 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             const int j_last = (n_out - 1) & ~15;
             const uint16_t* xo_row = XO + (size_t)min(m, M - 1) * n_pad + 8 * kh;
             for (int j0 = kOutLds; j0 < n_out; j0 += 64) {
-                v8u16 xraw4[4], raw[4][4];
+                v8u16 xraw4[4], raw[4][JB];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int jb = min(j0 + 16 * u, j_last);
                     xraw4[u] = *reinterpret_cast<const v8u16*>(xo_row + jb);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < JB; ++j)
                         raw[u][j] = *reinterpret_cast<const v8u16*>(wo_blocks[j] + 32 * jb);
                 }
                 // every load is issued before the first wait (the compiler
                 // would otherwise sink each one into the branch that uses it)
-                asm volatile(""
-                             : "+v"(xraw4[0]), "+v"(xraw4[1]), "+v"(xraw4[2]), "+v"(xraw4[3]),
-                               "+v"(raw[0][0]), "+v"(raw[0][1]), "+v"(raw[0][2]), "+v"(raw[0][3]),
-                               "+v"(raw[1][0]), "+v"(raw[1][1]), "+v"(raw[1][2]), "+v"(raw[1][3]),
-                               "+v"(raw[2][0]), "+v"(raw[2][1]), "+v"(raw[2][2]), "+v"(raw[2][3]),
-                               "+v"(raw[3][0]), "+v"(raw[3][1]), "+v"(raw[3][2]), "+v"(raw[3][3]));
+                if constexpr (JB == 4)
+                    asm volatile(""
+                                 : "+v"(xraw4[0]), "+v"(xraw4[1]), "+v"(xraw4[2]), "+v"(xraw4[3]),
+                                   "+v"(raw[0][0]), "+v"(raw[0][1]), "+v"(raw[0][2]), "+v"(raw[0][3]),
+                                   "+v"(raw[1][0]), "+v"(raw[1][1]), "+v"(raw[1][2]), "+v"(raw[1][3]),
+                                   "+v"(raw[2][0]), "+v"(raw[2][1]), "+v"(raw[2][2]), "+v"(raw[2][3]),
+                                   "+v"(raw[3][0]), "+v"(raw[3][1]), "+v"(raw[3][2]), "+v"(raw[3][3]));
+                else
+                    asm volatile(""
+                                 : "+v"(xraw4[0]), "+v"(xraw4[1]), "+v"(xraw4[2]), "+v"(xraw4[3]),
+                                   "+v"(raw[0][0]), "+v"(raw[0][1]), "+v"(raw[1][0]), "+v"(raw[1][1]),
+                                   "+v"(raw[2][0]), "+v"(raw[2][1]), "+v"(raw[3][0]), "+v"(raw[3][1]));
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     if (j0 + 16 * u < n_out) {
                         const vec_t xa = __builtin_bit_cast(vec_t, xraw4[u]);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
+                        for (int j = 0; j < JB; ++j)
                             f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw[u][j]), xa, f[j]);
                     }
                 }
@@ -525,12 +543,12 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                 // load each, columns past n_out reading the last outlier
                 // column (no branch around a load) and masked to 0.
                 const int first = idx[j0], last = idx[min(j0 + 15, n_out - 1)];
-                int b[4][8];
+                int b[JB][8];
                 uint32_t keep = 0xffu;
                 if (j0 + 16 <= n_out && last - first == 15 && (first & 7) == 0) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr_e, N - 1) * K;
+                    for (int j = 0; j < JB; ++j) {
+                        const int8_t* cb = CB + (size_t)min(n0 + wn * kWaveN + 32 * j + rr_e, N - 1) * K;
                         const uint2 w8 = *reinterpret_cast<const uint2*>(cb + first + 8 * kh);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) b[j][e] = (int)((e < 4 ? w8.x : w8.y) >> (8 * (e & 3)));
@@ -546,25 +564,23 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                         keep |= (j0 + 8 * kh + e < n_out ? 1u : 0u) << e;
                     }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int8_t* cb = CB + (size_t)min(n0 + wn * 128 + 32 * j + rr_e, N - 1) * K;
+                    for (int j = 0; j < JB; ++j) {
+                        const int8_t* cb = CB + (size_t)min(n0 + wn * kWaveN + 32 * j + rr_e, N - 1) * K;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) b[j][e] = cb[kcol[e]];
                     }
                     // all 32 byte loads in flight before the first wait
-                    asm volatile(""
-                                 : "+v"(b[0][0]), "+v"(b[0][1]), "+v"(b[0][2]), "+v"(b[0][3]),
-                                   "+v"(b[0][4]), "+v"(b[0][5]), "+v"(b[0][6]), "+v"(b[0][7]),
-                                   "+v"(b[1][0]), "+v"(b[1][1]), "+v"(b[1][2]), "+v"(b[1][3]),
-                                   "+v"(b[1][4]), "+v"(b[1][5]), "+v"(b[1][6]), "+v"(b[1][7]));
-                    asm volatile(""
-                                 : "+v"(b[2][0]), "+v"(b[2][1]), "+v"(b[2][2]), "+v"(b[2][3]),
-                                   "+v"(b[2][4]), "+v"(b[2][5]), "+v"(b[2][6]), "+v"(b[2][7]),
-                                   "+v"(b[3][0]), "+v"(b[3][1]), "+v"(b[3][2]), "+v"(b[3][3]),
-                                   "+v"(b[3][4]), "+v"(b[3][5]), "+v"(b[3][6]), "+v"(b[3][7]));
+#pragma unroll
+                    for (int j = 0; j < JB; j += 2)
+                        asm volatile(""
+                                     : "+v"(b[j][0]), "+v"(b[j][1]), "+v"(b[j][2]), "+v"(b[j][3]),
+                                       "+v"(b[j][4]), "+v"(b[j][5]), "+v"(b[j][6]), "+v"(b[j][7]),
+                                       "+v"(b[j + 1][0]), "+v"(b[j + 1][1]), "+v"(b[j + 1][2]),
+                                       "+v"(b[j + 1][3]), "+v"(b[j + 1][4]), "+v"(b[j + 1][5]),
+                                       "+v"(b[j + 1][6]), "+v"(b[j + 1][7]));
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < JB; ++j) {
                     v8u16 raw;
 #pragma unroll
                     for (int e = 0; e < 8; ++e)  // exact in fp16 and bf16
@@ -576,7 +592,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         }
 
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JB; ++j)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int nl = n_lane + 32 * j + 8 * a4;
