@@ -259,24 +259,34 @@ __device__ __forceinline__ uint2 codes8(v4i x, float scale, float nz) {
 }
 
 // Kernel C: the mask is the OR of the G group masks (one word = 32 columns);
-// exclusive popcount prefixes per word rank the outliers.  Then one wave per
-// row: the row is read in batches of 8 chunks per lane (4096 columns), all
-// loads of a batch in flight; absmax over the non-outlier columns, codes, and
-// the outlier values scattered into XO by rank.  A row of at most 4096
-// columns is read once (its batch stays in registers); longer rows are read
-// again for the codes.
+// exclusive popcount prefixes per word rank the outliers.  Then wpr waves per
+// row (1, or 2 or 4 when rows are few and long): the row is read in batches
+// of 8 chunks per lane (4096 columns), all loads of a batch in flight, each
+// of the row's waves taking a contiguous run of batches; absmax over the
+// non-outlier columns (combined across the row's waves in LDS), codes, and
+// the outlier values scattered into XO by rank.  A wave's run of one batch
+// is read once (it stays in registers); longer runs are read again for the
+// codes.
 template <bool BF16, bool FP8>
 __global__ __launch_bounds__(kThreads) void act_quant_rows(
     const uint16_t* __restrict__ X, int M, int K, const uint32_t* __restrict__ mask_g, int G,
     int8_t* __restrict__ CA, float* __restrict__ SCA, int32_t* __restrict__ idx,
-    int32_t* __restrict__ n_out, uint16_t* __restrict__ XO, CodeGather gather) {
+    int32_t* __restrict__ n_out, uint16_t* __restrict__ XO, int wpr, CodeGather gather) {
     __shared__ uint32_t mw[kMaskWordsMax];
     __shared__ int wpre[kMaskWordsMax];
     __shared__ int scan_lds[4];
+    __shared__ uint32_t s_am[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nchunk = K >> 3, nwords = K >> 5;
     constexpr int B = 8;  // chunks per lane per batch
     const int nbatch = (nchunk + B * kWave - 1) / (B * kWave);
+    // wpr (1, 2 or 4) waves per row: rows_wg rows per workgroup and pass;
+    // this wave takes batches [b_begin, b_end) of row g rows_wg + wave / wpr
+    // of row group g
+    const int rows_wg = 4 / wpr, part = wave & (wpr - 1);
+    const int nb_part = (nbatch + wpr - 1) / wpr;
+    const int b_begin = min(part * nb_part, nbatch), b_end = min(b_begin + nb_part, nbatch);
+    const int row_groups = (M + rows_wg - 1) / rows_wg;
     v4i xv[B];
     auto load_batch = [&](const uint16_t* xrow, int b) {
 #pragma unroll
@@ -289,8 +299,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
     };
     // the first row's first batch is requested before the mask, so that the
     // two latencies overlap
-    const int m_first = blockIdx.x * 4 + wave;
-    if (m_first < M) load_batch(X + (size_t)m_first * K, 0);
+    const int m_first = blockIdx.x * rows_wg + wave / wpr;
+    if (m_first < M && b_begin < b_end) load_batch(X + (size_t)m_first * K, b_begin);
     // the mask and the exclusive prefix of its popcounts; thread t owns a
     // contiguous run of words
     const int per = (nwords + kThreads - 1) / kThreads;
@@ -324,8 +334,11 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
         }
     }
 
-    for (int m = m_first; m < M; m += gridDim.x * 4) {
-        const uint16_t* xrow = X + (size_t)m * K;
+    // row groups: uniform over the workgroup (the row's waves meet at barriers)
+    for (int grp = blockIdx.x; grp < row_groups; grp += gridDim.x) {
+        const int m = grp * rows_wg + wave / wpr;
+        const bool row_ok = m < M;
+        const uint16_t* xrow = X + (size_t)min(m, M - 1) * K;
         auto chunk_bits = [&](int c) -> uint32_t {
             return c < nchunk ? (mw[c >> 2] >> (8 * (c & 3))) & 0xffu : 0xffu;
         };
@@ -343,23 +356,32 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
             }
         };
         uint32_t am2 = 0;  // packed magnitude maxima
-        for (int b = 0; b < nbatch; ++b) {
-            if (b > 0 || m != m_first) load_batch(xrow, b);
-            mask_batch(b);
+        if (row_ok) {
+            for (int b = b_begin; b < b_end; ++b) {
+                if (b > b_begin || grp != (int)blockIdx.x) load_batch(xrow, b);
+                mask_batch(b);
 #pragma unroll
-            for (int j = 0; j < B; ++j)
+                for (int j = 0; j < B; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) am2 = max_u16x2(am2, abs2((uint32_t)xv[j][i]));
+                    for (int i = 0; i < 4; ++i) am2 = max_u16x2(am2, abs2((uint32_t)xv[j][i]));
+            }
         }
-        const uint32_t am = wave_max_u32(max(am2 & 0xffffu, am2 >> 16));
+        uint32_t am = wave_max_u32(max(am2 & 0xffffu, am2 >> 16));
+        if (wpr > 1) {  // the row's waves combine their maxima
+            if (lane == 0) s_am[wave] = am;
+            __syncthreads();
+            for (int t = 0; t < wpr; ++t) am = max(am, s_am[(wave & ~(wpr - 1)) + t]);
+            __syncthreads();  // s_am is written again for the next row group
+        }
+        if (!row_ok) continue;  // no barrier below in this pass
         const float amax = widen16<BF16>((uint16_t)am);
-        if (lane == 0) SCA[m] = amax;
+        if (lane == 0 && part == 0) SCA[m] = amax;
         const float scale = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
         const float nz = opaque_neg_zero();
         int8_t* carow = CA + (size_t)m * K;
         uint16_t* xo = XO + (size_t)m * n_pad;
-        for (int b = 0; b < nbatch; ++b) {
-            if (nbatch > 1) {
+        for (int b = b_begin; b < b_end; ++b) {
+            if (b_end - b_begin > 1) {  // a single batch is still in registers
                 load_batch(xrow, b);
                 mask_batch(b);
             }
@@ -381,7 +403,8 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
                 }
             }
         }
-        for (int j = total + lane; j < n_pad; j += kWave) xo[j] = 0;
+        if (part == 0)
+            for (int j = total + lane; j < n_pad; j += kWave) xo[j] = 0;
     }
 
     // the weight codes at the outlier columns for the product that follows
@@ -468,13 +491,18 @@ hipError_t launch_quantize_act(const void* Xv, bool bf16, bool fp8, int M, int K
         act_colmask_partial<true><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, t, mask_g);
     else
         act_colmask_partial<false><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, t, mask_g);
-    int blocks = (M + 3) / 4;
+    // waves per row: rows that are few (under 2048, half a wave per SIMD or
+    // less) and long share their batches among 2 or 4 waves
+    const int nbatch = (K / 8 + 511) / 512;
+    const int wpr = M >= 2048 ? 1 : nbatch >= 4 ? 4 : nbatch >= 2 ? 2 : 1;
+    const int rows_wg = 4 / wpr;
+    int blocks = (M + rows_wg - 1) / rows_wg;
     if (blocks > 65536) blocks = 65536;
     void (*fn)(const uint16_t*, int, int, const uint32_t*, int, int8_t*, float*, int32_t*, int32_t*,
-               uint16_t*, CodeGather) =
+               uint16_t*, int, CodeGather) =
         bf16 ? (fp8 ? act_quant_rows<true, true> : act_quant_rows<true, false>)
              : (fp8 ? act_quant_rows<false, true> : act_quant_rows<false, false>);
-    fn<<<blocks, kThreads, 0, stream>>>(X, M, K, mask_g, p.groups, CA, SCA, idx, n_out, XO, g);
+    fn<<<blocks, kThreads, 0, stream>>>(X, M, K, mask_g, p.groups, CA, SCA, idx, n_out, XO, wpr, g);
     if (gather != nullptr) gather->out = g.out;
     return hipGetLastError();
 }

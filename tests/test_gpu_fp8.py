@@ -143,6 +143,7 @@ RAGGED = [
     (300, 520, 320, BF16, 3, True),
     (257, 769, 448, BF16, 40, True),   # more than 16 outlier columns
     (513, 257, 1024, F16, 5, False),
+    (37, 100, 8192, BF16, 3, True),    # 2 waves per activation row, odd M
 ]
 
 

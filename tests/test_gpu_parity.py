@@ -59,6 +59,10 @@ RAGGED = [
     (257, 769, 448, BF16, 40, True),
     (40, 64, 57344, BF16, 2, False),
     (8, 96, 133120, F16, 1, False),
+    # few long rows: the activation kernel shares each row among 2 or 4 waves
+    (37, 100, 8192, BF16, 3, True),     # 2 waves per row, odd M (a half-empty row group)
+    (50, 70, 12352, F16, 5, False),     # 4 waves per row, one batch each
+    (21, 40, 20480, F16, 2, True),      # 4 waves per row, the last with no batch
 ]
 
 
