@@ -8,11 +8,11 @@
 // vectors), section "Usage" (recovered weight CB * SCB / 127).
 //
 // Design (gfx950: 256 CUs in 8 XCDs, 160 KiB LDS per CU, 64 LDS banks):
-//  * Workgroup tile 256 x 256; 8 waves in a 2 x 4 grid, each wave owns a
-//    128 x 64 sub-tile = 4 x 2 blocks of 32 x 32 (128 accumulators per lane,
-//    in AGPRs).  One workgroup per CU, two waves per SIMD, so that one wave's
-//    MFMAs run while the other waits (1-2% faster than 4 waves of 128 x 128
-//    with twice the accumulators; the layout is a compile-time choice).
+//  * Workgroup tile 256 x 256; 4 waves in a 2 x 2 grid, each wave owns a
+//    128 x 128 sub-tile = 4 x 4 blocks of 32 x 32 (256 accumulators per lane,
+//    in AGPRs).  One workgroup per CU.  The wave layout is a compile-time
+//    choice: 8 waves of 128 x 64 (two per SIMD) measure within 1% of this
+//    on most shapes and 12% slower with K split.
 //  * K advances in 64-byte stages through a 4-deep ring of LDS buffers
 //    (A 256 x 64 + B 256 x 64 bytes each, 128 KiB in all).  Stages are filled
 //    by global_load_lds_dwordx4: each wave instruction moves 16 rows x 64 bytes
@@ -66,7 +66,7 @@ namespace {
 constexpr int BM = 256, BN = 256, BKS = 64;
 constexpr int kStages = 4;
 constexpr int kStageBytes = (BM + BN) * BKS;  // 32 KiB
-constexpr int kWavesN = 4;                  // waves along N (2 along M)
+constexpr int kWavesN = 2;                  // waves along N (2 along M)
 constexpr int kWaves = 2 * kWavesN;
 constexpr int kThreads = 64 * kWaves;
 constexpr int JB = 8 / kWavesN;             // 32-column blocks per wave
