@@ -394,6 +394,62 @@ def test_linear_workspace_reuse_any_shape(orc):
         compare(wl, g, ref, label=f"reuse {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,nout", [(40, 64, 57344, 3), (300, 700, 4096, 40)],
+                         ids=["split-K", "gathered-codes"])
+def test_tiled_product_graph_replays(M, N, K, nout):
+    """The tiled product with its workspace (split-K counters zeroed by a
+    kernel, outlier codes gathered): replays of a captured HIP graph, with
+    eager work and a call on other inputs between them, match the eager
+    result bit for bit, both for llmint8_matmul and for llmint8_linear."""
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    from gpu_helpers import to_torch
+    dev = torch.device("cuda:0")
+    wl = synth.make_random(M, N, K, BF16, seed=M + K, n_outlier_cols=nout, bias_sigma=0.01)
+    X, W = to_torch(wl.X, BF16, dev), to_torch(wl.W, BF16, dev)
+    bias = to_torch(wl.bias, BF16, dev)
+    X2 = (X * 0.5).contiguous()
+    CB, SCB = pkg.quantize_weight(W)
+    log(f"[parity] graph replays of the tiled product {M}x{N}x{K}")
+    q = pkg.alloc_act(M, K, torch.bfloat16, dev)
+    q2 = pkg.alloc_act(M, K, torch.bfloat16, dev)
+    mws = pkg.matmul_workspace(M, N, K, dev)
+    lws = pkg.linear_workspace(M, N, K, dev)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    C = torch.empty((M, N), dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+
+    def product():
+        pkg.quantize_act(X, wl.threshold, out=q, stream=stream)
+        pkg.matmul(q, CB, SCB, bias=bias, out=Y, C_i32=C, workspace=mws, stream=stream)
+
+    def forward():
+        pkg.linear(X, CB, SCB, bias=bias, threshold=wl.threshold, out=Y, act=q, C_i32=C,
+                   workspace=lws, stream=stream)
+
+    for fn in (product, forward):
+        with torch.cuda.stream(stream):
+            fn()
+        torch.cuda.synchronize()
+        Y0, C0 = Y.clone(), C.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            fn()
+        for r in range(4):
+            Y.zero_()
+            C.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Y, Y0), f"{fn.__name__} replay {r}: Y differs"
+            assert torch.equal(C, C0), f"{fn.__name__} replay {r}: C differs"
+            # other inputs through the same workspace, eagerly, between replays
+            pkg.quantize_act(X2, wl.threshold, out=q2)
+            pkg.matmul(q2, CB, SCB, workspace=mws)
+            pkg.linear(X2, CB, SCB, threshold=wl.threshold, workspace=lws)
+            torch.cuda.synchronize()
+
+
 def test_linear_fused_repeatable_and_graph_replays():
     """The fused forward gives the same bits on every call, and replays of a
     captured HIP graph (with eager work between them) match the eager call."""
