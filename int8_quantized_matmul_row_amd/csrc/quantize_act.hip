@@ -260,7 +260,7 @@ __device__ __forceinline__ uint2 codes8(v4i x, float scale, float nz) {
 
 // Kernel C: the mask is the OR of the G group masks (one word = 32 columns);
 // exclusive popcount prefixes per word rank the outliers.  Then wpr waves per
-// row (1, or 2 or 4 when rows are few and long): the row is read in batches
+// row (1, or 2 or 4 for rows longer than 4096 columns): the row is read in batches
 // of 8 chunks per lane (4096 columns), all loads of a batch in flight, each
 // of the row's waves taking a contiguous run of batches; absmax over the
 // non-outlier columns (combined across the row's waves in LDS), codes, and
@@ -491,10 +491,11 @@ hipError_t launch_quantize_act(const void* Xv, bool bf16, bool fp8, int M, int K
         act_colmask_partial<true><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, t, mask_g);
     else
         act_colmask_partial<false><<<ga, kThreads, 0, stream>>>(X, M, K, p.rows_per_group, t, mask_g);
-    // waves per row: rows that are few (under 2048, half a wave per SIMD or
-    // less) and long share their batches among 2 or 4 waves
+    // waves per row: a row longer than one batch (4096 columns) is shared by
+    // 2 or 4 waves, so that fewer waves read their run twice and short M
+    // still fills the CUs
     const int nbatch = (K / 8 + 511) / 512;
-    const int wpr = M >= 2048 ? 1 : nbatch >= 4 ? 4 : nbatch >= 2 ? 2 : 1;
+    const int wpr = nbatch >= 4 ? 4 : nbatch >= 2 ? 2 : 1;
     const int rows_wg = 4 / wpr;
     int blocks = (M + rows_wg - 1) / rows_wg;
     if (blocks > 65536) blocks = 65536;
