@@ -39,6 +39,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 ROTATE_BYTES = 512 << 20     # > 2x the Infinity Cache
+# the largest workload that fits one GPU: 4096 x 28672 x 8192 fp16 with 0.1% outlier columns
+DEFAULT_CONFIG = "sweep_0.1"
 KERNEL_SOURCES = {
     "decode": ["int8_quantized_matmul_row_amd/csrc/linear_decode.hip",
                "int8_quantized_matmul_row_amd/csrc/common.h"],
@@ -126,48 +128,81 @@ def load_traffic(config, family, variant="int8"):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s=12.0, variant="int8"):
-    """The CPU oracle (single-threaded C) on a bounded sample of the same step."""
+def host_cores():
+    """Host cores this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set (the GPU host's share of its CPUs)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(wl, variant="int8", budget_1core_s=8.0, budget_ncore_s=10.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same step.
+
+    The step is quantize_act over all M rows (single-threaded: the outlier set
+    couples the rows) plus the product and output of every row.  Two legs:
+    1 core, rows taken in a fixed random order until the budget is spent; and
+    the same per-row functions on every host core (`host_cores()` threads, each
+    on a contiguous chunk of an evenly spaced row sample sized to the budget).
+    Each leg's time is t(quantize_act) + t(rows) * M / rows.  Returns
+    (all-cores leg, 1-core leg)."""
     import numpy as np
     import oracle
     orc = oracle.get()
     fp8 = variant == "fp8"
-    CB, SCB = (orc.quantize_weight_fp8 if fp8 else orc.quantize_weight)(wl.W, wl.dtype)
-    forward = orc.forward_fp8 if fp8 else orc.forward
-    M = wl.M
-    if M * wl.N * wl.K <= (1 << 28):
-        # whole forward, repeated
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            forward(wl.X, None, wl.dtype, wl.threshold, bias=wl.bias, weight=(CB, SCB))
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 1000:
-                break
-        step_s = el / reps
-        sample = f"full {M}x{wl.N}x{wl.K} forward (quantize_act + matmul), {reps} repetitions"
-    else:
-        t0 = time.perf_counter()
-        CA, SCA, idx, XO = (orc.quantize_act_fp8 if fp8 else orc.quantize_act)(
-            wl.X, wl.dtype, wl.threshold)
-        t_act = time.perf_counter() - t0
-        per_row = 2 * wl.N * wl.K
-        rate = 0.2e9 if fp8 else 1.0e9  # single core, ops/s (E4M3 decode is slower)
-        n_rows = max(2, min(M, int(budget_s * rate / per_row)))
-        rows = np.linspace(0, M - 1, n_rows).astype(np.int64)
-        t0 = time.perf_counter()
-        if fp8:
-            C = orc.fp8_rows(CA, CB, rows)
-            orc.output_rows_fp8(C, SCA, SCB, wl.X, wl.dtype, idx, CB, wl.bias, rows)
-        else:
-            C = orc.int8_rows(CA, CB, rows)
-            orc.output_rows(C, SCA, SCB, wl.X, wl.dtype, idx, CB, wl.bias, rows)
-        t_rows = time.perf_counter() - t0
-        step_s = t_act + t_rows * M / n_rows
-        sample = (f"quantize_act on all {M} rows + matmul on {n_rows} evenly spaced rows, "
-                  f"extrapolated to {M} rows")
-    return {"value": round(2 * M * wl.N * wl.K / step_s / 1e12, 6), "unit": "TOPS", "cores": 1,
-            "kind": "oracle", "sample": sample, "ms_per_step": round(step_s * 1e3, 3)}
+    weight = (orc.quantize_weight_fp8 if fp8 else orc.quantize_weight)(wl.W, wl.dtype)
+    M, N, K = wl.M, wl.N, wl.K
+    ops = 2 * M * N * K
+    t0 = time.perf_counter()
+    act = (orc.quantize_act_fp8 if fp8 else orc.quantize_act)(wl.X, wl.dtype, wl.threshold)
+    t_act = time.perf_counter() - t0
+
+    # 1 core: rows 0 and M-1, then the others in a fixed random order, cycling
+    perm = np.random.default_rng(0).permutation(M)
+    uniq = [0, M - 1] + [int(r) for r in perm if r not in (0, M - 1)] if M > 1 else [0]
+    done, t0 = 0, time.perf_counter()
+    while True:  # chunks of up to 8 rows per call
+        r = np.array([uniq[(done + i) % M] for i in range(min(8, M))], dtype=np.int64)
+        oracle.forward_rows_threaded(orc, act, weight, wl.X, wl.dtype, wl.bias, r, 1, fp8=fp8)
+        done += len(r)
+        el = time.perf_counter() - t0
+        if el >= budget_1core_s:
+            break
+    rate1 = done / el
+    step1 = t_act + M / rate1
+    one = {"value": round(ops / step1 / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+           "sample": (f"quantize_act on all {M} rows ({t_act:.2f} s) + {done} rows of the product "
+                      f"and output on 1 core ({el:.1f} s), extrapolated to {M} rows"
+                      + (f" (the {M} rows cycled)" if done > M else "")),
+           "ms_per_step": round(step1 * 1e3, 3)}
+
+    # every core: a sample sized to the budget, split into per-thread chunks
+    cores = host_cores()
+    n_rows = int(min(M, max(1, rate1 * cores * budget_ncore_s)))
+    threads = min(cores, n_rows)
+    rows = np.unique(np.linspace(0, M - 1, n_rows).round().astype(np.int64))
+    passes, t0 = 0, time.perf_counter()
+    while True:  # whole passes over the sample until the budget is spent
+        oracle.forward_rows_threaded(orc, act, weight, wl.X, wl.dtype, wl.bias, rows, threads,
+                                     fp8=fp8)
+        passes += 1
+        el_n = time.perf_counter() - t0
+        if el_n >= budget_ncore_s / 2:
+            break
+    t_rows = el_n / passes
+    stepn = t_act + t_rows * M / len(rows)
+    full = len(rows) == M
+    alln = {"value": round(ops / stepn / 1e12, 6), "unit": "TOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"quantize_act on all {M} rows ({t_act:.2f} s, 1 thread) + the product and "
+                       f"output of {'all ' if full else ''}{len(rows)}"
+                       f"{'' if full else ' evenly spaced'} rows on {threads} threads "
+                       f"({t_rows:.3g} s per pass, {passes} passes)"
+                       f"{'' if full else f', extrapolated to {M} rows'}"),
+            "ms_per_step": round(stepn * 1e3, 3)}
+    return alln, one
 
 
 def calibrate_copy(torch, dev, nbytes, launches):
@@ -230,9 +265,9 @@ def measured_ceiling(torch, pkg, dev, bound, fp8):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="decode")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--threshold", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
@@ -320,29 +355,25 @@ def main():
     torch.cuda.synchronize()
     n_out = int(q.n_out.item())
 
-    # One graph holds one pass over the weight copies; the timed region replays
-    # it (a decode step is a few microseconds of GPU work, far below the cost of
-    # launching it from Python).
-    per_graph = n_copies
+    # The timed region replays one graph of exactly `steps` steps, step i on
+    # weight copy i % n_copies (a decode step is a few microseconds of GPU
+    # work, far below the cost of launching it from Python).  The graph is
+    # replayed once untimed first.
+    steps = args.steps
     graph = None
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            for i in range(per_graph):
+            for i in range(steps):
                 step(i)
-    reps_graph = max(1, -(-args.steps // per_graph))
-    steps = reps_graph * per_graph if graph is not None else args.steps
+        graph.replay()
+    torch.cuda.synchronize()
 
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if graph is not None:
-        for _ in range(2):
-            graph.replay()
-    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         g0.record(stream)
         if graph is not None:
-            for _ in range(reps_graph):
-                graph.replay()
+            graph.replay()
         else:
             for i in range(steps):
                 step(i)
@@ -423,7 +454,7 @@ def main():
                               "frac_hbm": round(wq_bytes / wq_ms / 1e6 / HBM_PEAK_GBS, 4)},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, variant=args.variant)
+        result["cpu_baseline"], result["cpu_baseline_1core"] = cpu_baseline(wl, variant=args.variant)
     print(json.dumps(result), flush=True)
 
 

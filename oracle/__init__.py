@@ -261,6 +261,35 @@ class Oracle:
         return dict(CB=CB, SCB=SCB, CA=CA, SCA=SCA, idx=idx, XO=XO, C=C, Y=Y)
 
 
+def forward_rows_threaded(orc: Oracle, act, weight, X, dtype, bias, rows, threads: int,
+                          fp8: bool = False):
+    """C and Y of `rows` from the activation outputs act = (CA, SCA, idx, XO) and
+    weight = (CB, SCB): the unchanged per-row functions (int8_rows or fp8_rows, then
+    output_rows or output_rows_fp8), each thread on a contiguous chunk of the rows.
+    Once the outlier set and the scales are fixed the rows are independent, so the
+    result is the same for every thread count.  ctypes releases the GIL for the
+    duration of each foreign call, so the chunks run on separate cores."""
+    import concurrent.futures as cf
+    CA, SCA, idx, _ = act
+    CB, SCB = weight
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    threads = max(1, min(int(threads), len(rows)))
+    chunks = np.array_split(rows, threads)
+    prod = orc.fp8_rows if fp8 else orc.int8_rows
+    out = orc.output_rows_fp8 if fp8 else orc.output_rows
+
+    def one(r):
+        C = prod(CA, CB, r)
+        return C, out(C, SCA, SCB, X, dtype, idx, CB, bias, r)
+
+    if threads == 1:
+        parts = [one(rows)]
+    else:
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            parts = list(ex.map(one, chunks))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
 _default: Oracle | None = None
 
 
