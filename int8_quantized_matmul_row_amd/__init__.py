@@ -287,6 +287,35 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _empty(shape, dtype, device, stream=None):
+    """torch.empty for a buffer the library's kernels use on `stream`.  Given a
+    stream, the block is marked as in use by it (record_stream), so that torch's
+    caching allocator does not hand it to other work while kernels on that stream
+    may still read or write it -- the binding allocates on the current stream, and
+    the kernels may run on another."""
+    t = _torch().empty(shape, dtype=dtype, device=device)
+    if stream is not None:
+        t.record_stream(stream)
+    return t
+
+
+def _check_weight(CB, SCB, bias, N, K, device, dtype16, code_dtype):
+    """CB [N,K] of code_dtype, SCB [N] float32, bias None or [N] of dtype16, all
+    contiguous on `device`: the shapes and types the kernels read."""
+    torch = _torch()
+    if CB.dtype != code_dtype or tuple(CB.shape) != (N, K):
+        raise ValueError(f"CB is {CB.dtype} {tuple(CB.shape)}, expected {code_dtype} ({N}, {K})")
+    if SCB.dtype != torch.float32 or tuple(SCB.shape) != (N,):
+        raise ValueError(f"SCB is {SCB.dtype} {tuple(SCB.shape)}, expected torch.float32 ({N},)")
+    _need(CB, "CB", device)
+    _need(SCB, "SCB", device)
+    if bias is not None:
+        if bias.dtype != dtype16 or bias.numel() != N:
+            raise ValueError(f"bias is {bias.dtype} with {bias.numel()} elements, "
+                             f"expected {dtype16} with {N}")
+        _need(bias, "bias", device)
+
+
 def _need(t, name, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -302,8 +331,8 @@ def quantize_weight(W, stream=None, out=None):
     _need(W, "W")
     N, K = W.shape
     CB, SCB = out if out is not None else (
-        torch.empty((N, K), dtype=torch.int8, device=W.device),
-        torch.empty((N,), dtype=torch.float32, device=W.device))
+        _empty((N, K), torch.int8, W.device, stream),
+        _empty((N,), torch.float32, W.device, stream))
     llmint8_quantize_weight(_ptr(W), dtype_code(W), N, K, _ptr(CB), _ptr(SCB), _stream(stream))
     return CB, SCB
 
@@ -317,15 +346,15 @@ class QuantizedAct(NamedTuple):
     dtype: int
 
 
-def alloc_act(M, K, dtype_t, device, fp8: bool = False):
+def alloc_act(M, K, dtype_t, device, fp8: bool = False, stream=None):
     """Output buffers of quantize_act (CA int8) or quantize_act_fp8 (CA uint8)."""
     torch = _torch()
     return QuantizedAct(
-        torch.empty((M, K), dtype=torch.uint8 if fp8 else torch.int8, device=device),
-        torch.empty((M,), dtype=torch.float32, device=device),
-        torch.empty((K,), dtype=torch.int32, device=device),
-        torch.empty((1,), dtype=torch.int32, device=device),
-        torch.empty((max(M * K, 1),), dtype=dtype_t, device=device),
+        _empty((M, K), torch.uint8 if fp8 else torch.int8, device, stream),
+        _empty((M,), torch.float32, device, stream),
+        _empty((K,), torch.int32, device, stream),
+        _empty((1,), torch.int32, device, stream),
+        _empty((max(M * K, 1),), dtype_t, device, stream),
         F16 if dtype_t == torch.float16 else BF16)
 
 
@@ -335,10 +364,10 @@ def quantize_tensor(A, stream=None):
     torch = _torch()
     _need(A, "A")
     R, C = A.shape
-    Q = torch.empty((R, C), dtype=torch.int8, device=A.device)
-    scale = torch.empty((R,), dtype=torch.float32, device=A.device)
+    Q = _empty((R, C), torch.int8, A.device, stream)
+    scale = _empty((R,), torch.float32, A.device, stream)
     n = llmint8_quantize_tensor_workspace_size(R, C)
-    ws = torch.empty((max(n, 1),), dtype=torch.uint8, device=A.device)
+    ws = _empty((max(n, 1),), torch.uint8, A.device, stream)
     llmint8_quantize_tensor(_ptr(A), dtype_code(A), R, C, _ptr(Q), _ptr(scale), _ptr(ws), n,
                             _stream(stream))
     return Q, scale
@@ -349,16 +378,16 @@ def matmul_codes(CA, SCA, CB, SCB, dtype_t, bias=None, out=None, stream=None):
     with no outlier columns -- e.g. two quantize_tensor results (per-tensor
     absmax) -- through llmint8_matmul."""
     M, K = CA.shape
-    q = alloc_act(M, K, dtype_t, CA.device)
+    q = alloc_act(M, K, dtype_t, CA.device, stream=stream)
     q.n_out.zero_()
     q = q._replace(CA=CA, SCA=SCA)
     return matmul(q, CB, SCB, bias=bias, out=out, stream=stream)
 
 
-def act_workspace(M, K, device):
+def act_workspace(M, K, device, stream=None):
     torch = _torch()
     n = llmint8_quantize_act_workspace_size(M, K)
-    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+    return _empty((max(n, 1),), torch.uint8, device, stream), n
 
 
 def quantize_act(X, threshold: float = 6.0, stream=None, out: Optional[QuantizedAct] = None,
@@ -366,8 +395,8 @@ def quantize_act(X, threshold: float = 6.0, stream=None, out: Optional[Quantized
     """X [M,K] fp16/bf16 -> QuantizedAct (outlier columns over all M rows)."""
     _need(X, "X")
     M, K = X.shape
-    q = out if out is not None else alloc_act(M, K, X.dtype, X.device)
-    ws, nbytes = workspace if workspace is not None else act_workspace(M, K, X.device)
+    q = out if out is not None else alloc_act(M, K, X.dtype, X.device, stream=stream)
+    ws, nbytes = workspace if workspace is not None else act_workspace(M, K, X.device, stream)
     llmint8_quantize_act(_ptr(X), dtype_code(X), M, K, float(threshold), _ptr(q.CA), _ptr(q.SCA),
                          _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(ws), nbytes,
                          _stream(stream))
@@ -380,12 +409,12 @@ def outlier_columns(q: QuantizedAct):
     return q.idx[:n].cpu()
 
 
-def matmul_workspace(M, N, K, device):
+def matmul_workspace(M, N, K, device, stream=None):
     """(buffer, bytes) of the optional product workspace (the weight codes at
     the outlier columns, gathered once per call when there are more than 16)."""
     torch = _torch()
     n = llmint8_matmul_workspace_size(M, N, K)
-    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+    return _empty((max(n, 1),), torch.uint8, device, stream), n
 
 
 def matmul(q: QuantizedAct, CB, SCB, bias=None, out=None, C_i32=None, stream=None,
@@ -397,11 +426,12 @@ def matmul(q: QuantizedAct, CB, SCB, bias=None, out=None, C_i32=None, stream=Non
     torch = _torch()
     M, K = q.CA.shape
     N = CB.shape[0]
-    if CB.shape[1] != K:
-        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
     dt_t = torch.float16 if q.dtype == F16 else torch.bfloat16
-    Y = out if out is not None else torch.empty((M, N), dtype=dt_t, device=q.CA.device)
-    ws, nbytes = workspace if workspace is not None else matmul_workspace(M, N, K, q.CA.device)
+    _check_weight(CB, SCB, bias, N, K, q.CA.device, dt_t, torch.int8)
+    Y = out if out is not None else _empty((M, N), dt_t, q.CA.device, stream)
+    if workspace is None:
+        workspace = matmul_workspace(M, N, K, q.CA.device, stream)
+    ws, nbytes = workspace
     args = (q.dtype, M, N, K, _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO),
             _ptr(CB), _ptr(SCB), _ptr(bias), _ptr(Y), _ptr(C_i32), _ptr(ws), nbytes,
             _stream(stream))
@@ -412,10 +442,10 @@ def matmul(q: QuantizedAct, CB, SCB, bias=None, out=None, C_i32=None, stream=Non
     return Y
 
 
-def linear_workspace(M, N, K, device):
+def linear_workspace(M, N, K, device, stream=None):
     torch = _torch()
     n = llmint8_linear_workspace_size(M, N, K)
-    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+    return _empty((max(n, 1),), torch.uint8, device, stream), n
 
 
 def linear(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None, out=None,
@@ -428,11 +458,12 @@ def linear(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None, out=None,
     _need(X, "X")
     M, K = X.shape
     N = CB.shape[0]
-    if CB.shape[1] != K:
-        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
-    q = act if act is not None else alloc_act(M, K, X.dtype, X.device)
-    Y = out if out is not None else torch.empty((M, N), dtype=X.dtype, device=X.device)
-    ws, nbytes = workspace if workspace is not None else linear_workspace(M, N, K, X.device)
+    _check_weight(CB, SCB, bias, N, K, X.device, X.dtype, torch.int8)
+    q = act if act is not None else alloc_act(M, K, X.dtype, X.device, stream=stream)
+    Y = out if out is not None else _empty((M, N), X.dtype, X.device, stream)
+    if workspace is None:
+        workspace = linear_workspace(M, N, K, X.device, stream)
+    ws, nbytes = workspace
     args = (_ptr(X), dtype_code(X), M, N, K, float(threshold), _ptr(CB), _ptr(SCB), _ptr(bias),
             _ptr(Y), _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(C_i32),
             _ptr(ws), nbytes, _stream(stream))
@@ -451,8 +482,8 @@ def quantize_weight_fp8(W, stream=None, out=None):
     _need(W, "W")
     N, K = W.shape
     CB, SCB = out if out is not None else (
-        torch.empty((N, K), dtype=torch.uint8, device=W.device),
-        torch.empty((N,), dtype=torch.float32, device=W.device))
+        _empty((N, K), torch.uint8, W.device, stream),
+        _empty((N,), torch.float32, W.device, stream))
     llmint8_quantize_weight_fp8(_ptr(W), dtype_code(W), N, K, _ptr(CB), _ptr(SCB),
                                 _stream(stream))
     return CB, SCB
@@ -463,8 +494,9 @@ def quantize_act_fp8(X, threshold: float = 6.0, stream=None, out: Optional[Quant
     """X [M,K] fp16/bf16 -> QuantizedAct with CA as uint8 E4M3 codes."""
     _need(X, "X")
     M, K = X.shape
-    q = out if out is not None else alloc_act(M, K, X.dtype, X.device, fp8=True)
-    ws, nbytes = workspace if workspace is not None else act_workspace(M, K, X.device)
+    q = out if out is not None else alloc_act(M, K, X.dtype, X.device, fp8=True,
+                                                  stream=stream)
+    ws, nbytes = workspace if workspace is not None else act_workspace(M, K, X.device, stream)
     llmint8_quantize_act_fp8(_ptr(X), dtype_code(X), M, K, float(threshold), _ptr(q.CA),
                              _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(ws),
                              nbytes, _stream(stream))
@@ -478,11 +510,12 @@ def matmul_fp8(q: QuantizedAct, CB, SCB, bias=None, out=None, C_f32=None, stream
     torch = _torch()
     M, K = q.CA.shape
     N = CB.shape[0]
-    if CB.shape[1] != K:
-        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
     dt_t = torch.float16 if q.dtype == F16 else torch.bfloat16
-    Y = out if out is not None else torch.empty((M, N), dtype=dt_t, device=q.CA.device)
-    ws, nbytes = workspace if workspace is not None else matmul_workspace(M, N, K, q.CA.device)
+    _check_weight(CB, SCB, bias, N, K, q.CA.device, dt_t, torch.uint8)
+    Y = out if out is not None else _empty((M, N), dt_t, q.CA.device, stream)
+    if workspace is None:
+        workspace = matmul_workspace(M, N, K, q.CA.device, stream)
+    ws, nbytes = workspace
     args = (q.dtype, M, N, K, _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO),
             _ptr(CB), _ptr(SCB), _ptr(bias), _ptr(Y), _ptr(C_f32), _ptr(ws), nbytes,
             _stream(stream))
@@ -493,10 +526,10 @@ def matmul_fp8(q: QuantizedAct, CB, SCB, bias=None, out=None, C_f32=None, stream
     return Y
 
 
-def linear_fp8_workspace(M, N, K, device):
+def linear_fp8_workspace(M, N, K, device, stream=None):
     torch = _torch()
     n = llmint8_linear_fp8_workspace_size(M, N, K)
-    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device), n
+    return _empty((max(n, 1),), torch.uint8, device, stream), n
 
 
 def linear_fp8(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None, out=None,
@@ -507,11 +540,12 @@ def linear_fp8(X, CB, SCB, bias=None, threshold: float = 6.0, stream=None, out=N
     _need(X, "X")
     M, K = X.shape
     N = CB.shape[0]
-    if CB.shape[1] != K:
-        raise ValueError(f"CB is {tuple(CB.shape)}, expected [N, {K}]")
-    q = act if act is not None else alloc_act(M, K, X.dtype, X.device, fp8=True)
-    Y = out if out is not None else torch.empty((M, N), dtype=X.dtype, device=X.device)
-    ws, nbytes = workspace if workspace is not None else linear_fp8_workspace(M, N, K, X.device)
+    _check_weight(CB, SCB, bias, N, K, X.device, X.dtype, torch.uint8)
+    q = act if act is not None else alloc_act(M, K, X.dtype, X.device, fp8=True, stream=stream)
+    Y = out if out is not None else _empty((M, N), X.dtype, X.device, stream)
+    if workspace is None:
+        workspace = linear_fp8_workspace(M, N, K, X.device, stream)
+    ws, nbytes = workspace
     args = (_ptr(X), dtype_code(X), M, N, K, float(threshold), _ptr(CB), _ptr(SCB), _ptr(bias),
             _ptr(Y), _ptr(q.CA), _ptr(q.SCA), _ptr(q.idx), _ptr(q.n_out), _ptr(q.XO), _ptr(C_f32),
             _ptr(ws), nbytes, _stream(stream))

@@ -37,6 +37,11 @@ class Linear8bitLt(torch.nn.Module):
     copying the module again never quantizes twice.  (A module created on the
     GPU holds an uninitialized weight: fill it, then call .cuda() to quantize.)
     in_features must be a multiple of 64.
+
+    Casts: CB stays int8 and SCB float32 under any cast (.half(), .to(dtype),
+    .type(...)); they only change device.  A cast between float16 and bfloat16
+    switches the layer's 16-bit type (its input, output and bias); a cast to
+    any other floating type leaves the 16-bit type as it is.
     """
 
     def __init__(self, in_features: int, out_features: int, bias: bool = True,
@@ -75,7 +80,30 @@ class Linear8bitLt(torch.nn.Module):
             self.weight = None
 
     def _apply(self, fn, *args, **kwargs):
-        super()._apply(fn, *args, **kwargs)
+        # CB (int8) and SCB (fp32 scales) keep their dtypes whatever the cast:
+        # they move by device only.  The layer's 16-bit type (input, output,
+        # bias, any kept 16-bit weight) follows a cast between float16 and
+        # bfloat16; a cast to another floating type moves the layer's tensors
+        # but keeps their 16-bit type, since the kernels take 16-bit data only.
+        here = self.SCB.device if self.quantized else (
+            self.weight.device if self.weight is not None else torch.device("cpu"))
+        probe = fn(torch.zeros(1, dtype=self._dtype, device=here))
+        target = probe.device
+        new16 = probe.dtype if probe.dtype in (torch.float16, torch.bfloat16) else self._dtype
+        CB, SCB = self.CB, self.SCB
+        self.CB = self.SCB = None
+
+        def move(t):
+            return t.to(device=target, dtype=new16 if t.is_floating_point() else None)
+
+        try:
+            super()._apply(move, *args, **kwargs)
+        finally:
+            if CB is not None:
+                self.CB, self.SCB = CB.to(target), SCB.to(target)
+        if new16 != self._dtype:
+            self._dtype = new16
+            self._act, self._ws = None, None
         self._quantize()
         return self
 
@@ -92,7 +120,8 @@ class Linear8bitLt(torch.nn.Module):
         if not X.is_contiguous():
             X = X.contiguous()
         M = X.shape[0]
-        if self._act is None or self._act.CA.shape[0] != M or self._act.CA.device != X.device:
+        if (self._act is None or self._act.CA.shape[0] != M or self._act.CA.device != X.device
+                or self._act.XO.dtype != X.dtype):
             self._act = alloc_act(M, self.in_features, X.dtype, X.device)
             self._ws = linear_workspace(M, self.out_features, self.in_features, X.device)
         Y, q = linear(X, self.CB, self.SCB, bias=self.bias, threshold=self.threshold,
@@ -210,11 +239,23 @@ def load_quantized(module: torch.nn.Module, path: str, device="cuda") -> torch.n
             if (info["in_features"], info["out_features"]) != (m.in_features, m.out_features):
                 raise ValueError(f"layer '{name}': file has {info['out_features']}x"
                                  f"{info['in_features']}, module {m.out_features}x{m.in_features}")
+            CB, SCB = f.get_tensor(f"{key}.CB"), f.get_tensor(f"{key}.SCB")
+            N, K = m.out_features, m.in_features
+            if CB.dtype != torch.int8 or tuple(CB.shape) != (N, K):
+                raise ValueError(f"layer '{name}': CB is {CB.dtype} {tuple(CB.shape)}, "
+                                 f"expected torch.int8 ({N}, {K})")
+            if SCB.dtype != torch.float32 or tuple(SCB.shape) != (N,):
+                raise ValueError(f"layer '{name}': SCB is {SCB.dtype} {tuple(SCB.shape)}, "
+                                 f"expected torch.float32 ({N},)")
+            dtype = getattr(torch, info["dtype"])
             m.weight = None
-            m.CB = f.get_tensor(f"{key}.CB").to(device)
-            m.SCB = f.get_tensor(f"{key}.SCB").to(device)
+            m.CB, m.SCB = CB.to(device), SCB.to(device)
             m.threshold = float(info["threshold"])
+            m._dtype = dtype
+            m._act, m._ws = None, None
             if info["bias"]:
-                m.bias = torch.nn.Parameter(f.get_tensor(f"{key}.bias").to(device),
+                m.bias = torch.nn.Parameter(f.get_tensor(f"{key}.bias").to(device, dtype),
                                             requires_grad=False)
+            else:
+                m.bias = None
     return module

@@ -67,3 +67,29 @@ def test_checkpoint_refuses_unquantized_layer(tmp_path):
     m = n8.Linear8bitLt.from_linear(torch.nn.Linear(64, 8, dtype=torch.float16))
     with pytest.raises(RuntimeError, match="not quantized"):
         n8.save_quantized(m, str(tmp_path / "x.safetensors"))
+
+
+def _quantized_on_host(dtype=torch.float16):
+    """A layer holding CB/SCB as if placed (host tensors; no kernel runs)."""
+    rng = np.random.default_rng(6)
+    m = n8.Linear8bitLt(128, 16, dtype=dtype)
+    m.weight = None
+    m.CB = torch.from_numpy(rng.integers(-127, 128, (16, 128), dtype=np.int8))
+    m.SCB = torch.from_numpy(rng.random(16, dtype=np.float32))
+    m.bias = torch.nn.Parameter(torch.randn(16).to(dtype), requires_grad=False)
+    return m
+
+
+@pytest.mark.parametrize("cast", ["half", "bfloat16", "float", "double", "to_f16", "type_f32"])
+def test_casts_keep_int8_codes_and_fp32_scales(cast):
+    """The recovered weight CB * SCB / 127 ("Usage" section) needs SCB's fp32
+    values: no cast may touch them, or CB's int8 codes."""
+    m = _quantized_on_host(torch.bfloat16)
+    CB, SCB = m.CB.clone(), m.SCB.clone()
+    {"half": lambda: m.half(), "bfloat16": lambda: m.bfloat16(), "float": lambda: m.float(),
+     "double": lambda: m.double(), "to_f16": lambda: m.to(torch.float16),
+     "type_f32": lambda: m.type(torch.float32)}[cast]()
+    assert m.CB.dtype == torch.int8 and torch.equal(m.CB, CB)
+    assert m.SCB.dtype == torch.float32 and torch.equal(m.SCB, SCB)
+    expect = {"half": torch.float16, "to_f16": torch.float16}.get(cast, torch.bfloat16)
+    assert m._dtype == expect and m.bias.dtype == expect
