@@ -2,6 +2,7 @@
 workload and compare every stage with the CPU oracle."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -138,3 +139,23 @@ def sample_rows(M, n, seed=0):
     while len(rows) < min(n, M):
         rows.add(int(rng.integers(0, M)))
     return np.array(sorted(rows), dtype=np.int64)
+
+
+def host_threads() -> int:
+    """Threads for the oracle's row loops: this process's CPUs, at most 16 (a
+    GPU host's share)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_forward(orc, wl, threshold, weight, rows=None):
+    """orc.forward's dict, with the product and output rows spread over
+    host_threads() threads (the oracle's own per-row functions; the same result
+    for any thread count).  rows=None: every row."""
+    import oracle
+    CB, SCB = weight
+    act = orc.quantize_act(wl.X, wl.dtype, threshold)
+    rows = np.arange(wl.M, dtype=np.int64) if rows is None else rows
+    C, Y = oracle.forward_rows_threaded(orc, act, weight, wl.X, wl.dtype, wl.bias, rows,
+                                        host_threads())
+    CA, SCA, idx, XO = act
+    return dict(CB=CB, SCB=SCB, CA=CA, SCA=SCA, idx=idx, XO=XO, C=C, Y=Y)

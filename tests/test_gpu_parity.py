@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import compare, log, run_gpu, sample_rows
+from gpu_helpers import compare, host_threads, log, oracle_forward, run_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -269,10 +269,14 @@ def test_deterministic_and_bias_applied(orc):
 
 # ---- full-size workloads on sampled rows ------------------------------------
 def sampled_check(orc, wl, n_rows, threshold=None, weight_cache=None, label=None):
+    """Every quantization stage in full; C and Y on n_rows sampled rows (rows 0
+    and M-1 among them), or on every row when n_rows >= M."""
     t = wl.threshold if threshold is None else threshold
     label = label or f"{wl.name} t={t}"
-    log(f"[parity] {label} M={wl.M} N={wl.N} K={wl.K} sampled rows={n_rows}")
-    rows = sample_rows(wl.M, n_rows)
+    every = n_rows >= wl.M
+    log(f"[parity] {label} M={wl.M} N={wl.N} K={wl.K} "
+        f"{'every row' if every else f'sampled rows={n_rows}'} (oracle on {host_threads()} threads)")
+    rows = None if every else sample_rows(wl.M, n_rows)
     if weight_cache is not None and wl.name in weight_cache:
         (CB_ref, SCB_ref), dev_w = weight_cache[wl.name]
         g = run_gpu(wl, t, weight=dev_w)
@@ -283,16 +287,16 @@ def sampled_check(orc, wl, n_rows, threshold=None, weight_cache=None, label=None
         assert np.array_equal(g["SCB"], SCB_ref), f"{label}: SCB"
         if weight_cache is not None:
             weight_cache[wl.name] = ((CB_ref, SCB_ref), g["weight"])
-    ref = orc.forward(wl.X, None, wl.dtype, t, bias=wl.bias, rows=rows,
-                      weight=(CB_ref, SCB_ref))
+    ref = oracle_forward(orc, wl, t, (CB_ref, SCB_ref), rows=rows)
     err, scale = compare(wl, g, ref, rows=rows, label=label)
     log(f"[parity] {label}: ok, n_out={g['n_out']} max|dY|={err:.3g} max|Y|={scale:.3g}")
     return g
 
 
 def test_prefill_full_size(orc):
+    """2048 x 16384 x 4096: C and Y on every row."""
     wl = synth.make_workload("prefill")
-    sampled_check(orc, wl, 32)
+    sampled_check(orc, wl, wl.M)
 
 
 @pytest.fixture(scope="module")
@@ -304,14 +308,14 @@ def sweep_weight():
 def test_sweep_full_size(orc, name, sweep_weight):
     wl = synth.make_workload(name, with_weight=not sweep_weight)
     wl.name = "sweep"  # one weight for the four densities
-    sampled_check(orc, wl, 12, weight_cache=sweep_weight, label=name)
+    sampled_check(orc, wl, 64, weight_cache=sweep_weight, label=name)
 
 
 @pytest.mark.parametrize("t", [float("inf"), 0.0])
 def test_sweep_threshold_extremes_full_size(orc, t, sweep_weight):
     wl = synth.make_workload("sweep_0.1", with_weight=not sweep_weight)
     wl.name = "sweep"
-    g = sampled_check(orc, wl, 8 if t == 0.0 else 12, threshold=t, weight_cache=sweep_weight,
+    g = sampled_check(orc, wl, 16 if t == 0.0 else 64, threshold=t, weight_cache=sweep_weight,
                       label=f"sweep_0.1 t={t}")
     assert g["n_out"] == (0 if t != 0.0 else wl.K)
 
@@ -319,7 +323,7 @@ def test_sweep_threshold_extremes_full_size(orc, t, sweep_weight):
 @pytest.mark.parametrize("name", ["bloom_up", "bloom_down"])
 def test_bloom_ffn_full_size(orc, name):
     wl = synth.make_workload(name)
-    sampled_check(orc, wl, 6)
+    sampled_check(orc, wl, 48)
 
 
 # ---- the one-call forward (llmint8_linear): fused small-M kernel and the
