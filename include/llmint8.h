@@ -212,6 +212,35 @@ llmint8_status llmint8_linear_profiled(const void* X, int dtype, int64_t M, int6
                                        hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 /*
+ * For callers that cannot allocate device memory: code being captured into a
+ * HIP graph, serving loops and harnesses that forbid hipMalloc.  The same
+ * forward as llmint8_linear, with the same arguments and results, minus the
+ * workspace: the scratch memory it needs (the activation kernel's partial
+ * column masks, split-K partial tiles and arrival counters, the weight codes at
+ * the outlier columns) lives in a static device array of
+ * LLMINT8_SCRATCH_BYTES bytes that the library holds on each device it runs on
+ * until the process ends.  Nothing is allocated or freed, by the library or
+ * by any library routine it calls.
+ *   - Shapes whose llmint8_linear_workspace_size exceeds LLMINT8_SCRATCH_BYTES
+ *     are refused with LLMINT8_ERR_UNSUPPORTED before any HIP call.  Decode
+ *     batches need none, 2048 x 16384 x 4096 needs 16 MiB, 4096 x 28672 x 8192
+ *     28 MiB and 512 x 57344 x 14336 56 MiB; 512 x 14336 x 57344 (70 MiB with
+ *     its split-K partial tiles) is refused.
+ *   - Every call on a device uses that device's one array: calls on the same
+ *     device that overlap in time (on different streams, or from threads that
+ *     enqueue concurrently) race on it and give undefined results.  Calls
+ *     ordered on one stream are safe; each call clears what it needs cleared.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress) with that device current.
+ */
+#define LLMINT8_SCRATCH_BYTES (64u << 20)
+llmint8_status llmint8_linear_noalloc(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                                      float threshold, const int8_t* CB, const float* SCB,
+                                      const void* bias, void* Y, int8_t* CA, float* SCA,
+                                      int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                      int32_t* C_i32, hipStream_t stream);
+
+/*
  * ---- FP8 (E4M3) variant of the decomposition -------------------------------
  * The zhichai.top summary of LLM.int8() (outlook section, its list of the
  * method's limitations) names an 8-bit floating-point type as future work.

@@ -29,6 +29,7 @@ F16 = 0
 BF16 = 1
 K_ALIGN = 64
 K_MAX = 133120
+SCRATCH_BYTES = 64 << 20  # LLMINT8_SCRATCH_BYTES: the static scratch of llmint8_linear_noalloc
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or device", 3: "HIP runtime error"}
 
@@ -44,6 +45,7 @@ EXPORTS = (
     "llmint8_linear_workspace_size",
     "llmint8_linear",
     "llmint8_linear_profiled",
+    "llmint8_linear_noalloc",
     "llmint8_quantize_weight_fp8",
     "llmint8_quantize_act_fp8",
     "llmint8_matmul_fp8",
@@ -100,6 +102,7 @@ def lib() -> ctypes.CDLL:
            ctypes.c_size_t, _P]
     L.llmint8_linear.argtypes = lin
     L.llmint8_linear_profiled.argtypes = lin + [_P, _P]
+    L.llmint8_linear_noalloc.argtypes = lin[:-3] + [_P]
     L.llmint8_quantize_weight_fp8.argtypes = L.llmint8_quantize_weight.argtypes
     L.llmint8_quantize_act_fp8.argtypes = L.llmint8_quantize_act.argtypes
     L.llmint8_matmul_fp8.argtypes = mm
@@ -110,7 +113,7 @@ def lib() -> ctypes.CDLL:
     L.llmint8_linear_fp8_profiled.argtypes = lin + [_P, _P]
     for f in ("llmint8_quantize_weight", "llmint8_quantize_tensor", "llmint8_quantize_act",
               "llmint8_matmul", "llmint8_matmul_profiled", "llmint8_linear",
-              "llmint8_linear_profiled", "llmint8_quantize_weight_fp8",
+              "llmint8_linear_profiled", "llmint8_linear_noalloc", "llmint8_quantize_weight_fp8",
               "llmint8_quantize_act_fp8", "llmint8_matmul_fp8", "llmint8_matmul_fp8_profiled",
               "llmint8_linear_fp8", "llmint8_linear_fp8_profiled"):
         getattr(L, f).restype = _INT
@@ -195,6 +198,14 @@ def llmint8_linear_profiled(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, 
            lib().llmint8_linear_profiled(X, dtype, M, N, K, ctypes.c_float(threshold), CB, SCB,
                                          bias, Y, CA, SCA, outlier_idx, n_outliers, X_outlier,
                                          C_i32, workspace, workspace_bytes, stream, start, stop))
+
+
+def llmint8_linear_noalloc(X, dtype, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                           n_outliers, X_outlier, C_i32, stream=0):
+    _check("llmint8_linear_noalloc",
+           lib().llmint8_linear_noalloc(X, dtype, M, N, K, ctypes.c_float(threshold), CB, SCB, bias,
+                                        Y, CA, SCA, outlier_idx, n_outliers, X_outlier, C_i32,
+                                        stream))
 
 
 def llmint8_quantize_weight_fp8(W, dtype, N, K, CB, SCB, stream=0):

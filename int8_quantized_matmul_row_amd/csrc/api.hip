@@ -107,12 +107,44 @@ size_t linear_workspace(int64_t M, int64_t N, int64_t K, bool fp8) {
     return mm == 0 ? act : align256(act) + mm;
 }
 
+// ---- device scratch for the entry point that allocates nothing -------------
+// One array per device (each device's code object holds its own copy), kept
+// until the process ends.  Host code never passes the array's name to a
+// kernel: its device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[LLMINT8_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch[64];
+
+// The current device's scratch address (device ids are checked by
+// check_device first).
+llmint8_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= 64) return LLMINT8_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (p == nullptr) return hip_fail(hipErrorInvalidSymbol);
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return LLMINT8_OK;
+}
+
+// use_scratch: the workspace is the device's static scratch array (the
+// workspace arguments are ignored); shapes that need more than it holds are
+// refused before any HIP call.
 llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_t N, int64_t K,
                            float threshold, const int8_t* CB, const float* SCB, const void* bias,
                            void* Y, int8_t* CA, float* SCA, int32_t* outlier_idx,
                            int32_t* n_outliers, void* X_outlier, int32_t* C_i32, float* C_f32,
                            void* workspace, size_t workspace_bytes, hipStream_t stream,
-                           hipEvent_t ev_start, hipEvent_t ev_stop) {
+                           hipEvent_t ev_start, hipEvent_t ev_stop, bool use_scratch = false) {
     llmint8_status s = check_dtype(dtype);
     if (s != LLMINT8_OK) return s;
     if ((s = check_sizes(M, N, K)) != LLMINT8_OK) return s;
@@ -127,9 +159,20 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
         (C_f32 && !aligned16(C_f32)) || (workspace && !aligned16(workspace)))
         return LLMINT8_ERR_INVALID_ARGUMENT;
     const size_t need = linear_workspace(M, N, K, fp8);
-    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    if (use_scratch) {
+        if (need > (size_t)LLMINT8_SCRATCH_BYTES) return LLMINT8_ERR_UNSUPPORTED;
+    } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
         return LLMINT8_ERR_INVALID_ARGUMENT;
+    }
     if ((s = check_device()) != LLMINT8_OK) return s;
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            if ((s = scratch_address(&workspace)) != LLMINT8_OK) return s;
+            workspace_bytes = need;
+        }
+    }
     const bool bf16 = dtype == LLMINT8_BF16;
     hipError_t e;
     if (M > 0 && N > 0 && llmint8::linear_decode_supported((int)M, (int)K)) {
@@ -359,6 +402,16 @@ llmint8_status llmint8_linear_profiled(const void* X, int dtype, int64_t M, int6
     return linear_impl(X, dtype, false, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
                        n_outliers, X_outlier, C_i32, nullptr, workspace, workspace_bytes, stream,
                        start, stop);
+}
+
+llmint8_status llmint8_linear_noalloc(const void* X, int dtype, int64_t M, int64_t N, int64_t K,
+                                      float threshold, const int8_t* CB, const float* SCB,
+                                      const void* bias, void* Y, int8_t* CA, float* SCA,
+                                      int32_t* outlier_idx, int32_t* n_outliers, void* X_outlier,
+                                      int32_t* C_i32, hipStream_t stream) {
+    return linear_impl(X, dtype, false, M, N, K, threshold, CB, SCB, bias, Y, CA, SCA, outlier_idx,
+                       n_outliers, X_outlier, C_i32, nullptr, nullptr, 0, stream, nullptr, nullptr,
+                       true);
 }
 
 llmint8_status llmint8_matmul_fp8(int dtype, int64_t M, int64_t N, int64_t K, const uint8_t* CA,

@@ -167,3 +167,23 @@ def test_peak_mfma_rejects_bad_arguments_before_any_hip_call():
     assert call(sink_bytes=4 * 1024 - 1) == INVALID  # one word per thread of 4 blocks
     assert call(blocks=0) == INVALID
     assert call(iters=0) == INVALID
+
+
+def test_noalloc_refuses_what_its_scratch_cannot_hold_before_any_hip_call():
+    """llmint8_linear_noalloc: the same argument checks as llmint8_linear, and
+    shapes whose workspace exceeds the static scratch array are refused."""
+    L = pkg.lib()
+
+    def call(M=2048, N=16384, K=4096, t=6.0, X=A, CB=A, SCB=A, Y=A, CA=A, SCA=A, idx=A, n=A, XO=A):
+        return L.llmint8_linear_noalloc(X, 0, M, N, K, ctypes.c_float(t), CB, SCB, None, Y, CA, SCA,
+                                        idx, n, XO, None, None)
+
+    assert pkg.llmint8_linear_workspace_size(4096, 28672, 8192) <= pkg.SCRATCH_BYTES
+    assert pkg.llmint8_linear_workspace_size(512, 14336, 57344) > pkg.SCRATCH_BYTES
+    assert call(M=512, N=14336, K=57344) == UNSUPPORTED
+    assert call(K=100) == UNSUPPORTED
+    assert call(t=float("nan")) == INVALID
+    assert call(t=-1.0) == INVALID
+    for key in ("X", "CB", "SCB", "Y", "CA", "SCA", "idx", "n", "XO"):
+        assert call(**{key: None}) == INVALID, key
+    assert call(XO=A + 2) == INVALID
