@@ -295,6 +295,36 @@ __device__ __forceinline__ void dma16(const int8_t* gptr, uint32_t lds_addr) {
         : "memory");
 }
 
+// A raw buffer descriptor (stride 0, 32-bit data format) for `bytes` bytes
+// from `base`, in scalar registers.  Loads through it at offsets >= bytes
+// return 0 and touch no memory.
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));  // base[47:32], stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);                // num_records
+    r[3] = 0x00020000;                                                // data format 32
+    return r;
+}
+
+// One buffer_load_dwordx4 ... lds: lane p's 16 bytes at byte offset voff of
+// the buffer land in LDS at lds_addr + 16 p (offsets past the buffer's size
+// read 0).  Issued through asm for the same reasons as dma16; M0 is saved and
+// restored.
+__device__ __forceinline__ void dma_line(const v4i& rsrc, uint32_t voff, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds_addr), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const int8_t* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)p;
 }

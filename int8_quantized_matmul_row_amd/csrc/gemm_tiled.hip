@@ -63,21 +63,22 @@ namespace llmint8 {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BKS = 64;
-constexpr int kStages = 4;
-constexpr int kStageBytes = (BM + BN) * BKS;  // 32 KiB
+constexpr int BM = 256, BN = 256;
+constexpr int BKS = 128;  // K bytes per stage: one whole 128-byte line of every row
+constexpr int kStages = 2;
+constexpr int kStageBytes = (BM + BN) * BKS;  // 64 KiB
 constexpr int kWavesN = 2;                  // waves along N (2 along M)
 constexpr int kWaves = 2 * kWavesN;
 constexpr int kThreads = 64 * kWaves;
 constexpr int JB = 8 / kWavesN;             // 32-column blocks per wave
 constexpr int kWaveN = 32 * JB;             // columns per wave
-constexpr int kDmaRows = BM / kWaves / 16;  // stage-load instructions per operand and wave
+constexpr int kDmaInst = BM / kWaves / 8;   // stage-load instructions (8 rows each) per operand and wave
 constexpr int kGroupM = 8;
 constexpr int kOutLds = 16;  // outlier columns whose weight codes are staged in LDS
 constexpr int kGatherThreads = 256;
 constexpr int kCUs = 256;             // compute units of the device (gfx950)
 constexpr int kMaxSplit = 8;          // workgroups per tile when K is split
-constexpr int kMinSplitStages = 16;   // K stages per split, at least
+constexpr int kMinSplitStages = 8;    // K stages (128 bytes) per split, at least
 static_assert(kOutLds == kGatherFirst, "the gathered codes start where the LDS ones end");
 constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
 constexpr int kSmemBytes =
@@ -198,41 +199,60 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     int tm, tn;
     map_tile(tile, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int nk_all = K / BKS;
+    // K runs in 128-byte stages; a K that is an odd multiple of 64 ends in a
+    // half stage, of which only the first 64-byte unit is computed.
+    const int nk_all = (K + BKS - 1) / BKS;
     const int kt_begin = ks * nk_all / split, nk = (ks + 1) * nk_all / split - kt_begin;
+    const bool half_last = (K % BKS) != 0 && ks == split - 1;
 
-    // ---- stage loads: wave w fills rows [64w, 64w + 64) of A and of B, 16 rows
-    // per instruction; lane p lands in row 16 q + p/4, slot p%4, and so fetches
-    // the logical chunk (p%4) ^ ((p/16)&3).  Rows past M / N re-read the last
-    // valid row (their results are never stored).
-    const int dchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
-    const int8_t* pa[kDmaRows];
-    const int8_t* pb[kDmaRows];
+    // ---- stage loads: buffer_load_dwordx4 ... lds, one instruction = 8 rows x
+    // 128 bytes, whole lines.  Wave w fills rows [64w, 64w + 64) of A and of
+    // B, instruction i rows 64w + 8i + lane/8; lane p lands in slot p%8 of its
+    // row and so fetches the logical 16-byte chunk (p%8) ^ ((row/2) % 8).  Each
+    // operand is addressed through a descriptor based at the tile's first row
+    // and holding exactly its valid rows: rows past M (N) re-read the last
+    // valid row (their results are never stored), and the unused half of a
+    // half stage reads 0 past the last row instead of leaving the matrix.
+    const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+    const v4i rsrc_a = buffer_rsrc(CA + (size_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
+    const v4i rsrc_b = buffer_rsrc(CB + (size_t)n0 * K, (uint32_t)rows_b * (uint32_t)K);
+    uint32_t voff_a[kDmaInst], voff_b[kDmaInst];
 #pragma unroll
-    for (int i = 0; i < kDmaRows; ++i) {
-        const int r = 16 * kDmaRows * wave + 16 * i + (lane >> 2);
-        pa[i] = CA + (size_t)min(m0 + r, M - 1) * K + (size_t)kt_begin * BKS + dchunk;
-        pb[i] = CB + (size_t)min(n0 + r, N - 1) * K + (size_t)kt_begin * BKS + dchunk;
+    for (int i = 0; i < kDmaInst; ++i) {
+        const int r = 8 * kDmaInst * wave + 8 * i + (lane >> 3);
+        const int ch = ((lane & 7) ^ ((4 * i + (lane >> 4)) & 7)) * 16;
+        voff_a[i] = (uint32_t)min(r, rows_a - 1) * (uint32_t)K + (uint32_t)kt_begin * BKS + ch;
+        voff_b[i] = (uint32_t)min(r, rows_b - 1) * (uint32_t)K + (uint32_t)kt_begin * BKS + ch;
     }
-    const uint32_t lds_base = lds_address(smem) + 16 * kDmaRows * wave * BKS;  // this wave's rows
-    auto issue = [&](int kt) {
-        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + (kt % kStages) * kStageBytes);
+    const uint32_t lds_base =
+        __builtin_amdgcn_readfirstlane(lds_address(smem) + 8 * kDmaInst * wave * BKS);  // this wave's rows
+    // stage-load instruction d (A rows for d < kDmaInst, then B rows) of stage
+    // kt (relative to kt_begin) into ring buffer u
+    auto dma = [&](int d, int kt, int u) {
+        const uint32_t kd = (uint32_t)kt * BKS;
+        if (d < kDmaInst)
+            dma_line(rsrc_a, voff_a[d] + kd, lds_base + u * kStageBytes + 8 * d * BKS);
+        else
+            dma_line(rsrc_b, voff_b[d - kDmaInst] + kd,
+                     lds_base + u * kStageBytes + BM * BKS + 8 * (d - kDmaInst) * BKS);
+    };
+    auto issue = [&](int kt, int u) {
 #pragma unroll
-        for (int i = 0; i < kDmaRows; ++i) dma16(pa[i] + (size_t)kt * BKS, st + 16 * i * BKS);
-#pragma unroll
-        for (int i = 0; i < kDmaRows; ++i) dma16(pb[i] + (size_t)kt * BKS, st + BM * BKS + 16 * i * BKS);
+        for (int d = 0; d < 2 * kDmaInst; ++d) dma(d, kt, u);
     };
 
-    // ---- fragments: lane l reads row (l & 31) of each 32-row block, chunk
-    // 2 ks + l/32 of the stage.  Fragment f < 4 is A block f, f >= 4 is B block
-    // f - 4.
+    // ---- fragments: lane l reads row (l & 31) of each 32-row block.  In
+    // 64-byte unit h of a stage, its 32 bytes are the logical chunks
+    // 4h + l/32 and 4h + 2 + l/32 (the same for A and B), at LDS slot
+    // chunk ^ ((row/2) % 8): each 16-lane phase of a read (16 rows, one chunk)
+    // touches all 64 banks once.  Fragment f < 4 is A block f, f >= 4 is B
+    // block f - 4.
     const int rr = lane & 31;
     const int a_off = wm * 128 * BKS, b_off = BM * BKS + wn * kWaveN * BKS;
-    auto read_frag = [&](int kt, int ks, int f) -> v4i {
-        const int slot = ((2 * ks + (lane >> 5)) ^ ((rr >> 2) & 3)) * 16;
-        const int off = (kt % kStages) * kStageBytes + slot +
-                        (f < 4 ? a_off + 32 * f * BKS : b_off + 32 * (f - 4) * BKS);
-        return *reinterpret_cast<const v4i*>(smem + rr * BKS + off);
+    auto read_frag = [&](int u, int h, int e, int f) -> v4i {
+        const int slot = ((4 * h + 2 * e + (lane >> 5)) ^ ((rr >> 1) & 7)) * 16;
+        const int off = u * kStageBytes + slot + (f < 4 ? a_off + 32 * f * BKS : b_off + 32 * (f - 4) * BKS);
+        return lds_load<v4i>(smem, (uint32_t)(rr * BKS + off));
     };
 
     typedef typename TileAcc<FP8>::type acc_t;
@@ -266,21 +286,19 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     }
     if (!e_valid) e_col = 0;
 
-    // Every stage issues the loads of stage kt+3, clamped to the last stage:
-    // past K they re-read it into a ring buffer no wave reads again.  So each
-    // stage waits on the same load count and the unrolled loop needs no
-    // branches (a loop whose stages run conditionally made the compiler merge
-    // register versions with hundreds of copies).  All loads are awaited
+    // The prologue loads stages 0 and 1; from then on, stage kt loads stage
+    // kt + 2 into the buffer it has just finished with, clamped to the last
+    // stage (past K they re-read it into a buffer no wave reads again), so
+    // every stage runs the same branch-free code.  All loads are awaited
     // before the epilogue reuses the ring.
-    issue(0);
+    issue(0, 0);
     constexpr int kWoPasses = BN * kOutLds / kThreads;  // rows tid/16 + (kThreads/16) q
     int32_t wo_raw[kWoPasses];
 #pragma unroll
     for (int q = 0; q < kWoPasses; ++q)
         wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + (kThreads / 16) * q, N - 1) * K + e_col];
-    issue(min(1, nk - 1));
-    issue(min(2, nk - 1));
-    wait_vmcnt<4 * kDmaRows>();  // stage 0 and everything issued before stage 1
+    issue(min(1, nk - 1), 1);
+    wait_vmcnt<2 * kDmaInst>();  // stage 0 and everything issued before stage 1
     // the values are used from here on only (the compiler would otherwise
     // hoist their conversions above the stage loads, and wait there)
     asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw));
@@ -298,12 +316,11 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
             (uint16_t)(narrow16<BF16>(code_value<FP8>((int8_t)wo_raw[q])) & e_mask);
     stage_barrier();
 
-    // Fragment f (A block f < 4, B block f - 4) of a stage is 32 bytes per
-    // lane: chunks l/32 and 2 + l/32 of its row, the same for A and B.  FP8:
-    // one v_mfma_scale_f32_32x32x64_f8f6f4 per block and stage (the
-    // instruction sees one permutation of the 64 columns on both sides).
-    // int8: two v_mfma_i32_32x32x32_i8, on the low halves (the stage's first
-    // 32 columns) and on the high halves (the second 32).
+    // Fragment f of a unit is 32 bytes per lane.  FP8: one
+    // v_mfma_scale_f32_32x32x64_f8f6f4 per block and unit (the instruction
+    // sees one permutation of the 64 columns on both sides).  int8: two
+    // v_mfma_i32_32x32x32_i8, on the low halves (the unit's chunks 0, 1) and
+    // on the high halves (chunks 2, 3).
     auto mma = [&](const v8i& b, const v8i& a, acc_t c) -> acc_t {
         if constexpr (FP8) {
             return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
@@ -314,61 +331,79 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                                                           __builtin_shufflevector(a, a, 4, 5, 6, 7), c, 0, 0, 0);
         }
     };
-    // Stage pipeline: MFMA q of a stage is block (i, j) = (q/JB, q%JB).  A
-    // block i is refilled with stage kt+1 in place right after its last use
-    // (MFMA JB i + JB-1); the B blocks, used until the stage's last MFMAs, have
-    // a second register set that takes stage kt+1 during its first JB MFMAs.
-    // The wave's stage loads go out with the even MFMAs.
-    // Stages run in groups of four, so that the two B sets swap statically and
-    // the ring slot u = kt % 4 is a constant (every LDS offset folds into the
-    // instruction's immediate).  The order is pinned with sched_barrier.
-    auto read_frag8 = [&](int u, int f) -> v8i {
-        return cat8(read_frag(u, 0, f), read_frag(u, 1, f));
+    auto read_frag8 = [&](int u, int h, int f) -> v8i {
+        return cat8(read_frag(u, h, 0, f), read_frag(u, h, 1, f));
     };
+    // Unit pipeline: MFMA q of a unit is block (i, j) = (q/JB, q%JB).  A block
+    // i is refilled with the next unit in place right after its last use (MFMA
+    // JB i + JB-1); the B blocks, used until the unit's last MFMAs, have a
+    // second register set (gb1 holds unit 1 of every stage, gb0 unit 0).
     v8i ga[4], gb0[JB], gb1[JB];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) ga[f] = read_frag8(0, f);
+    for (int f = 0; f < 4; ++f) ga[f] = read_frag8(0, 0, f);
 #pragma unroll
-    for (int f = 0; f < JB; ++f) gb0[f] = read_frag8(0, 4 + f);
-    auto stage = [&](int kt, int u, v8i (&bc)[JB], v8i (&bn)[JB]) {
-        // stage kt+1 must have landed; issued after it: stage kt+2
-        wait_vmcnt<2 * kDmaRows>();
-        stage_barrier();
-        const int un = (u + 1) & 3;
-        const uint32_t st = __builtin_amdgcn_readfirstlane(lds_base + ((u + 3) & 3) * kStageBytes);
-        const size_t kd = (size_t)min(kt + 3, nk - 1) * BKS;
+    for (int f = 0; f < JB; ++f) gb0[f] = read_frag8(0, 0, 4 + f);
+    // Stage kt in ring buffer u (a compile-time constant: stages run in pairs).
+    // Unit 0 reads unit 1 of the same buffer.  Two MFMA blocks into unit 1,
+    // every wave waits for its loads of stage kt+1 and for its reads of this
+    // buffer, and meets the others at the barrier: stage kt+1 has landed in
+    // buffer 1-u, and no wave reads buffer u again.  The rest of unit 1 reads
+    // unit 0 of stage kt+1 and spreads the loads of stage kt+2 into buffer u
+    // over its MFMAs, so each load has a whole stage to land.
+    constexpr int kBarrierAt = 2;
+    auto stage = [&](int kt, int u) {
 #pragma unroll
         for (int q = 0; q < 4 * JB; ++q) {
             const int i = q / JB, j = q % JB;
-            acc[i][j] = mma(bc[j], ga[i], acc[i][j]);
-            // (at the last stage these read a stale buffer; unused)
-            if (q < JB) bn[q] = read_frag8(un, 4 + q);
-            if (j == JB - 1) ga[i] = read_frag8(un, i);
-            if ((q & 1) == 0 && (q >> 1) < 2 * kDmaRows) {
-                const int d = q >> 1;  // A rows, then B rows
-                if (d < kDmaRows) dma16(pa[d] + kd, st + 16 * d * BKS);
-                else dma16(pb[d - kDmaRows] + kd, st + BM * BKS + 16 * (d - kDmaRows) * BKS);
+            acc[i][j] = mma(gb0[j], ga[i], acc[i][j]);
+            if (q < JB) gb1[q] = read_frag8(u, 1, 4 + q);
+            if (j == JB - 1) ga[i] = read_frag8(u, 1, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int kn = min(kt + 2, nk - 1);
+#pragma unroll
+        for (int q = 0; q < 4 * JB; ++q) {
+            const int i = q / JB, j = q % JB;
+            acc[i][j] = mma(gb1[j], ga[i], acc[i][j]);
+            if (q == kBarrierAt - 1) {
+                __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+                stage_barrier();
+            }
+            if (q >= kBarrierAt) {
+                // (at the last stage these read a stale buffer; unused)
+                if (q - kBarrierAt < JB) gb0[q - kBarrierAt] = read_frag8(1 - u, 0, 4 + q - kBarrierAt);
+                if (j == JB - 1) ga[i] = read_frag8(1 - u, 0, i);
+                // loads d0 .. d1-1 of the 2 kDmaInst go out with MFMA q
+                constexpr int kSlots = 4 * JB - kBarrierAt;
+                const int d0 = (q - kBarrierAt) * 2 * kDmaInst / kSlots;
+                const int d1 = (q - kBarrierAt + 1) * 2 * kDmaInst / kSlots;
+#pragma unroll
+                for (int d = d0; d < d1; ++d) dma(d, kn, u);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Stage kt+3 goes to buffer (kt-1)%4, last read (as stage kt-1) during
-    // stage kt-2; those reads were consumed by stage kt-1's MFMAs before every
-    // wave reached stage kt's barrier.
-    int kt = 0;
-    for (; kt + 4 <= nk; kt += 4) {
-        stage(kt, 0, gb0, gb1);
-        stage(kt + 1, 1, gb1, gb0);
-        stage(kt + 2, 2, gb0, gb1);
-        stage(kt + 3, 3, gb1, gb0);
-    }
-    if (kt < nk) {
-        stage(kt, 0, gb0, gb1);
-        if (kt + 1 < nk) {
-            stage(kt + 1, 1, gb1, gb0);
-            if (kt + 2 < nk) stage(kt + 2, 2, gb0, gb1);
+    // The last stage of a K that is an odd multiple of 64: unit 0 only, in a
+    // buffer known at run time.
+    auto half_stage = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4 * JB; ++q) {
+            const int i = q / JB, j = q % JB;
+            acc[i][j] = mma(gb0[j], ga[i], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    const int nfull = half_last ? nk - 1 : nk;
+    int kt = 0;
+    for (; kt + 2 <= nfull; kt += 2) {
+        stage(kt, 0);
+        stage(kt + 1, 1);
     }
+    if (kt < nfull) {
+        stage(kt, 0);
+        ++kt;
+    }
+    if (half_last) half_stage();
     wait_vmcnt<0>();  // the clamped loads past K have landed too
 
     // ---- split K: the partial sums meet in the workspace ---------------------

@@ -63,6 +63,8 @@ RAGGED = [
     (37, 100, 8192, BF16, 3, True),     # 2 waves per row, odd M (a half-empty row group)
     (50, 70, 12352, F16, 5, False),     # 4 waves per row, one batch each
     (21, 40, 20480, F16, 2, True),      # 4 waves per row, the last with no batch
+    # the tiled product's K split in 4, the last part ending in a half (64-byte) stage
+    (300, 700, 4160, F16, 20, True),
 ]
 
 
@@ -166,6 +168,7 @@ SPLIT = [
     (300, 700, 4096, F16, 40),    # 6 tiles, K split in 4; codes gathered too
     (40, 64, 57344, BF16, 3),     # 1 tile, split in 8
     (520, 300, 2048, BF16, 0),    # 6 tiles, split in 2; three tile rows
+    (300, 700, 4160, F16, 20),    # split in 4; the last split ends in a half (64-byte) K stage
 ]
 
 
