@@ -73,7 +73,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int JB = 8 / kWavesN;             // 32-column blocks per wave
 constexpr int kWaveN = 32 * JB;             // columns per wave
 constexpr int kDmaInst = BM / kWaves / 8;   // stage-load instructions (8 rows each) per operand and wave
-constexpr int kGroupM = 8;
+constexpr int kGroupM = 4;
 constexpr int kOutLds = 16;  // outlier columns whose weight codes are staged in LDS
 constexpr int kGatherThreads = 256;
 constexpr int kCUs = 256;             // compute units of the device (gfx950)
@@ -189,6 +189,9 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     // weight codes of the tile's rows at the first kOutLds outlier columns, as
     // 16-bit values (0 past n_out): row r, column e at s_wo[r * kOutLds + e]
     __shared__ __attribute__((aligned(16))) uint16_t s_wo[BN * kOutLds];
+    // the tile's rows of XO at the first kOutLds outlier columns: row r at
+    // s_xo[r * kOutLds] (0 past n_out: XO's padding)
+    __shared__ __attribute__((aligned(16))) uint16_t s_xo[BM * kOutLds];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -297,23 +300,13 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 #pragma unroll
     for (int q = 0; q < kWoPasses; ++q)
         wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + (kThreads / 16) * q, N - 1) * K + e_col];
+    // XO's first kOutLds columns of tile row t8 (in bounds for n_pad = 0 too:
+    // XO holds M * K >= 64 elements)
+    const int n_pad0 = (n_out + 31) & ~31;
+    const v4i* xo_src = reinterpret_cast<const v4i*>(XO + (size_t)min(m0 + t8, M - 1) * n_pad0);
+    v4i xo_raw0 = xo_src[0], xo_raw1 = xo_src[1];
     issue(min(1, nk - 1), 1);
     wait_vmcnt<2 * kDmaInst>();  // stage 0 and everything issued before stage 1
-    // the values are used from here on only (the compiler would otherwise
-    // hoist their conversions above the stage loads, and wait there)
-    asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw));
-#pragma unroll
-    for (int q = 0; q < kWoPasses; ++q) asm volatile("" : "+v"(wo_raw[q]));
-    if (kThreads == 256 || tid < 256) {
-        s_sa[tid] = sa_raw;
-        s_sb[tid] = sb_raw / code_max<FP8>();
-        s_bias[tid] = bias ? widen16<BF16>(bias_raw) : 0.0f;
-    }
-    const uint32_t e_mask = e_valid ? 0xFFFFu : 0u;  // a mask, not a select: no branches
-#pragma unroll
-    for (int q = 0; q < kWoPasses; ++q)
-        s_wo[((tid >> 4) + (kThreads / 16) * q) * kOutLds + e_out] =
-            (uint16_t)(narrow16<BF16>(code_value<FP8>((int8_t)wo_raw[q])) & e_mask);
     stage_barrier();
 
     // Fragment f of a unit is 32 bytes per lane.  FP8: one
@@ -405,6 +398,28 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     }
     if (half_last) half_stage();
     wait_vmcnt<0>();  // the clamped loads past K have landed too
+
+    // The epilogue operands loaded in the prologue go to LDS only now: a use
+    // there would make the compiler wait for every load in flight, the second
+    // stage's included (it cannot see the stage loads).  The values are pinned
+    // until here so that their conversions are not hoisted either.
+    asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw), "+v"(xo_raw0), "+v"(xo_raw1));
+#pragma unroll
+    for (int q = 0; q < kWoPasses; ++q) asm volatile("" : "+v"(wo_raw[q]));
+    if (kThreads == 256 || tid < 256) {
+        s_sa[tid] = sa_raw;
+        s_sb[tid] = sb_raw / code_max<FP8>();
+        s_bias[tid] = bias ? widen16<BF16>(bias_raw) : 0.0f;
+        *reinterpret_cast<v4i*>(s_xo + tid * kOutLds) = xo_raw0;
+        *reinterpret_cast<v4i*>(s_xo + tid * kOutLds + 8) = xo_raw1;
+    }
+    {
+        const uint32_t e_mask = e_valid ? 0xFFFFu : 0u;  // a mask, not a select: no branches
+#pragma unroll
+        for (int q = 0; q < kWoPasses; ++q)
+            s_wo[((tid >> 4) + (kThreads / 16) * q) * kOutLds + e_out] =
+                (uint16_t)(narrow16<BF16>(code_value<FP8>((int8_t)wo_raw[q])) & e_mask);
+    }
 
     // ---- split K: the partial sums meet in the workspace ---------------------
     // Stored in register order: 16 bytes (registers 4c..4c+3 of a block) per
@@ -500,12 +515,9 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                     }
                 }
         }
-        // outlier k-block 0: the XO row is requested before the conversion
-        // below so that its latency overlaps it (unconditional, from a clamped
-        // address: a load under a branch is awaited where the branch rejoins;
-        // in bounds for n_pad = 0 too, XO holds M * K >= 16 elements)
+        // outlier k-block 0: the row's XO values, staged in LDS
         const bool have_out = n_out > 0;
-        const v8u16 xraw = *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + 8 * kh);
+        const v8u16 xraw = *reinterpret_cast<const v8u16*>(s_xo + (m_lane + 32 * i) * kOutLds + 8 * kh);
         const float sa = s_sa[m_lane + 32 * i] / code_max<FP8>();
         v16f f[JB];
 #pragma unroll
