@@ -124,8 +124,8 @@ llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t
  *     of the 256 CUs (T <= 128): S = min(floor(256/T), floor(K/1024), 8) workgroups per
  *     tile (if S >= 2), needing 4T bytes of counters rounded up to 256, then
  *     S * T * 256 KiB of partial tiles;
- *   - 64 * ceil(N / 32) * min(K rounded up to 32, 512) bytes: the weight
- *     codes at 512 outlier columns. */
+ *   - N * min(K, 1024) bytes: the weight codes at up to 1024 outlier
+ *     columns. */
 size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /*
@@ -146,14 +146,17 @@ size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
  *            when the shape splits and the workspace holds it: the product
  *            then spreads K over several workgroups per tile;
  *          - the rest, R bytes, for the weight codes at the outlier columns
- *            beyond the first 16, gathered once per call (a small kernel
- *            ahead of the GEMM), which makes the outlier part of the product
- *            several times faster.  R bytes hold
- *            32 * floor(R / (64 * ceil(N / 32) * 32)) columns, at most K:
- *            512 at the default size, every column with
- *            64 * ceil(N / 32) * (K rounded up to 32) bytes.  With more
- *            outlier columns than that (n_outliers is read on the device)
- *            the product gathers the codes itself, as without a workspace.
+ *            when there are more than 16 of them, gathered once per call (by
+ *            the activation kernel in llmint8_linear, else by a small kernel
+ *            ahead of the GEMM) into N rows of C bytes, C a multiple of 64:
+ *            C = 64 * floor(R / (64 N)), at most K (1024 at the default
+ *            size, every column with N * K bytes).  The outlier part of the
+ *            product then runs as a second pipelined K loop over those
+ *            columns.  With more outlier columns than C (n_outliers is read
+ *            on the device) the product gathers each tile's codes itself,
+ *            several times slower, unless the outlier columns are exactly
+ *            0 .. n_outliers-1 (every column at threshold 0), whose codes it
+ *            reads from CB directly.
  *          The contents need no initialization and are not kept.  Calls
  *          that share a workspace must not overlap.
  */

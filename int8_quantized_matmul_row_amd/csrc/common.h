@@ -166,40 +166,33 @@ __device__ __forceinline__ float code_value(int8_t b) {
 }
 
 // ---- weight codes at the outlier columns, gathered for the tiled product ---
-// Element (n, c), weight row n and outlier column c, sits at 16-bit offset
-// gathered_block(n / 32, c / 16, cap) + (n % 32) * 16 + c % 16: 1 KiB blocks
-// of 32 rows x 16 columns, cap / 16 of them per 32 rows (cap a multiple of 32
-// and n_out <= cap).  It holds the value of CB[n][col(c)] in 16-bit (exact:
-// int8 codes and E4M3 values), 0 for c >= n_out and for rows n >= N.  Columns
-// below kGatherFirst are not written (the product stages those in LDS).
-constexpr int kGatherFirst = 16;
+// The tiled product multiplies XO [M, n_pad] by the weight codes at the
+// outlier columns in 64-column stages.  When those columns are not simply
+// 0 .. n_out-1 (then the codes are CB's own first columns), they are gathered
+// once per call into a row-major buffer of `cap` bytes per weight row (cap a
+// multiple of 64, n_pad <= cap): byte c of row n is CB[n][col(c)] for
+// c < n_out and 0 for n_out <= c < n_pad (code 0 is +0 in both formats).
+// Outlier counts up to kOutLds are handled from LDS and need no gather.
+constexpr int kOutLds = 16;
 
-__device__ __forceinline__ size_t gathered_block(int rb, int b, int cap) {
-    return ((size_t)rb * (cap / 16) + b) * 512;
-}
-
-// A workgroup of 256 threads writes row blocks rb0, rb0 + stride, ...: per
-// pass, thread t writes 8 columns of one row, block column t / 64 (then every
-// fourth), row (t % 64) / 2, half t % 2.  col(c) is the c-th outlier column.
-template <bool BF16, bool FP8, typename Col>
-__device__ __forceinline__ void gather_code_blocks(int N, int K, int cap, int n_out, Col col,
-                                                   const int8_t* __restrict__ CB,
-                                                   uint16_t* __restrict__ out, int rb0, int stride) {
-    const int nb = ((n_out + 31) & ~31) / 16, row_blocks = (N + 31) / 32;
-    const int q = threadIdx.x & 63, r = q >> 1, h = q & 1;
-    for (int rb = rb0; rb < row_blocks; rb += stride) {
-        const int n = rb * 32 + r;
-        const int8_t* row = CB + (size_t)min(n, N - 1) * K;
-        for (int b = kGatherFirst / 16 + (int)(threadIdx.x >> 6); b < nb; b += 4) {
-            v8u16 v;
+// Work item e = (row n, 16-column chunk q): 16 byte loads from clamped
+// addresses, all issued before the first use, then one 16-byte store.
+template <typename Col>
+__device__ __forceinline__ void gather_codes(int N, int K, int cap, int n_out, Col col,
+                                             const int8_t* __restrict__ CB, int8_t* __restrict__ out,
+                                             int64_t start, int64_t stride) {
+    const int n_pad = (n_out + 31) & ~31, nq = n_pad / 16;
+    for (int64_t e = start; e < (int64_t)N * nq; e += stride) {
+        const int n = (int)(e / nq), c0 = (int)(e - (int64_t)n * nq) * 16;
+        const int8_t* row = CB + (size_t)n * K;
+        uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = 16 * b + 8 * h + e;
-                const int8_t code = row[col(min(c, n_out - 1))];
-                v[e] = c < n_out && n < N ? narrow16<BF16>(code_value<FP8>(code)) : (uint16_t)0;
-            }
-            *reinterpret_cast<v8u16*>(out + gathered_block(rb, b, cap) + r * 16 + 8 * h) = v;
+        for (int k = 0; k < 16; ++k) {
+            const int c = c0 + k;
+            const uint32_t byte = (uint32_t)(uint8_t)row[col(min(c, n_out - 1))] & (c < n_out ? 0xffu : 0u);
+            w[k >> 2] |= byte << (8 * (k & 3));
         }
+        *reinterpret_cast<v4i*>(out + (size_t)n * cap + c0) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     }
 }
 
@@ -358,11 +351,11 @@ hipError_t launch_quantize_tensor(const void* A, bool bf16, int64_t rows, int64_
 // Weight codes the activation kernel gathers (layout above) for the tiled
 // product that follows it, at most kActGatherCols columns; out == nullptr:
 // none.  The launcher clears out when it did not gather.
-constexpr int kActGatherCols = 512;
+constexpr int kActGatherCols = 1024;
 struct CodeGather {
     const int8_t* CB = nullptr;
     int N = 0, cap = 0;
-    uint16_t* out = nullptr;
+    int8_t* out = nullptr;
 };
 
 size_t quantize_act_workspace(int64_t M, int64_t K);
@@ -401,7 +394,7 @@ struct TiledLayout {
     uint32_t* counters = nullptr;
     int n_counters = 0;
     int32_t* part = nullptr;
-    uint16_t* codes = nullptr;
+    int8_t* codes = nullptr;
     int cap = 0;
 };
 TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes);

@@ -408,8 +408,10 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
     }
 
     // the weight codes at the outlier columns for the product that follows
-    // (when asked for): this workgroup's share of the weight's row blocks
-    if (gather.out != nullptr && total > kGatherFirst && total <= gather.cap) {
+    // (when asked for, and when the product reads them from the gather: more
+    // than kOutLds columns, not simply 0 .. total-1): this workgroup's share
+    // of the work items
+    if (gather.out != nullptr && total > kOutLds && total <= gather.cap) {
         __shared__ int s_cols[kActGatherCols];
         for (int w = tid; w < nwords; w += kThreads) {
             uint32_t b = mw[w];
@@ -420,8 +422,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
             }
         }
         __syncthreads();
-        gather_code_blocks<BF16, FP8>(gather.N, K, gather.cap, total, [&](int c) { return s_cols[c]; },
-                                      gather.CB, gather.out, blockIdx.x, gridDim.x);
+        if (s_cols[total - 1] != total - 1)
+            gather_codes(gather.N, K, gather.cap, total, [&](int c) { return s_cols[c]; }, gather.CB, gather.out,
+                         (int64_t)blockIdx.x * kThreads + tid, (int64_t)gridDim.x * kThreads);
     }
 }
 

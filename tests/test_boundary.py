@@ -79,23 +79,24 @@ def test_workspace_sizes():
     assert pkg.llmint8_quantize_act_workspace_size(64, 100) == 0       # unsupported K
     # the tiled product: split-K partial tiles when the 256 x 256 tiles fill
     # under half of the 256 CUs (256 KiB each, per split, after 256 bytes of
-    # counters), then the gathered outlier codes (16-bit, 32-row blocks, up
-    # to 512 columns, fewer when K is smaller); nothing for the small-M kernel
+    # counters), then the gathered outlier codes (one byte per weight row and
+    # column, up to 1024 columns, fewer when K is smaller); nothing for the
+    # small-M kernel
     assert pkg.llmint8_matmul_workspace_size(8, 4096, 4096) == 0
     assert pkg.llmint8_matmul_workspace_size(16, 4096, 4096) == 0
     # 16 tiles, K = 64 stages split in 4
     assert pkg.llmint8_matmul_workspace_size(17, 4096, 4096) == \
-        256 + 4 * 16 * (256 << 10) + 4096 * 2 * 512
+        256 + 4 * 16 * (256 << 10) + 4096 * 1024
     # 512 tiles: no split
     assert pkg.llmint8_matmul_workspace_size(2048, 16384, 4096) == 16 << 20
     # 2 tiles, but K is 2 stages: no split
-    assert pkg.llmint8_matmul_workspace_size(300, 33, 128) == 64 * 2 * 128
+    assert pkg.llmint8_matmul_workspace_size(300, 33, 128) == 33 * 128
     # 1 tile, split in 8 (the most)
     assert pkg.llmint8_matmul_workspace_size(40, 64, 57344) == \
-        256 + 8 * (256 << 10) + 64 * 2 * 512
+        256 + 8 * (256 << 10) + 64 * 1024
     # the BLOOM-shaped down projection: 112 tiles, split in 2
     assert pkg.llmint8_matmul_workspace_size(512, 14336, 57344) == \
-        512 + 2 * 112 * (256 << 10) + 14336 * 2 * 512
+        512 + 2 * 112 * (256 << 10) + 14336 * 1024
     assert pkg.llmint8_matmul_workspace_size(300, 33, 96) == 0           # unsupported K
     assert pkg.llmint8_linear_workspace_size(2048, 16384, 4096) >= \
         pkg.llmint8_quantize_act_workspace_size(2048, 4096) + (16 << 20)

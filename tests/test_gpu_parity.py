@@ -105,9 +105,10 @@ MANY = [
 @pytest.mark.parametrize("M,N,K,dt,nout,t", MANY,
                          ids=[f"{r[0]}x{r[1]}x{r[2]}-{r[4]}" for r in MANY])
 def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8):
-    """The tiled product gives the same bits whether the epilogue reads the
-    outlier weight codes from the gathered blocks (default and full-capacity
-    workspaces) or gathers them itself (no workspace, or one too small)."""
+    """The tiled product gives the same bits whether its outlier K loop reads
+    the weight codes gathered into the workspace (default and full-capacity
+    workspaces) or the plain kernel gathers them per tile (no workspace, one
+    too small, or C exported)."""
     import torch
     import int8_quantized_matmul_row_amd as pkg
     from gpu_helpers import to_torch
@@ -128,15 +129,20 @@ def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8):
     log(f"[parity] gathered outlier codes {M}x{N}x{K} fp8={fp8} n_out={n_out}")
     assert n_out > 16
     default_bytes = pkg.llmint8_matmul_workspace_size(M, N, K)
-    full_bytes = (N + 31) // 32 * 64 * ((K + 31) // 32 * 32)
-    small_bytes = (N + 31) // 32 * 64 * 16   # holds no 32-column group
+    full_bytes = N * K                # every column
+    small_bytes = 64 * N - 1          # holds no 64-column group
     runs = {}
     for name, nbytes in [("none", 0), ("small", small_bytes), ("default", default_bytes),
                          ("full", full_bytes)]:
         ws = torch.full((max(nbytes, 1),), 0x5A, dtype=torch.uint8, device=dev)  # stale bytes
         Y = mm(q, CB, SCB, bias=bias, workspace=(ws if nbytes else None, nbytes))
         runs[name] = Y.view(torch.int16).cpu()
-    for name in ("small", "default", "full"):
+    # exporting C moves the call to the kernel that gathers the codes itself
+    C = torch.empty((M, N), dtype=torch.float32 if fp8 else torch.int32, device=dev)
+    ws = torch.empty((max(default_bytes, 1),), dtype=torch.uint8, device=dev)
+    ckw = {"C_f32": C} if fp8 else {"C_i32": C}
+    runs["export"] = mm(q, CB, SCB, bias=bias, workspace=(ws, default_bytes), **ckw).view(torch.int16).cpu()
+    for name in ("small", "default", "full", "export"):
         assert torch.equal(runs[name], runs["none"]), name
     # the one-call forward: codes gathered by the activation kernel (default
     # workspace), or by the product's own gather kernel (a workspace holding
@@ -207,6 +213,9 @@ def test_split_k_matches_unsplit(M, N, K, dt, nout, fp8):
     Y1, C1 = run(None)
     Y2, C2 = run(None)
     assert torch.equal(Y1, Y2) and torch.equal(C1, C2)
+    # without the C export (more than 16 outlier columns: the other kernel)
+    Y3 = (pkg.matmul_fp8 if fp8 else pkg.matmul)(q, CB, SCB, bias=bias).view(torch.int16).cpu()
+    assert torch.equal(Y3, Y1)
     if not fp8:
         assert torch.equal(C1, C0)
         assert torch.equal(Y1, Y0)
