@@ -135,7 +135,9 @@ size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
  *   C[m,n] = sum_k CA[m,k] * CB[n,k]  (exact int32),
  * which equals C * SCA * SCB / 127^2 + XO . (recovered W[:, idx])^T + bias.
  * Inputs are the outputs of llmint8_quantize_act (CA, SCA, outlier_idx,
- * n_outliers, X_outlier) and llmint8_quantize_weight (CB, SCB).
+ * n_outliers, X_outlier) and llmint8_quantize_weight (CB, SCB); in particular
+ * the first n_outliers entries of outlier_idx are distinct columns below K in
+ * ascending order (the product relies on it and does not check it).
  *   bias   [N] 16-bit or NULL.
  *   Y      [M,N] 16-bit out (round to nearest even from fp32).
  *   C_i32  [M,N] int32 out or NULL: when given, the same kernels also store the

@@ -5,6 +5,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include "llmint8.h"
+
 namespace llmint8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -175,24 +177,122 @@ __device__ __forceinline__ float code_value(int8_t b) {
 // Outlier counts up to kOutLds are handled from LDS and need no gather.
 constexpr int kOutLds = 16;
 
-// Work item e = (row n, 16-column chunk q): 16 byte loads from clamped
-// addresses, all issued before the first use, then one 16-byte store.
-template <typename Col>
-__device__ __forceinline__ void gather_codes(int N, int K, int cap, int n_out, Col col,
-                                             const int8_t* __restrict__ CB, int8_t* __restrict__ out,
-                                             int64_t start, int64_t stride) {
-    const int n_pad = (n_out + 31) & ~31, nq = n_pad / 16;
-    for (int64_t e = start; e < (int64_t)N * nq; e += stride) {
-        const int n = (int)(e / nq), c0 = (int)(e - (int64_t)n * nq) * 16;
-        const int8_t* row = CB + (size_t)n * K;
-        uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int c = c0 + k;
-            const uint32_t byte = (uint32_t)(uint8_t)row[col(min(c, n_out - 1))] & (c < n_out ? 0xffu : 0u);
-            w[k >> 2] |= byte << (8 * (k & 3));
+// The gather runs over chunks of the outlier list, the same for every weight
+// row: a dense chunk is every outlier column of one kGatherSeg-byte segment
+// of the row holding at least kGatherDense of them (the segment is read whole,
+// coalesced, and the codes picked from LDS); a sparse chunk is up to
+// kGatherRun consecutive outlier columns from sparser segments (one byte load
+// each).
+// Chunk i covers outlier columns lo[i] .. lo[i+1]-1; seg[i] is its segment
+// (dense) or -1.
+constexpr int kGatherSeg = 1024, kGatherDense = 16, kGatherRun = 64;
+constexpr int kGatherSegMax = (LLMINT8_K_MAX + kGatherSeg - 1) / kGatherSeg;
+// Chunks: at most one dense chunk per segment; the sparse columns (under
+// kGatherDense per segment) fill a chunk every kGatherRun, plus one cut short
+// at each dense segment: under 3 per segment.
+constexpr int kGatherChunksMax = 3 * kGatherSegMax + 1;
+struct GatherChunks {
+    int n;
+    int lo[kGatherChunksMax + 1];
+    short seg[kGatherChunksMax];
+};
+struct GatherChunk {
+    int lo, hi, seg;
+};
+
+// Whether every chunk may be sparse without a look at the segments: fewer
+// than kGatherDense outlier columns per segment on average (a dense segment
+// among them is then gathered with byte loads, the same codes).  Chunk i is
+// then columns kGatherRun i .. kGatherRun (i+1) - 1.
+__device__ __forceinline__ bool gather_all_sparse(int K, int n_out) {
+    return (int64_t)n_out * kGatherSeg < (int64_t)kGatherDense * K;
+}
+
+// One thread builds the chunk list (seg_count(s): the number of outlier
+// columns below kGatherSeg s, seg_count(nseg) = n_out).
+template <typename SegCount>
+__device__ __forceinline__ void build_gather_chunks(int K, int n_out, SegCount seg_count, GatherChunks& g) {
+    const int nseg = (K + kGatherSeg - 1) / kGatherSeg;
+    int n = 0, run = -1;  // run: first column of the open sparse chunk
+    int next = seg_count(0);
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int lo = next, hi = seg_count(sg + 1);
+        next = hi;
+        if (hi - lo >= kGatherDense) {
+            if (run >= 0) {
+                g.lo[n] = run;
+                g.seg[n++] = -1;
+                run = -1;
+            }
+            g.lo[n] = lo;
+            g.seg[n++] = (short)sg;
+        } else if (hi > lo) {
+            if (run < 0) run = lo;
+            for (; hi - run > kGatherRun; run += kGatherRun) {  // the open chunk is full
+                g.lo[n] = run;
+                g.seg[n++] = -1;
+            }
         }
-        *reinterpret_cast<v4i*>(out + (size_t)n * cap + c0) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+    if (run >= 0) {
+        g.lo[n] = run;
+        g.seg[n++] = -1;
+    }
+    g.lo[n] = n_out;
+    g.n = n;
+}
+
+// Work items (weight row n, chunk i < nch; chunk(i) its columns and segment),
+// one per 16-lane group of a THREADS-thread
+// workgroup, THREADS / 16 per workgroup and pass (wg = this workgroup's rank
+// among n_wg).  A group writes its chunk's codes to out[n * cap + j], 16
+// consecutive j per store instruction; the group of chunk 0 also writes the
+// zeros at n_out .. n_pad-1.  buf: kGatherSeg bytes per group.  Every thread
+// of the workgroup calls it (it holds barriers).
+template <int THREADS, typename Col, typename Chunk>
+__device__ __forceinline__ void gather_codes(int N, int K, int cap, int n_out, Col col, int nch, Chunk chunk,
+                                             const int8_t* __restrict__ CB, int8_t* __restrict__ out,
+                                             int8_t* buf, int tid, int wg, int n_wg) {
+    constexpr int kGroups = THREADS / 16;
+    const int n_pad = (n_out + 31) & ~31;
+    const int grp = tid >> 4, q = tid & 15;
+    int8_t* gb = buf + grp * kGatherSeg;
+    const int64_t items = (int64_t)N * nch;
+    for (int64_t base = (int64_t)wg * kGroups; base < items; base += (int64_t)n_wg * kGroups) {
+        const int64_t e = base + grp;
+        const bool ok = e < items;
+        const int n = ok ? (int)(e / nch) : 0, ch = ok ? (int)(e - (int64_t)n * nch) : 0;
+        const GatherChunk c_ = ok ? chunk(ch) : GatherChunk{0, 0, -1};
+        const int lo = c_.lo, hi = c_.hi, sg = c_.seg;
+        const int8_t* row = CB + (size_t)n * K;
+        if (sg >= 0) {
+            v4i v[kGatherSeg / 256];
+#pragma unroll
+            for (int u = 0; u < kGatherSeg / 256; ++u) {
+                const int o = sg * kGatherSeg + 256 * u + 16 * q;
+                v[u] = o < K ? *reinterpret_cast<const v4i*>(row + o) : v4i{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < kGatherSeg / 256; ++u) *reinterpret_cast<v4i*>(gb + 256 * u + 16 * q) = v[u];
+        }
+        __syncthreads();
+        // 64 codes per round, 4 per lane, every read issued before the stores
+        // (reads past the chunk re-read its last column and are not stored)
+        int8_t* orow = out + (size_t)n * cap;
+        for (int j0 = lo; j0 < hi; j0 += 64) {
+            int8_t b[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = col(min(j0 + q + 16 * t, hi - 1));
+                b[t] = sg >= 0 ? gb[c - sg * kGatherSeg] : row[c];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (j0 + q + 16 * t < hi) orow[j0 + q + 16 * t] = b[t];
+        }
+        if (ok && ch == 0)
+            for (int j = n_out + q; j < n_pad; j += 16) orow[j] = 0;
+        __syncthreads();  // the group's buffer is read out before the next pass
     }
 }
 

@@ -495,8 +495,33 @@ __global__ __launch_bounds__(kGatherThreads) void gemm_prep(
     if (codes == nullptr) return;
     const int n_out = *n_out_ptr;
     if (n_out <= kOutLds || n_out > cap || idx[n_out - 1] == n_out - 1) return;
-    gather_codes(N, K, cap, n_out, [&](int c) { return idx[c]; }, CB, codes,
-                 (int64_t)blockIdx.x * kGatherThreads + threadIdx.x, (int64_t)gridDim.x * kGatherThreads);
+    __shared__ __attribute__((aligned(16))) int8_t buf[(kGatherThreads / 16) * kGatherSeg];
+    auto col = [&](int c) { return idx[c]; };
+    if (gather_all_sparse(K, n_out)) {
+        gather_codes<kGatherThreads>(
+            N, K, cap, n_out, col, (n_out + kGatherRun - 1) / kGatherRun,
+            [&](int i) { return GatherChunk{kGatherRun * i, min(kGatherRun * (i + 1), n_out), -1}; }, CB, codes,
+            buf, threadIdx.x, blockIdx.x, gridDim.x);
+        return;
+    }
+    __shared__ int s_seg[kGatherSegMax + 1];
+    __shared__ GatherChunks s_chunks;
+    // outlier columns below each segment start: j for the starts in
+    // (idx[j-1], idx[j]] of the ascending list (every start once; one pass of
+    // loads, no dependent chain)
+    const int nseg = (K + kGatherSeg - 1) / kGatherSeg;
+    for (int j = threadIdx.x; j <= n_out; j += kGatherThreads) {
+        const int s_lo = j > 0 ? idx[j - 1] / kGatherSeg + 1 : 0;
+        const int s_hi = j < n_out ? min(idx[j] / kGatherSeg, nseg) : nseg;  // (clamped: stays in s_seg)
+        for (int sg = s_lo; sg <= s_hi; ++sg) s_seg[sg] = j;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) build_gather_chunks(K, n_out, [&](int sg) { return s_seg[sg]; }, s_chunks);
+    __syncthreads();
+    gather_codes<kGatherThreads>(
+        N, K, cap, n_out, col, s_chunks.n,
+        [&](int i) { return GatherChunk{s_chunks.lo[i], s_chunks.lo[i + 1], s_chunks.seg[i]}; }, CB, codes, buf,
+        threadIdx.x, blockIdx.x, gridDim.x);
 }
 
 // At most kOutLds outlier columns (or a call outlier_body cannot take).  LDS:
@@ -970,9 +995,11 @@ hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t
     const TiledLayout L = tiled_layout(a.M, a.N, a.K, a.ws, a.ws_bytes);
     int8_t* gather_to = a.codes_gathered ? nullptr : L.codes;
     if (gather_to != nullptr || L.split > 1) {
-        // the gather's work items: a 16-column chunk of one weight row
-        const int64_t items = (int64_t)a.N * (L.cap / 16);
-        const int64_t want = (items + kGatherThreads - 1) / kGatherThreads;
+        // the gather's work items: a chunk of one weight row's outlier
+        // columns, 16 per workgroup and pass (sized for one chunk per
+        // segment; the workgroups loop over the rest)
+        const int64_t items = (int64_t)a.N * ((a.K + kGatherSeg - 1) / kGatherSeg);
+        const int64_t want = (items + kGatherThreads / 16 - 1) / (kGatherThreads / 16);
         const int blocks = gather_to == nullptr ? 1 : (int)(want < 2048 ? (want < 1 ? 1 : want) : 2048);
         gemm_prep<<<blocks, kGatherThreads, 0, stream>>>(a.N, a.K, L.cap, a.idx, a.n_out, a.CB, gather_to,
                                                          L.counters, L.split > 1 ? L.n_counters : 0);

@@ -421,10 +421,31 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
                 b &= b - 1;
             }
         }
-        __syncthreads();
-        if (s_cols[total - 1] != total - 1)
-            gather_codes(gather.N, K, gather.cap, total, [&](int c) { return s_cols[c]; }, gather.CB, gather.out,
-                         (int64_t)blockIdx.x * kThreads + tid, (int64_t)gridDim.x * kThreads);
+        __syncthreads();  // s_cols complete (every wave reads it); mw read for the last time
+        // mw, no longer read, holds the gather's segment buffers
+        static_assert(sizeof(mw) >= (kThreads / 16) * kGatherSeg, "gather buffers");
+        auto col = [&](int c) { return s_cols[c]; };
+        if (s_cols[total - 1] == total - 1) {
+            // columns 0 .. total-1: the product reads CB itself
+        } else if (gather_all_sparse(K, total)) {
+            gather_codes<kThreads>(
+                gather.N, K, gather.cap, total, col, (total + kGatherRun - 1) / kGatherRun,
+                [&](int i) { return GatherChunk{kGatherRun * i, min(kGatherRun * (i + 1), total), -1}; },
+                gather.CB, gather.out, reinterpret_cast<int8_t*>(mw), tid, blockIdx.x, gridDim.x);
+        } else {
+            // the chunk list, from the word prefixes (32 columns per word)
+            __shared__ GatherChunks s_chunks;
+            if (tid == 0)
+                build_gather_chunks(
+                    K, total,
+                    [&](int sg) { return sg * (kGatherSeg / 32) < nwords ? wpre[sg * (kGatherSeg / 32)] : total; },
+                    s_chunks);
+            __syncthreads();
+            gather_codes<kThreads>(
+                gather.N, K, gather.cap, total, col, s_chunks.n,
+                [&](int i) { return GatherChunk{s_chunks.lo[i], s_chunks.lo[i + 1], s_chunks.seg[i]}; },
+                gather.CB, gather.out, reinterpret_cast<int8_t*>(mw), tid, blockIdx.x, gridDim.x);
+        }
     }
 }
 
