@@ -481,7 +481,12 @@ llmint8_status llmint8_peak_mfma(int fp8, const int8_t* operands, size_t operand
 }
 
 const char* llmint8_status_string(llmint8_status s) {
-    switch (s) {
+    // A C caller may pass any int; its bytes are read as one (loading a value
+    // outside the enumerators as the enum type would be undefined in C++).
+    static_assert(sizeof(llmint8_status) == sizeof(int), "status is int-sized");
+    int code;
+    memcpy(&code, &s, sizeof code);
+    switch (code) {
         case LLMINT8_OK: return "ok";
         case LLMINT8_ERR_INVALID_ARGUMENT: return "invalid argument";
         case LLMINT8_ERR_UNSUPPORTED: return "unsupported shape or device";

@@ -944,7 +944,7 @@ static size_t gathered_codes_bytes(int64_t N, int64_t cap) { return (size_t)N * 
 // stages long.
 static int split_of(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    if (tiles * 2 > kCUs) return 1;
+    if (tiles == 0 || tiles * 2 > kCUs) return 1;  // (no tiles: an empty call)
     int64_t s = kCUs / tiles;
     if (s > K / BKS / kMinSplitStages) s = K / BKS / kMinSplitStages;
     if (s > kMaxSplit) s = kMaxSplit;

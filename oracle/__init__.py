@@ -23,11 +23,9 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast
           "-Wall", "-Wextra"]
 
 
-def build(out_path: str = LIBRARY, mutant: int = 0) -> str:
-    """Compile the oracle with gcc.  mutant > 0 plants a known mistake."""
-    cmd = ["gcc", *CFLAGS, SOURCE, "-o", out_path, "-lm"]
-    if mutant:
-        cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
+def build(out_path: str = LIBRARY, source: str = SOURCE, extra_flags=()) -> str:
+    """Compile the oracle (or another copy of its source) with gcc."""
+    cmd = ["gcc", *CFLAGS, *extra_flags, source, "-o", out_path, "-lm"]
     tmp = out_path + ".tmp"
     cmd[cmd.index(out_path)] = tmp
     subprocess.run(cmd, check=True)

@@ -49,20 +49,13 @@
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math
  * (SSE arithmetic on x86-64, so every float operation is one IEEE binary32
  * operation, round-to-nearest-even).
- *
- * Defining ORACLE_MUTANT=n plants one known mistake (n >= 1); the test suite
- * builds such copies on the CPU to show that its pins catch each mistake.
- * The normal build defines nothing and contains none of them.
+
  */
 #include <fenv.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
-
-#ifndef ORACLE_MUTANT
-#define ORACLE_MUTANT 0
-#endif
 
 #define OK 0
 #define ERR_ARG 1
@@ -106,11 +99,7 @@ static float absmax_scale(float absmax) {
 
 static int8_t quantize_value(float x, float scale) {
     float product = x * scale; /* one fp32 multiply */
-#if ORACLE_MUTANT == 4
-    float r = (product < 0) ? -floorf(-product + 0.5f) : floorf(product + 0.5f); /* half away */
-#else
     float r = nearbyintf(product); /* round half to even (default mode) */
-#endif
     if (r > 127.0f) r = 127.0f;
     if (r < -127.0f) r = -127.0f;
     return (int8_t)r;
@@ -134,22 +123,14 @@ static uint8_t e4m3_encode(float x) {
     const double a = fabs((double)x);
     if (a < ldexp(1.0, -6)) {
         /* subnormal range: multiples of 2^-9; q = 8 is the code of 2^-6 */
-#if ORACLE_MUTANT == 15
-        return sign; /* mistake: subnormals flushed to zero */
-#else
         const double q = nearbyint(a * 512.0);
         return (uint8_t)(sign | (uint8_t)q);
-#endif
     }
     int e2;
     frexp(a, &e2);
     int E = e2 - 1;                       /* 2^E <= a < 2^(E+1) */
     const double sig = ldexp(a, 3 - E);   /* in [8, 16): 3 fraction bits above the point */
-#if ORACLE_MUTANT == 13
-    double q = floor(sig + 0.5); /* mistake: ties away from zero */
-#else
     double q = nearbyint(sig); /* ties to even (default rounding mode) */
-#endif
     if (q == 16.0) {
         q = 8.0;
         E += 1;
@@ -159,11 +140,7 @@ static uint8_t e4m3_encode(float x) {
 }
 
 static float e4m3_scale(float absmax) {
-#if ORACLE_MUTANT == 16
-    return 127.0f / absmax; /* mistake: the int8 range */
-#else
     return 448.0f / absmax; /* one IEEE fp32 division */
-#endif
 }
 
 static uint8_t e4m3_quantize_value(float x, float scale) {
@@ -203,21 +180,6 @@ int oracle_quantize_tensor(const uint16_t* A, int dtype, int64_t rows, int64_t c
         a = fabsf(a);
         if (a > amax) amax = a;
     }
-#if ORACLE_MUTANT == 12
-    /* mistake: the scale taken per row, not over the whole tensor */
-    for (int64_t r = 0; r < rows; ++r) {
-        float ra = 0.0f;
-        for (int64_t c = 0; c < cols; ++c) {
-            float a = fabsf(widen(A[r * cols + c], dtype));
-            if (a > ra) ra = a;
-        }
-        scale[r] = ra;
-        for (int64_t c = 0; c < cols; ++c)
-            Q[r * cols + c] = ra == 0.0f ? 0 : quantize_value(widen(A[r * cols + c], dtype), absmax_scale(ra));
-    }
-    (void)amax;
-    return OK;
-#endif
     for (int64_t r = 0; r < rows; ++r) scale[r] = amax;
     if (amax == 0.0f) {
         memset(Q, 0, (size_t)n);
@@ -241,28 +203,6 @@ static int quantize_weight_codes(const uint16_t* W, int dtype, int64_t N, int64_
     if (fegetround() != FE_TONEAREST) return ERR_ARG;
     int8_t* CB = (int8_t*)codes;
     uint8_t* CB8 = (uint8_t*)codes;
-#if ORACLE_MUTANT == 3
-    if (fp8) return ERR_ARG; /* this planted mistake concerns the int8 codes */
-    /* mistake: one scale per input column instead of per output row */
-    for (int64_t k = 0; k < K; ++k) {
-        float amax = 0.0f;
-        for (int64_t n = 0; n < N; ++n) {
-            float a = fabsf(widen(W[n * K + k], dtype));
-            if (a > amax) amax = a;
-        }
-        for (int64_t n = 0; n < N; ++n)
-            CB[n * K + k] = amax == 0.0f ? 0 : quantize_value(widen(W[n * K + k], dtype), absmax_scale(amax));
-    }
-    for (int64_t n = 0; n < N; ++n) {
-        float amax = 0.0f;
-        for (int64_t k = 0; k < K; ++k) {
-            float a = fabsf(widen(W[n * K + k], dtype));
-            if (a > amax) amax = a;
-        }
-        SCB[n] = amax;
-    }
-    return OK;
-#endif
     for (int64_t n = 0; n < N; ++n) {
         const uint16_t* row = W + n * K;
         float amax = 0.0f;
@@ -328,11 +268,7 @@ static int quantize_act_codes(const uint16_t* X, int dtype, int64_t M, int64_t K
             float a = fabsf(widen(X[m * K + k], dtype));
             if (a > colmax) colmax = a;
         }
-#if ORACLE_MUTANT == 1
-        int outlier = M > 0 && colmax > t; /* mistake: strict comparison */
-#else
         int outlier = M > 0 && colmax >= t;
-#endif
         is_out[k] = (unsigned char)outlier;
         if (outlier) idx[count++] = (int32_t)k;
     }
@@ -342,11 +278,7 @@ static int quantize_act_codes(const uint16_t* X, int dtype, int64_t M, int64_t K
         const uint16_t* row = X + m * K;
         float amax = 0.0f;
         for (int64_t k = 0; k < K; ++k) {
-#if ORACLE_MUTANT == 2
-            /* mistake: the row scale also covers the outlier columns */
-#else
             if (is_out[k]) continue;
-#endif
             float a = fabsf(widen(row[k], dtype));
             if (a > amax) amax = a;
         }
@@ -354,29 +286,17 @@ static int quantize_act_codes(const uint16_t* X, int dtype, int64_t M, int64_t K
         if (fp8) {
             float s = amax == 0.0f ? 0.0f : e4m3_scale(amax);
             for (int64_t k = 0; k < K; ++k) {
-#if ORACLE_MUTANT == 8
-                int zero = 0; /* mistake: outlier entries not removed */
-#else
                 int zero = is_out[k];
-#endif
                 CA8[m * K + k] = zero ? 0x00 : e4m3_quantize_value(widen(row[k], dtype), s);
             }
         } else {
             float s = amax == 0.0f ? 0.0f : absmax_scale(amax);
             for (int64_t k = 0; k < K; ++k) {
-#if ORACLE_MUTANT == 8
-                int zero = amax == 0.0f; /* mistake: outlier entries not removed */
-#else
                 int zero = is_out[k] || amax == 0.0f;
-#endif
                 CA[m * K + k] = zero ? 0 : quantize_value(widen(row[k], dtype), s);
             }
         }
-#if ORACLE_MUTANT == 10
-        for (int32_t j = 0; j < count; ++j) XO[m * (int64_t)count + j] = row[j]; /* mistake: index */
-#else
         for (int32_t j = 0; j < count; ++j) XO[m * (int64_t)count + j] = row[idx[j]];
-#endif
     }
     free(is_out);
     return OK;
@@ -406,11 +326,7 @@ int oracle_int8_rows(const int8_t* CA, const int8_t* CB, int64_t M, int64_t N, i
         for (int64_t n = 0; n < N; ++n) {
             const int8_t* b = CB + n * K;
             int64_t acc = 0;
-#if ORACLE_MUTANT == 11
-            for (int64_t k = 0; k + 1 < K; ++k) acc += (int64_t)a[k] * (int64_t)b[k]; /* mistake: drops a term */
-#else
             for (int64_t k = 0; k < K; ++k) acc += (int64_t)a[k] * (int64_t)b[k];
-#endif
             if (acc > INT32_MAX || acc < INT32_MIN) return ERR_OVERFLOW;
             C[r * N + n] = (int32_t)acc;
         }
@@ -421,12 +337,7 @@ int oracle_int8_rows(const int8_t* CA, const int8_t* CB, int64_t M, int64_t N, i
 /* ---- recovered weights: CB[n,k] * SCB[n] / 127 ([GENTLE] "Usage") -------- */
 
 static double recovered_weight(const int8_t* CB, const float* SCB, int64_t K, int64_t n, int64_t k) {
-#if ORACLE_MUTANT == 6
-    (void)SCB;
-    return (double)CB[n * K + k]; /* mistake: scale not applied */
-#else
     return (double)CB[n * K + k] * (double)SCB[n] / 127.0;
-#endif
 }
 
 int oracle_recover_weight(const int8_t* CB, const float* SCB, int64_t N, int64_t K, double* Wdq) {
@@ -455,27 +366,14 @@ int oracle_output_rows(const int32_t* C, const float* SCA, const float* SCB,
         int64_t m = rows[r];
         if (m < 0 || m >= M) return ERR_ARG;
         for (int64_t n = 0; n < N; ++n) {
-#if ORACLE_MUTANT == 5
-            double y_int8 = (double)C[r * N + n] * (double)SCA[m] * (double)SCB[n] / 127.0;
-#else
             double y_int8 = (double)C[r * N + n] * (double)SCA[m] * (double)SCB[n] / 16129.0;
-#endif
             double y_out = 0.0;
             for (int32_t j = 0; j < n_out; ++j) {
                 int64_t k = idx[j];
                 y_out += (double)widen(X[m * K + k], dtype) * recovered_weight(CB, SCB, K, n, k);
             }
-#if ORACLE_MUTANT == 7
-            (void)bias;
-            double b = 0.0; /* mistake: bias dropped */
-#else
             double b = bias ? (double)widen(bias[n], dtype) : 0.0;
-#endif
-#if ORACLE_MUTANT == 9
-            Y[r * N + n] = y_int8 - y_out + b; /* mistake: wrong sign */
-#else
             Y[r * N + n] = y_int8 + y_out + b;
-#endif
         }
     }
     return OK;
@@ -520,11 +418,7 @@ int oracle_output_rows_fp8(const double* C, const float* SCA, const float* SCB,
         int64_t m = rows[r];
         if (m < 0 || m >= M) return ERR_ARG;
         for (int64_t n = 0; n < N; ++n) {
-#if ORACLE_MUTANT == 14
-            double y8 = C[r * N + n] * (double)SCA[m] * (double)SCB[n] / 448.0; /* mistake */
-#else
             double y8 = C[r * N + n] * (double)SCA[m] * (double)SCB[n] / 200704.0;
-#endif
             double y_out = 0.0;
             for (int32_t j = 0; j < n_out; ++j) {
                 int64_t k = idx[j];

@@ -98,6 +98,9 @@ def test_workspace_sizes():
     assert pkg.llmint8_matmul_workspace_size(512, 14336, 57344) == \
         512 + 2 * 112 * (256 << 10) + 14336 * 1024
     assert pkg.llmint8_matmul_workspace_size(300, 33, 96) == 0           # unsupported K
+    assert pkg.llmint8_matmul_workspace_size(300, 0, 4096) == 0          # empty: no tiles
+    assert pkg.llmint8_linear_workspace_size(300, 0, 4096) == \
+        pkg.llmint8_quantize_act_workspace_size(300, 4096)
     assert pkg.llmint8_linear_workspace_size(2048, 16384, 4096) >= \
         pkg.llmint8_quantize_act_workspace_size(2048, 4096) + (16 << 20)
 
