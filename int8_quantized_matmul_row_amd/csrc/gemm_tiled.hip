@@ -450,7 +450,9 @@ __device__ __forceinline__ void stage_y(int8_t* smem, const float* s_sb, const f
         }
 }
 
-// The staged tile to Y (after a barrier): full 16-byte row-contiguous stores.
+// The staged tile to Y (after a barrier): full 16-byte row-contiguous stores,
+// non-temporal (Y is not read again here; every tile of a round stores at
+// once, and the stream stays out of the way of the operand panels in L2).
 __device__ __forceinline__ void store_y(const int8_t* smem, uint16_t* __restrict__ Y, int M, int N, int m0, int n0,
                                         int tid_e) {
     const int rows = min(BM, M - m0), cols = min(BN, N - n0);
@@ -459,8 +461,8 @@ __device__ __forceinline__ void store_y(const int8_t* smem, uint16_t* __restrict
         const int c8 = (tid_e & 31) * 8;
         for (int r = tid_e >> 5; r < rows; r += kThreads / 32) {
             if (c8 < cols)
-                *reinterpret_cast<v4i*>(Y + (size_t)(m0 + r) * N + n0 + c8) =
-                    *reinterpret_cast<const v4i*>(smem + r * kYStride + c8 * 2);
+                __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(smem + r * kYStride + c8 * 2),
+                                            reinterpret_cast<v4i*>(Y + (size_t)(m0 + r) * N + n0 + c8));
         }
     } else {
         const uint16_t* ys = reinterpret_cast<const uint16_t*>(smem);
