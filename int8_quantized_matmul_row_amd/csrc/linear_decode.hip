@@ -66,11 +66,13 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t xl[(kDecXBytes + 1024) / 2];
     __shared__ __attribute__((aligned(16))) int8_t ca[kDecCaBytes];
     __shared__ uint16_t idx_s[kDecMaxK];           // ascending outlier columns
+    __shared__ uint32_t mask_w[kDecMaxK / 32];     // outlier bits, chunk c in byte c
     __shared__ uint32_t rmax_w[kDecWaves][kDecMaxRows / 2];  // rows 2p, 2p+1 packed
     __shared__ float sca[kDecMaxRows];
-    __shared__ __attribute__((aligned(16))) float scl[kDecMaxRows];  // 127 / SCA (0 for an all-zero row)
-    __shared__ int scan_lds[kDecWaves];
+    __shared__ int s_nout;
+    __shared__ uint16_t xo_s[kDecMaxRows][kDecGather];  // XO of the first kDecGather outlier columns (0 past n_out)
     __shared__ int red[kDecWaves][4][64];          // int32 partial tiles, or fp32 bit patterns
+    __shared__ float red_o[kDecWaves][4][64];      // the 16-bit outlier product's partial tiles (many columns)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar arithmetic
@@ -198,58 +200,61 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         }
     }
 
-    // ---- ranks: exclusive scan of the outlier counts in column order; the
-    // counts of chunk tid (low half) and chunk tid + 512 (high half) travel in
-    // one word (each total is at most K/2 < 2^16); row scales ----------------
-    int n_out;
-    int rank[CPT];
-    {
-        uint32_t cnt = 0;
-#pragma unroll
-        for (int j = 0; j < CPT; ++j) cnt |= (uint32_t)__popc(mbits[j]) << (16 * j);
-        const uint32_t incl = (uint32_t)wave_incl_scan((int)cnt);
-        if (lane == 63) scan_lds[wave] = (int)incl;
-        __syncthreads();  // per-wave row maxima and scan totals complete
-        if (tid < M) {
-            uint32_t m = 0;
-#pragma unroll
-            for (int w = 0; w < kDecWaves; ++w) m = max(m, (rmax_w[w][tid >> 1] >> (16 * (tid & 1))) & 0xffffu);
-            const float amax = widen16<BF16>((uint16_t)m);
-            sca[tid] = amax;
-            scl[tid] = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
-        }
-        uint32_t base = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < kDecWaves; ++w) {
-            const uint32_t v = (uint32_t)scan_lds[w];
-            if (w < wave) base += v;
-            total += v;
-        }
-        const uint32_t ex = base + incl - cnt;
-        const int tot0 = (int)(total & 0xffffu);
-        rank[0] = (int)(ex & 0xffffu);
-        if constexpr (CPT > 1) rank[1] = tot0 + (int)(ex >> 16);
-        n_out = __builtin_amdgcn_readfirstlane(tot0 + (int)(total >> 16));  // the same in every lane
-    }
-    // the ascending outlier list
+    // ---- the mask bytes and the row scales ----------------------------------
+    // Each thread's outlier bits (one byte per chunk) go to LDS for the list.
+    // After the barrier every wave derives the row scales itself (lane r of
+    // each group of 8 reduces row r's per-wave maxima), so they are uniform
+    // values and need no second barrier.
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int c = tid + kDecThreads * j;
-        uint32_t bits = mbits[j];
-        int rk = rank[j];
-        while (bits) {
-            idx_s[rk++] = (uint16_t)(c * 8 + __builtin_ctz(bits));
-            bits &= bits - 1;
-        }
+        if (c < nchunk) reinterpret_cast<uint8_t*>(mask_w)[c] = (uint8_t)mbits[j];
     }
-    __syncthreads();
-    // this output's weight bytes in the first outlier columns, fetched now
-    int cbg[kDecGather];
+    __syncthreads();  // per-wave row maxima and the mask complete
+    float scl_r[kDecMaxRows];  // 127 / SCA (0 for an all-zero row)
     {
-        const int8_t* cbrow = CB + (size_t)n_c * K;
+        const int r = lane & (kDecMaxRows - 1);
+        uint32_t m = 0;
 #pragma unroll
-        for (int j = 0; j < kDecGather; ++j)  // the column is the same in every lane
-            cbg[j] = cbrow[__builtin_amdgcn_readfirstlane(j < n_out ? (int)idx_s[j] : 0)];
+        for (int w = 0; w < kDecWaves; ++w) m = max(m, (rmax_w[w][r >> 1] >> (16 * (r & 1))) & 0xffffu);
+        const float amax = widen16<BF16>((uint16_t)m);
+        const float sc = amax == 0.0f ? 0.0f : code_max<FP8>() / amax;
+        if (wave == 0 && lane < M) sca[lane] = amax;
+#pragma unroll
+        for (int q = 0; q < kDecMaxRows; ++q)
+            scl_r[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), q));
+    }
+    // wave 0: the ascending outlier list (lane l takes the contiguous words
+    // kWpl l .. kWpl l + kWpl - 1, so its columns are contiguous in the list),
+    // the count, and the outlier values of the first kDecGather columns for
+    // the epilogue; published by the barrier before the MFMAs
+    if (wave == 0) {
+        constexpr int kWpl = kDecMaxK / 32 / 64;
+        const int nwords = K >> 5;
+        uint32_t w[kWpl];
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kWpl; ++i) {
+            const int wi = lane * kWpl + i;
+            w[i] = wi < nwords ? mask_w[wi] : 0u;
+            cnt += __popc(w[i]);
+        }
+        const int incl = wave_incl_scan(cnt);
+        int r = incl - cnt;
+#pragma unroll
+        for (int i = 0; i < kWpl; ++i) {
+            uint32_t bits = w[i];
+            while (bits) {
+                idx_s[r++] = (uint16_t)((lane * kWpl + i) * 32 + __builtin_ctz(bits));
+                bits &= bits - 1;
+            }
+        }
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (lane == 0) s_nout = total;
+        // (this wave's own list writes precede these reads in its LDS queue)
+        const int gm = lane / kDecGather, gj = lane % kDecGather;
+        if (gm < kDecMaxRows)
+            xo_s[gm][gj] = gj < total && gm < M ? xl[gm * K + idx_s[gj]] : (uint16_t)0;
     }
 
     // ---- 5. int8 activations into LDS, from the registers ----------------------
@@ -270,13 +275,12 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             const int c = tid + kDecThreads * j;
             export_ca[j] = c < nchunk && (unsigned)(c - (int)blockIdx.x * per) < (unsigned)per;
         }
-        const v4f sc0 = lds_load<v4f>(scl, 0), sc1 = lds_load<v4f>(scl, 16);
         const float nz = opaque_neg_zero();
         v2u codes[CPT][kDecMaxRows];
 #pragma unroll
         for (int r = 0; r < kDecMaxRows; ++r) {
             if (FULL || r < M) {
-                const float scale = r < 4 ? sc0[r & 3] : sc1[r & 3];
+                const float scale = scl_r[r];
 #pragma unroll
                 for (int j = 0; j < CPT; ++j) {
                     const int c = tid + kDecThreads * j;
@@ -327,17 +331,37 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
             }
         }
     }
-    // workgroup 0 writes the outlier list, its count, XO and SCA
-    if (blockIdx.x == 0) {
-        const int n_pad = (n_out + 31) & ~31;
-        for (int j = tid; j < n_out; j += kDecThreads) idx_out[j] = idx_s[j];
-        for (int r = 0; r < M; ++r)
-            for (int j = tid; j < n_pad; j += kDecThreads)
-                XO_out[r * n_pad + j] = j < n_out ? xl[r * K + idx_s[j]] : (uint16_t)0;
-        if (tid == 0) *n_out_out = n_out;
-        if (tid < M) SCA_out[tid] = sca[tid];
+    __syncthreads();  // the codes, the outlier list and its count complete
+    const int n_out = s_nout;
+    // With more than kDecGather outlier columns the 16-bit product runs as
+    // MFMAs over the whole of K against X masked to its outlier columns (a
+    // column-by-column loop in the epilogue would take one dependent load per
+    // column: 233 us at t = 0 on 8x4096x4096).
+    const bool dense_out = n_out > kDecGather;
+    // this output's weight bytes in the first outlier columns; their latency
+    // hides under the MFMAs (unconditional: a load under a branch would be
+    // awaited where the branch rejoins; unused when dense_out)
+    int cbg[kDecGather];
+    {
+        const int8_t* cbrow = CB + (size_t)n_c * K;
+#pragma unroll
+        for (int j = 0; j < kDecGather; ++j)  // the column is the same in every lane
+            cbg[j] = cbrow[__builtin_amdgcn_readfirstlane(j < n_out ? (int)idx_s[j] : 0)];
     }
-    __syncthreads();
+    // the outlier list, XO, the count and SCA, spread over the workgroups
+    {
+        const int n_pad = (n_out + 31) & ~31;
+        const int stride = (int)gridDim.x * kDecThreads;
+        for (int j = (int)blockIdx.x * kDecThreads + tid; j < n_out; j += stride) idx_out[j] = idx_s[j];
+        for (int e = (int)blockIdx.x * kDecThreads + tid; e < M * n_pad; e += stride) {
+            const int r = e / n_pad, j = e - r * n_pad;
+            XO_out[e] = j < n_out ? xl[r * K + idx_s[j]] : (uint16_t)0;
+        }
+        if (blockIdx.x == 0) {
+            if (tid == 0) *n_out_out = n_out;
+            if (tid < M) SCA_out[tid] = sca[tid];
+        }
+    }
 
     // ---- 6. MFMA over this wave's K steps ---------------------------------------
     // A = CA rows (lane row r16 = token), B = CB rows (channel): accumulator
@@ -379,6 +403,52 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[0][v] + acc[1][v];
         }
+        if (dense_out) {
+            // the 16-bit outlier product over this wave's steps: A = X masked
+            // to its outlier columns (lane: token r16, the same 16 columns as
+            // its weight bytes; mask bits from LDS, each bit widened to a
+            // 16-bit lane mask), B = the weight codes as 16-bit values
+            // (exact), two v_mfma_f32_16x16x32 per step on the 8-column halves
+            const uint16_t* px = xl + min(r16, M - 1) * K + kg * 16;
+            v4f acc_o = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) {
+                const int s = grp * SPW + i;
+                if (s < nsteps) {
+                    const int col = s * 64 + kg * 16;
+                    const uint32_t bits = (mask_w[col >> 5] >> (col & 31)) & 0xffffu;
+                    v8u16 x0 = *reinterpret_cast<const v8u16*>(px + s * 64);
+                    v8u16 x1 = *reinterpret_cast<const v8u16*>(px + s * 64 + 8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        x0[e] = (bits >> e) & 1u ? x0[e] : (unsigned short)0;
+                        x1[e] = (bits >> (8 + e)) & 1u ? x1[e] : (unsigned short)0;
+                    }
+                    v8u16 b0, b1;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        b0[e] = narrow16<BF16>(code_value<FP8>((int8_t)((uint32_t)breg[i][e >> 2] >> (8 * (e & 3)))));
+                        b1[e] = narrow16<BF16>(code_value<FP8>((int8_t)((uint32_t)breg[i][2 + (e >> 2)] >> (8 * (e & 3)))));
+                    }
+                    if constexpr (BF16) {
+                        acc_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x0),
+                                                                        __builtin_bit_cast(v8bf, b0), acc_o, 0, 0, 0);
+                        acc_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x1),
+                                                                        __builtin_bit_cast(v8bf, b1), acc_o, 0, 0, 0);
+                    } else {
+                        acc_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x0),
+                                                                       __builtin_bit_cast(v8h, b0), acc_o, 0, 0, 0);
+                        acc_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x1),
+                                                                       __builtin_bit_cast(v8h, b1), acc_o, 0, 0, 0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float f = acc_o[v];  // by value (see the FP8 partials above)
+                red_o[wave][v][lane] = f;
+            }
+        }
     }
     __syncthreads();
 
@@ -399,13 +469,15 @@ __global__ __launch_bounds__(kDecThreads) void linear_decode_kernel(
         if (C_i32) C_i32[(size_t)e_m * N + n_e] = c32;
         y = (float)c32 * (sca[e_m] / code_max<FP8>());
     }
-    const uint16_t* xrow = xl + (size_t)e_m * K;
+    if (dense_out) {
+        float o = 0.0f;  // the groups' partial sums, in a fixed order
 #pragma unroll
-    for (int j = 0; j < kDecGather; ++j)
-        if (j < n_out) y += widen16<BF16>(xrow[idx_s[j]]) * code_value<FP8>((int8_t)cbg[j]);
-    for (int j = kDecGather; j < n_out; ++j) {
-        const int k = idx_s[j];
-        y += widen16<BF16>(xrow[k]) * code_value<FP8>(CB[(size_t)n_e * K + k]);
+        for (int g = 0; g < G; ++g) o += red_o[et + T * g][v][l];
+        y += o;
+    } else {
+#pragma unroll
+        for (int j = 0; j < kDecGather; ++j)
+            if (j < n_out) y += widen16<BF16>(xo_s[e_m][j]) * code_value<FP8>((int8_t)cbg[j]);
     }
     const float bv = bias ? widen16<BF16>(bias_raw) : 0.0f;
     Y[(size_t)e_m * N + n_e] = narrow16<BF16>(y * (scb_raw / code_max<FP8>()) + bv);

@@ -360,6 +360,11 @@ LINEAR = [
     (257, 769, 448, BF16, 40, True, 6.0),     # tiled; the activation kernel gathers codes
     (64, 33, 576, F16, 150, True, 6.0),
     (300, 100, 1024, F16, 2, True, 0.0),      # more outlier columns than the workspace holds
+    # the fused decode kernel with more than 8 outlier columns: the 16-bit
+    # product as MFMAs over all of K against X masked to the outlier columns
+    (8, 512, 4096, F16, 4, True, 0.0),
+    (4, 300, 8192, BF16, 40, False, 6.0),     # two chunks per thread
+    (8, 96, 4096, BF16, 0, True, 2.0),        # a few hundred columns at t = 2
 ]
 
 
