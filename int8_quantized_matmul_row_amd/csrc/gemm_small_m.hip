@@ -17,6 +17,8 @@
 // steps ahead of the MFMAs that consume them.  The per-wave partial tiles are
 // summed through LDS, then 256 threads each finish one (m, n):
 //   Y = (C * SCA[m]/127 + sum_j XO[m,j] * CB[n, idx[j]]) * SCB[n]/127 + bias[n]
+// With more than 32 outlier columns the outlier sum runs as 16-bit MFMAs over
+// blocks of 32 outlier ranks (XO rows against the gathered weight codes).
 //
 // FP8 (the E4M3 variant; format in common.h): each 16-byte step feeds two
 // v_mfma_f32_16x16x32_fp8_fp8, one per 8-byte half (again the same split for
@@ -30,6 +32,7 @@ namespace llmint8 {
 namespace {
 
 constexpr int kBatch = 8;
+constexpr int kDenseOut = 32;  // more outlier columns than this: the outlier product as MFMAs
 
 template <int WAVES>
 __device__ __forceinline__ void load_steps(const int8_t* __restrict__ pa, const int8_t* __restrict__ pb,
@@ -80,6 +83,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     typedef typename SmallAcc<FP8>::vec acc_t;
     typedef typename SmallAcc<FP8>::elem elem_t;
     __shared__ elem_t red[WAVES][4][64];
+    __shared__ float red_o[WAVES][4][64];  // the 16-bit outlier product's partial tiles (many columns)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * 16;
     const int r16 = lane & 15, kg = lane >> 4;
@@ -100,6 +104,44 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[v];
+    // Many outlier columns: the 16-bit outlier product as v_mfma_f32_16x16x32
+    // over blocks of 32 outlier ranks (block q to wave q % WAVES): A = XO rows
+    // (lane: token r16, ranks 32q + 8kg .. +8, contiguous; XO is 0 past
+    // n_out), B = the weight codes at those ranks' columns as 16-bit values
+    // (exact; ranks past n_out read the last outlier column, against XO's 0).
+    // A loop over the columns per output would take one dependent load each.
+    const int n_out = *n_out_ptr;
+    const bool dense_out = n_out > kDenseOut;
+    if (dense_out) {
+        const int n_pad = (n_out + 31) & ~31;
+        const uint16_t* xo = XO + (size_t)min(r16, M - 1) * n_pad + kg * 8;
+        const int8_t* cbr = CB + (size_t)min(n0 + r16, N - 1) * K;
+        v4f acc_o = {0, 0, 0, 0};
+        for (int q = wave; q * 32 < n_out; q += WAVES) {
+            const int j0 = q * 32 + kg * 8;
+            const v8u16 a = *reinterpret_cast<const v8u16*>(xo + q * 32);
+            const v4i i0 = *reinterpret_cast<const v4i*>(idx + j0);
+            const v4i i1 = *reinterpret_cast<const v4i*>(idx + j0 + 4);
+            const int last = idx[n_out - 1];
+            v8u16 b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = j0 + e < n_out ? (e < 4 ? i0[e] : i1[e - 4]) : last;
+                b[e] = narrow16<BF16>(code_value<FP8>(cbr[col]));
+            }
+            if constexpr (BF16)
+                acc_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
+                                                                acc_o, 0, 0, 0);
+            else
+                acc_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b),
+                                                               acc_o, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float f = acc_o[v];  // by value: bit_cast of a vector element reads element 0
+            red_o[wave][v][lane] = f;
+        }
+    }
     __syncthreads();
     if (tid >= 256) return;
 
@@ -118,8 +160,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     }
 
     float y = (float)c * (SCA[m] / code_max<FP8>());
-    const int n_out = *n_out_ptr;
-    if (n_out > 0) {
+    if (dense_out) {
+        float o = 0.0f;  // the waves' partial sums, in a fixed order
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) o += red_o[w][v][l];
+        y += o;
+    } else if (n_out > 0) {
         const int n_pad = (n_out + 31) & ~31;
         const uint16_t* xo = XO + (size_t)m * n_pad;
         const int8_t* cb = CB + (size_t)n * K;

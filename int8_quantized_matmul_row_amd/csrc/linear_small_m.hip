@@ -24,7 +24,10 @@
 //    registers; the weight bytes of the outlier columns are picked out of those
 //    same registers into LDS;
 //  * one thread per (token, channel) adds the K-group partial sums and writes
-//      Y = (C * SCA[m]/127 + sum_j XO[m,j] * CB[n, idx[j]]) * SCB[n]/127 + bias[n].
+//      Y = (C * SCA[m]/127 + sum_j XO[m,j] * CB[n, idx[j]]) * SCB[n]/127 + bias[n];
+//    with more than 64 outlier columns (up to every column at threshold 0) the
+//    outlier sum runs as 16-bit MFMAs over all of K against X masked to its
+//    outlier columns and the weight registers.
 // The activation outputs (CA, SCA, the outlier list and count, XO) are written
 // too, so the call has the results of llmint8_quantize_act followed by
 // llmint8_matmul: CA spread over the workgroups, the rest by workgroup 0.
@@ -38,7 +41,7 @@ constexpr int kLinThreads = 512;
 constexpr int kLinWaves = 8;
 constexpr int kLinMaxChunks = 1024;                  // K / 8 (K <= 8192)
 constexpr int kLinCaBytes = 16 * (4096 + 16);        // >= rows * (K + 16) for every variant
-constexpr int kLinOutCap = 64;                       // outliers staged in LDS (more: read from memory)
+constexpr int kLinOutCap = 64;                       // outliers staged in LDS (more: the product as MFMAs)
 
 // MR: activation rows held (8 or 16, >= M); CPT: 8-column chunks per thread
 // (K <= 4096 -> 1, K <= 8192 -> 2 with MR = 8); NB: output channels per
@@ -68,6 +71,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_small_m_kernel(
     __shared__ float scl[16];                       // 127 / SCA (0 for an all-zero row)
     __shared__ int scan_lds[kLinWaves];
     __shared__ int red[kLinWaves][4][64];
+    __shared__ float red_o[kLinWaves][4][64];     // the outlier product's partial tiles (many columns)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n0 = blockIdx.x * NB;
@@ -305,7 +309,51 @@ __global__ __launch_bounds__(kLinThreads) void linear_small_m_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][v][lane] = acc[v];
     }
-    if (n_out > 0) {
+    // More outlier columns than kLinOutCap: the 16-bit outlier product as two
+    // v_mfma_f32_16x16x32 per step over this wave's steps: A = X (read again,
+    // from L2) masked to its outlier columns (lane: token r16, the same 16
+    // columns as its weight bytes; token rows past M read row M-1, unused),
+    // B = the weight codes as 16-bit values (exact).  A loop over the columns
+    // per output would take one dependent load each.
+    const bool dense_out = n_out > kLinOutCap;
+    if (dense_out) {
+        const uint16_t* px = X + (size_t)min(r16, M - 1) * K + kg * 16;
+        v4f acc_o = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int s = grp * SPW + i;
+            if (s < nsteps) {
+                const int c = 8 * s + 2 * kg;
+                const uint32_t bits = (uint32_t)mask[c] | ((uint32_t)mask[c + 1] << 8);
+                v8u16 x0 = *reinterpret_cast<const v8u16*>(px + (size_t)s * 64);
+                v8u16 x1 = *reinterpret_cast<const v8u16*>(px + (size_t)s * 64 + 8);
+                v8u16 b0, b1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    x0[e] = (bits >> e) & 1u ? x0[e] : (unsigned short)0;
+                    x1[e] = (bits >> (8 + e)) & 1u ? x1[e] : (unsigned short)0;
+                    b0[e] = narrow16<BF16>((float)(int8_t)((uint32_t)breg[i][e >> 2] >> (8 * (e & 3))));
+                    b1[e] = narrow16<BF16>((float)(int8_t)((uint32_t)breg[i][2 + (e >> 2)] >> (8 * (e & 3))));
+                }
+                if constexpr (BF16) {
+                    acc_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x0),
+                                                                    __builtin_bit_cast(v8bf, b0), acc_o, 0, 0, 0);
+                    acc_o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, x1),
+                                                                    __builtin_bit_cast(v8bf, b1), acc_o, 0, 0, 0);
+                } else {
+                    acc_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x0),
+                                                                   __builtin_bit_cast(v8h, b0), acc_o, 0, 0, 0);
+                    acc_o = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, x1),
+                                                                   __builtin_bit_cast(v8h, b1), acc_o, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float f = acc_o[v];  // by value: bit_cast of a vector element reads element 0
+            red_o[wave][v][lane] = f;
+        }
+    } else if (n_out > 0) {
         // lane (r16, kg) holds the weight bytes of chunks 8 s + 2 kg and 8 s + 2 kg + 1
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
@@ -337,21 +385,13 @@ __global__ __launch_bounds__(kLinThreads) void linear_small_m_kernel(
     for (int g = 0; g < G; ++g) c32 += red[et + T * g][v][l];
     if (C_i32) C_i32[(size_t)e_m * N + n_e] = c32;
     float y = (float)c32 * (sca[e_m] / 127.0f);
-    const int staged = min(n_out, kLinOutCap);
-    for (int j = 0; j < staged; ++j) y += xo_s[e_m][j] * cbo[e_n][j];
-    if (n_out > kLinOutCap) {
-        // more outliers than staged: walk the mask for the rest (slow path)
-        int j = 0;
-        for (int c = 0; c < nchunk; ++c) {
-            uint32_t bits = mask[c];
-            while (bits) {
-                const int k = c * 8 + __builtin_ctz(bits);
-                bits &= bits - 1;
-                if (j >= kLinOutCap)
-                    y += widen16<BF16>(X[(size_t)e_m * K + k]) * (float)CB[(size_t)n_e * K + k];
-                ++j;
-            }
-        }
+    if (dense_out) {
+        float o = 0.0f;  // the groups' partial sums, in a fixed order
+#pragma unroll
+        for (int g = 0; g < G; ++g) o += red_o[et + T * g][v][l];
+        y += o;
+    } else {
+        for (int j = 0; j < n_out; ++j) y += xo_s[e_m][j] * cbo[e_n][j];
     }
     const float bv = bias ? widen16<BF16>(bias_raw) : 0.0f;
     Y[(size_t)e_m * N + n_e] = narrow16<BF16>(y * (scb_raw / 127.0f) + bv);

@@ -77,7 +77,8 @@ def test_ragged_shapes(orc, M, N, K, dt, nout, bias):
 
 
 # ---- degenerate cases the method has ----------------------------------------
-@pytest.mark.parametrize("M,N,K", [(8, 100, 256), (64, 300, 512)])
+@pytest.mark.parametrize("M,N,K", [(8, 100, 256), (64, 300, 512),
+                                   (16, 130, 4096)])  # the small-M product over 4096 outlier columns
 def test_threshold_zero_every_column_outlier(orc, M, N, K):
     wl = synth.make_random(M, N, K, F16, seed=21, n_outlier_cols=2, bias_sigma=0.01)
     g, ref = full_check(orc, wl, threshold=0.0)
