@@ -114,10 +114,11 @@ class Hip:
         return ms.value
 
 
-def load_traffic(config, family, variant="int8"):
+def load_traffic(config, family, variant="int8", threshold=None):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; otherwise None."""
-    suffix = "" if variant == "int8" else f"_{variant}"
+    was taken on the current kernel source (and at the threshold asked for, when
+    it is not the workload's own); otherwise None."""
+    suffix = ("" if variant == "int8" else f"_{variant}") + ("" if threshold is None else f"_t{threshold:g}")
     path = os.path.join(ROOT, "profiles", f"traffic_{config}{suffix}.json")
     if not os.path.exists(path):
         return None
@@ -430,7 +431,7 @@ def main():
     ceiling = measured_ceiling(torch, pkg, dev, roof["bound"], fp8)
     ceiling["frac"] = round(roof["achieved"] / ceiling["value"], 4)
     roof["measured_peak"] = ceiling
-    roof["traffic"] = load_traffic(args.config, fam, args.variant)
+    roof["traffic"] = load_traffic(args.config, fam, args.variant, args.threshold)
     roof["kernel"] = KERNEL_NAMES[fam]
     roof["kernel_ms"] = round(k_ms, 5)
     roof["algorithmic_bytes"] = alg_bytes
