@@ -40,10 +40,11 @@
 //    (4 tile rows per group) and its tiles share CA/CB panels in its own L2.
 //  * Few tiles (at most half the CUs, e.g. M = 512 against a 57344-long K):
 //    given a workspace, K is split over up to 8 workgroups per tile.  Each
-//    stores its int32 (FP8: fp32) accumulators there and counts itself in
-//    with an atomic; the last to arrive adds the partial sums in split order
-//    (the same result whichever arrives last; exact for int8) and runs the
-//    epilogue.  The counters are zeroed by a kernel ahead of the GEMM.
+//    stores its int32 (FP8: fp32) accumulators there with device-coherent
+//    stores (no fence writes back the XCD's L2) and counts itself in with an
+//    atomic; the last to arrive reads every part back coherently, adds them in
+//    split order (the same result whichever arrives last; exact for int8) and
+//    runs the epilogue.  The counters are zeroed by a kernel ahead of the GEMM.
 //  * Epilogue: accumulators -> fp32 times SCA[m]/127 (FP8: /448), plus the
 //    16-bit outlier product as v_mfma_f32_32x32x16_{f16,bf16} of the weight
 //    codes at the outlier columns (int8 values and E4M3 values are exact in
@@ -357,15 +358,22 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
 
 // ---- split K: the partial sums meet in the workspace --------------------------
 // Stored in register order: 16 bytes (registers 4c..4c+3 of a block) per lane,
-// a wave's 64 lanes contiguous, so every access is a full 1 KiB.  Returns
-// whether this workgroup finishes the tile (the last to arrive); it then holds
-// the sum of every split's part, in split order.
+// a wave's 64 lanes contiguous, so every access is a full 1 KiB.  The stores
+// and the last arriver's loads are device-coherent (sc1: written through,
+// read past a stale L2 line), so no device-scope fence has to write back or
+// invalidate a whole XCD's L2: the stores complete (vmcnt) before the arrival
+// count, and the loads follow it.  Returns whether this workgroup finishes the
+// tile (the last to arrive); it then holds the sum of every split's part, in
+// split order.  st: the tile's index among the split tiles.
 template <bool FP8>
-__device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[4][JB], int tile, int ks, int split,
+__device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[4][JB], int st, int ks, int split,
                                           uint32_t* __restrict__ counters, int32_t* __restrict__ part, int wave,
                                           int lane, int tid, int* s_last) {
     typedef typename TileAcc<FP8>::type acc_t;
     constexpr int kWaveWords = 4 * JB * 16 * 64;  // blocks x 16 registers x 64 lanes
+    constexpr int kCoherent = 16;                 // cache policy sc1: device scope
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        part + (size_t)st * split * (kWaves * kWaveWords), 0, split * (kWaves * kWaveWords) * 4, 0x00020000);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -376,18 +384,17 @@ __device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[4][
                 // element reads element 0)
                 const v16i bits = __builtin_bit_cast(v16i, acc[i][j]);
                 const v4i w = {bits[4 * c], bits[4 * c + 1], bits[4 * c + 2], bits[4 * c + 3]};
-                *reinterpret_cast<v4i*>(part + (((size_t)tile * split + ks) * kWaves + wave) * kWaveWords +
-                                        ((i * JB + j) * 4 + c) * 256 + lane * 4) = w;
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    w, rsrc, ((ks * kWaves + wave) * kWaveWords + ((i * JB + j) * 4 + c) * 256 + lane * 4) * 4, 0,
+                    kCoherent);
             }
-    __threadfence();  // the stores are visible device-wide before the count
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part is stored device-wide
     __syncthreads();
-    if (tid == 0) *s_last = atomicAdd(counters + tile, 1u) == (unsigned)(split - 1);
+    if (tid == 0) *s_last = atomicAdd(counters + st, 1u) == (unsigned)(split - 1);
     __syncthreads();
     if (!*s_last) return false;  // another workgroup finishes this tile
-    __threadfence();
     // sum in split order, this workgroup's own part read back too (the same
     // result whichever workgroup arrives last)
-    const int32_t* p0 = part + (size_t)tile * split * (kWaves * kWaveWords) + wave * kWaveWords + lane * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -400,8 +407,9 @@ __device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[4][
                     for (int c = 0; c < 4; ++c) {
                         const auto x = __builtin_bit_cast(
                             typename Part4<FP8>::type,
-                            *reinterpret_cast<const v4i*>(p0 + (size_t)sp * (kWaves * kWaveWords) +
-                                                          ((i * JB + j) * 4 + c) * 256));
+                            __builtin_amdgcn_raw_buffer_load_b128(
+                                rsrc, ((sp * kWaves + wave) * kWaveWords + ((i * JB + j) * 4 + c) * 256 + lane * 4) * 4,
+                                0, kCoherent));
 #pragma unroll
                         for (int e = 0; e < 4; ++e) t[4 * c + e] = sp == 0 ? x[e] : t[4 * c + e] + x[e];
                     }
