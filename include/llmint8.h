@@ -119,11 +119,17 @@ llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of optional device workspace llmint8_matmul can use for M x N x K
- * (0 for M <= 16 and for invalid sizes).  For M > 16 it is the sum of:
- *   - split K, when T = ceil(M/256) * ceil(N/256) tiles fill at most half
- *     of the 256 CUs (T <= 128): S = min(floor(256/T), floor(K/1024), 8) workgroups per
- *     tile (if S >= 2), needing 4T bytes of counters rounded up to 256, then
- *     S * T * 256 KiB of partial tiles;
+ * (0 for M <= 16 and for invalid sizes).  For M > 16 the product works on
+ * tiles of 256 rows by W columns, W = 256 or 224: for each W, T(W) =
+ * ceil(M/256) * ceil(N/W) tiles, S(W) workgroups per tile (below), and the
+ * W with the fewer MFMA cycles per CU, ceil(T*S/256) * W * ceil(ceil(K/128)/S),
+ * is taken, 256 on a tie (224 at 512 x 57344 x 14336 and 512 x 14336 x 57344;
+ * the environment variable LLMINT8_TILE_COLS, "256" or "224", forces one,
+ * for tests).  The workspace is the sum of:
+ *   - split K, when the T tiles fill at most half of the 256 CUs (T <= 128):
+ *     S = min(floor(256/T), floor(K/1024), 8) workgroups per tile (if S >= 2),
+ *     needing 4T bytes of counters rounded up to 256, then S * T * 256 * W * 4
+ *     bytes of partial tiles;
  *   - N * min(K, 1024) bytes: the weight codes at up to 1024 outlier
  *     columns. */
 size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);

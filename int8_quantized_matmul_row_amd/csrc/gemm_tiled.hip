@@ -10,7 +10,11 @@
 // Design (gfx950: 256 CUs in 8 XCDs, 160 KiB LDS per CU, 64 LDS banks):
 //  * Workgroup tile 256 x 256; 4 waves in a 2 x 2 grid, each wave owns a
 //    128 x 128 sub-tile = 4 x 4 blocks of 32 x 32 (256 accumulators per lane,
-//    in AGPRs).  One workgroup per CU.
+//    in AGPRs).  One workgroup per CU.  Where it fills the CUs better (N with
+//    a factor 7, such as 57344 and 14336 at M = 512), the tile is 256 x 224:
+//    4 waves in a 4 x 1 grid, each 64 x 224 = 2 x 7 blocks (224 accumulators);
+//    the host picks the width from the shape (rounds of workgroups times the
+//    work of one).
 //  * K advances in 128-byte stages (one whole line of every row) through a
 //    2-deep ring of LDS buffers (A 256 x 128 + B 256 x 128 bytes, 64 KiB
 //    each).  Stages are filled by buffer_load_dwordx4 ... lds: each wave
@@ -54,9 +58,11 @@
 //    one of two paths, which share no registers (a single kernel with two
 //    separate bodies costs one dispatch):
 //      - plain_body: at most 16 outlier columns, from operands staged in LDS
-//        with the prologue's loads; or, when the other path cannot take the
-//        call (more columns than the gathered codes hold and not simply
-//        columns 0 .. n_out-1, or C exported), per-32-row-block gathers.
+//        with the prologue's loads (the 224-column tile whose K is not split
+//        takes their weight codes from the B stages during the K loop
+//        instead); or, when the other path cannot take the call (more
+//        columns than the gathered codes hold and not simply columns
+//        0 .. n_out-1, or C exported), per-32-row-block gathers.
 //      - outlier_body: more than 16 outlier columns.  After the int8 loop
 //        (skipped when every column is an outlier: CA is then all zero), the
 //        accumulators are dequantized in place and a second K loop of the
@@ -65,31 +71,48 @@
 //        0 .. n_out-1 (every column at threshold 0), else the codes gathered
 //        once per call (gemm_prep, or the activation kernel) into the
 //        workspace.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 
 namespace llmint8 {
 
 namespace {
 
-constexpr int BM = 256, BN = 256;
+constexpr int BM = 256;   // tile rows
+constexpr int kRowsB = 256;  // weight rows per stage in LDS (the widest tile; rows past a narrower tile's are clamped re-reads)
 constexpr int BKS = 128;  // K bytes per stage: one whole 128-byte line of every row
 constexpr int kStages = 2;
-constexpr int kStageBytes = (BM + BN) * BKS;  // 64 KiB
-constexpr int kWavesN = 2;                  // waves along N (2 along M)
-constexpr int kWaves = 2 * kWavesN;
+constexpr int kStageBytes = (BM + kRowsB) * BKS;  // 64 KiB
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int JB = 8 / kWavesN;             // 32-column blocks per wave
-constexpr int kWaveN = 32 * JB;             // columns per wave
 constexpr int kDmaInst = BM / kWaves / 8;   // stage-load instructions (8 rows each) per operand and wave
 constexpr int kGroupM = 4;
 constexpr int kGatherThreads = 256;
 constexpr int kCUs = 256;             // compute units of the device (gfx950)
 constexpr int kMaxSplit = 8;          // workgroups per tile when K is split
 constexpr int kMinSplitStages = 8;    // K stages (128 bytes) per split, at least
-constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
-constexpr int kSmemBytes =
-    kStages * kStageBytes > BM * kYStride ? kStages * kStageBytes : BM * kYStride;
 constexpr int kBarrierAt = 2;         // MFMA block of a stage's second unit at its barrier
+
+// The tile's columns TN and the waves' grid: 256 columns as 2 x 2 waves of
+// 4 x 4 blocks (32 x 32), or 224 columns as 4 x 1 waves of 2 x 7 blocks (224
+// accumulators per lane), for weights whose N holds a factor 7 (the tiles of
+// 256 leave the last round of CUs partly idle).  The stage layout in LDS is
+// the same for both.
+template <int TN>
+struct Tile {
+    static_assert(TN == 256 || TN == 224, "tile columns");
+    static constexpr int BN = TN;
+    static constexpr int WM = TN == 256 ? 2 : 4;  // waves along M
+    static constexpr int WN = kWaves / WM;        // waves along N
+    static constexpr int IB = BM / 32 / WM;       // 32-row blocks per wave
+    static constexpr int JB = BN / 32 / WN;       // 32-column blocks per wave
+    static constexpr int kWaveM = 32 * IB, kWaveN = 32 * JB;
+    static constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
+    static constexpr int kSmemBytes =
+        kStages * kStageBytes > BM * kYStride ? kStages * kStageBytes : BM * kYStride;
+};
 
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int total = tiles_m * tiles_n;
@@ -199,15 +222,16 @@ struct TileGeom {
     bool half_last;
 };
 
+template <int TN>
 __device__ __forceinline__ TileGeom tile_geom(int tile, int ks, int split, int M, int N, int K, int tiles_m,
                                               int tiles_n) {
     TileGeom g;
     int tm, tn;
     map_tile(tile, tiles_m, tiles_n, tm, tn);
     g.m0 = tm * BM;
-    g.n0 = tn * BN;
+    g.n0 = tn * TN;
     g.rows_a = min(BM, M - g.m0);
-    g.rows_b = min(BN, N - g.n0);
+    g.rows_b = min(TN, N - g.n0);
     // K runs in 128-byte stages; a K that is an odd multiple of 64 ends in a
     // half stage, of which only the first 64-byte unit is computed.
     const int nk_all = (K + BKS - 1) / BKS;
@@ -218,31 +242,54 @@ __device__ __forceinline__ TileGeom tile_geom(int tile, int ks, int split, int M
 }
 
 // ---- LDS fragments of a stage in ring buffer u ------------------------------
-// Lane l reads row (l & 31) of each 32-row block.  Fragment f < 4 is A block f
-// of the wave's rows, f >= 4 is B block f - 4 of its columns.
+// Lane l reads row (l & 31) of each 32-row block.  Fragment f < IB is A block
+// f of the wave's rows, f >= IB is B block f - IB of its columns.
+template <int TN>
 __device__ __forceinline__ v8i read_frag8(const int8_t* smem, int u, int h, int f, int wm, int wn, int lane) {
+    typedef Tile<TN> T;
     const int rr = lane & 31;
-    const int a_off = wm * 128 * BKS, b_off = BM * BKS + wn * kWaveN * BKS;
-    const int base = u * kStageBytes + rr * BKS + (f < 4 ? a_off + 32 * f * BKS : b_off + 32 * (f - 4) * BKS);
+    const int a_off = wm * T::kWaveM * BKS, b_off = BM * BKS + wn * T::kWaveN * BKS;
+    const int base =
+        u * kStageBytes + rr * BKS + (f < T::IB ? a_off + 32 * f * BKS : b_off + 32 * (f - T::IB) * BKS);
     const int sw = (rr >> 1) & 7;
     const v4i lo = lds_load<v4i>(smem, (uint32_t)(base + (((4 * h + (lane >> 5)) ^ sw) * 16)));
     const v4i hi = lds_load<v4i>(smem, (uint32_t)(base + (((4 * h + 2 + (lane >> 5)) ^ sw) * 16)));
     return cat8(lo, hi);
 }
 
+// the lane index again, from v_mbcnt (opaque, so that it is not kept in a
+// register across the K loop)
+__device__ __forceinline__ int lane_again() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // ---- the int8 (FP8) K loop of one tile ----------------------------------------
-template <bool FP8>
-__device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB], v8i (&ga)[4], v8i (&gb0)[JB],
-                                       v8i (&gb1)[JB], int8_t* smem, const int8_t* __restrict__ CA,
-                                       const int8_t* __restrict__ CB, int K, const TileGeom& g, int wave,
-                                       int lane) {
+// EXTRACT (a tile whose K is not split): the weight codes of the first
+// outlier columns listed in s_xcol (ascending, ended by -BKS; at most
+// kOutLds, written before the call) are taken from the B stages as they pass
+// through LDS, thread t for the tile's weight row t, into s_wo (row t, column
+// e at s_wo[t * kOutLds + e], as 16-bit values; the other entries are left as
+// they are).  The next column's stage is compared once per stage (one scalar
+// branch), so no load of the weight codes leaves the loop: gathering them
+// from memory cost every tile a 128-byte line per row and column, while the
+// tile's first stages wait behind those loads.
+template <bool BF16, bool FP8, bool EXTRACT, int TN>
+__device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[Tile<TN>::IB][Tile<TN>::JB],
+                                       v8i (&ga)[Tile<TN>::IB], v8i (&gb0)[Tile<TN>::JB], v8i (&gb1)[Tile<TN>::JB],
+                                       int8_t* smem, const int8_t* __restrict__ CA, const int8_t* __restrict__ CB,
+                                       int K, const TileGeom& g, int wave, int lane, uint16_t* s_wo,
+                                       const int* s_xcol) {
     typedef typename TileAcc<FP8>::type acc_t;
-    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    constexpr int IB = Tile<TN>::IB, JB = Tile<TN>::JB;
+    const int wm = wave / Tile<TN>::WN, wn = wave % Tile<TN>::WN;
     // ---- stage loads: one instruction = 8 rows x 128 bytes, whole lines.  Wave
     // w fills rows [64w, 64w + 64) of A and of B, instruction i rows
     // 64w + 8i + lane/8; lane p lands in slot p%8 of its row and so fetches the
-    // logical 16-byte chunk (p%8) ^ ((row/2) % 8).  Rows past M (N) re-read the
-    // last valid row (their results are never stored).
+    // logical 16-byte chunk (p%8) ^ ((row/2) % 8).  Rows past M (N, or the
+    // tile's columns) re-read the last valid row (their results are never
+    // stored).
     const v4i rsrc_a = buffer_rsrc(CA + (size_t)g.m0 * K, (uint32_t)g.rows_a * (uint32_t)K);
     const v4i rsrc_b = buffer_rsrc(CB + (size_t)g.n0 * K, (uint32_t)g.rows_b * (uint32_t)K);
     uint32_t voff_a[kDmaInst], voff_b[kDmaInst];
@@ -265,6 +312,7 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
         else
             dma_line(rsrc_b, voff_b[d - kDmaInst] + kd,
                      lds_base + u * kStageBytes + BM * BKS + 8 * (d - kDmaInst) * BKS);
+        static_assert(kRowsB == BM, "A and B stage rows are loaded by the same instructions");
     };
     // The prologue loads stages 0 and 1; from then on, stage kt loads stage
     // kt + 2 into the buffer it has just finished with, clamped to the last
@@ -275,6 +323,7 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
 #pragma unroll
     for (int d = 0; d < 2 * kDmaInst; ++d) dma(d, min(1, nk - 1), 1);
     wait_vmcnt<2 * kDmaInst>();  // stage 0 and everything issued before it
+    if constexpr (EXTRACT) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): s_xcol and s_wo written
     stage_barrier();
 
     // Fragment f of a unit is 32 bytes per lane.  FP8: one
@@ -290,15 +339,36 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
                                                           __builtin_shufflevector(a, a, 4, 5, 6, 7), c, 0, 0, 0);
         }
     };
-    auto rf = [&](int u, int h, int f) -> v8i { return read_frag8(smem, u, h, f, wm, wn, lane); };
+    auto rf = [&](int u, int h, int f) -> v8i { return read_frag8<TN>(smem, u, h, f, wm, wn, lane); };
+    // the next outlier column to take (uniform) and its place in s_xcol; its
+    // stage is x_col >> 7, -1 at the list's end (no stage matches it, so the
+    // loop below takes at most kOutLds columns in all)
+    int x_p = 0, x_col = -BKS;
+    if constexpr (EXTRACT) x_col = __builtin_amdgcn_readfirstlane(s_xcol[0]);
+    auto extract = [&](int kt, int u) {
+        if constexpr (EXTRACT) {
+            if (kt == (x_col >> 7)) {
+                const int t = wave * 64 + lane_again();  // (nothing held across the loop)
+                const int row = u * kStageBytes + BM * BKS + t * BKS;
+                const int sw = (t >> 1) & 7;
+                do {
+                    const int c = x_col & (BKS - 1);
+                    const int8_t v = smem[row + ((((c >> 4) ^ sw) << 4) | (c & 15))];
+                    if (t < TN) s_wo[t * kOutLds + x_p] = narrow16<BF16>(code_value<FP8>(v));
+                    ++x_p;
+                    x_col = __builtin_amdgcn_readfirstlane(s_xcol[x_p]);
+                } while ((x_col >> 7) == kt);
+            }
+        }
+    };
     // Unit pipeline: MFMA q of a unit is block (i, j) = (q/JB, q%JB).  A block
     // i is refilled with the next unit in place right after its last use (MFMA
     // JB i + JB-1); the B blocks have a second register set (gb1 holds unit 1
     // of every stage, gb0 unit 0).
 #pragma unroll
-    for (int f = 0; f < 4; ++f) ga[f] = rf(0, 0, f);
+    for (int f = 0; f < IB; ++f) ga[f] = rf(0, 0, f);
 #pragma unroll
-    for (int f = 0; f < JB; ++f) gb0[f] = rf(0, 0, 4 + f);
+    for (int f = 0; f < JB; ++f) gb0[f] = rf(0, 0, IB + f);
     // Stage kt in ring buffer u (a compile-time constant: stages run in pairs).
     // Unit 0 reads unit 1 of the same buffer.  kBarrierAt MFMA blocks into unit
     // 1, every wave waits for its loads of stage kt+1 and for its reads of this
@@ -307,17 +377,18 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
     // unit 0 of stage kt+1 and spreads the loads of stage kt+2 into buffer u
     // over its MFMAs, so each load has a whole stage to land.
     auto stage = [&](int kt, int u) {
+        extract(kt, u);  // stage kt is in buffer u until the barrier below
 #pragma unroll
-        for (int q = 0; q < 4 * JB; ++q) {
+        for (int q = 0; q < IB * JB; ++q) {
             const int i = q / JB, j = q % JB;
             acc[i][j] = mma(gb0[j], ga[i], acc[i][j]);
-            if (q < JB) gb1[q] = rf(u, 1, 4 + q);
+            if (q < JB) gb1[q] = rf(u, 1, IB + q);
             if (j == JB - 1) ga[i] = rf(u, 1, i);
             __builtin_amdgcn_sched_barrier(0);
         }
         const int kn = min(kt + 2, nk - 1);
 #pragma unroll
-        for (int q = 0; q < 4 * JB; ++q) {
+        for (int q = 0; q < IB * JB; ++q) {
             const int i = q / JB, j = q % JB;
             acc[i][j] = mma(gb1[j], ga[i], acc[i][j]);
             if (q == kBarrierAt - 1) {
@@ -326,10 +397,10 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
             }
             if (q >= kBarrierAt) {
                 // (at the last stage these read a stale buffer; unused)
-                if (q - kBarrierAt < JB) gb0[q - kBarrierAt] = rf(1 - u, 0, 4 + q - kBarrierAt);
+                if (q - kBarrierAt < JB) gb0[q - kBarrierAt] = rf(1 - u, 0, IB + q - kBarrierAt);
                 if (j == JB - 1) ga[i] = rf(1 - u, 0, i);
                 // loads d0 .. d1-1 of the 2 kDmaInst go out with MFMA q
-                constexpr int kSlots = 4 * JB - kBarrierAt;
+                constexpr int kSlots = IB * JB - kBarrierAt;
                 const int d0 = (q - kBarrierAt) * 2 * kDmaInst / kSlots;
                 const int d1 = (q - kBarrierAt + 1) * 2 * kDmaInst / kSlots;
 #pragma unroll
@@ -346,8 +417,9 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
     }
     if (kt < nfull) stage(kt, 0);
     if (g.half_last) {  // unit 0 of the last stage, in a buffer known at run time
+        extract(nfull, nfull & 1);
 #pragma unroll
-        for (int q = 0; q < 4 * JB; ++q) {
+        for (int q = 0; q < IB * JB; ++q) {
             const int i = q / JB, j = q % JB;
             acc[i][j] = mma(gb0[j], ga[i], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
@@ -365,17 +437,18 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[4][JB]
 // count, and the loads follow it.  Returns whether this workgroup finishes the
 // tile (the last to arrive); it then holds the sum of every split's part, in
 // split order.  st: the tile's index among the split tiles.
-template <bool FP8>
-__device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[4][JB], int st, int ks, int split,
-                                          uint32_t* __restrict__ counters, int32_t* __restrict__ part, int wave,
-                                          int lane, int tid, int* s_last) {
+template <bool FP8, int TN>
+__device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[Tile<TN>::IB][Tile<TN>::JB], int st,
+                                          int ks, int split, uint32_t* __restrict__ counters,
+                                          int32_t* __restrict__ part, int wave, int lane, int tid, int* s_last) {
     typedef typename TileAcc<FP8>::type acc_t;
-    constexpr int kWaveWords = 4 * JB * 16 * 64;  // blocks x 16 registers x 64 lanes
+    constexpr int IB = Tile<TN>::IB, JB = Tile<TN>::JB;
+    constexpr int kWaveWords = IB * JB * 16 * 64;  // blocks x 16 registers x 64 lanes
     constexpr int kCoherent = 16;                 // cache policy sc1: device scope
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         part + (size_t)st * split * (kWaves * kWaveWords), 0, split * (kWaves * kWaveWords) * 4, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int j = 0; j < JB; ++j)
 #pragma unroll
@@ -396,7 +469,7 @@ __device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[4][
     // sum in split order, this workgroup's own part read back too (the same
     // result whichever workgroup arrives last)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
             acc_t t;
@@ -422,11 +495,15 @@ __device__ __forceinline__ bool split_sum(typename TileAcc<FP8>::type (&acc)[4][
 
 // The int32 (FP8: fp32) accumulators of block row i to C (tests), rows and
 // columns past M, N skipped.
-template <bool FP8>
-__device__ __forceinline__ void export_c(const typename TileAcc<FP8>::type (&acc)[4][JB], int i, int M, int N,
-                                         int m, int n_base, int32_t* __restrict__ C_i32, float* __restrict__ C_f32) {
+template <bool FP8, int TN>
+__device__ __forceinline__ void export_c(const typename TileAcc<FP8>::type (&acc)[Tile<TN>::IB][Tile<TN>::JB], int i,
+                                         int M, int N, int m, int n_base, int32_t* __restrict__ C_i32,
+                                         float* __restrict__ C_f32) {
+    // (opaque per call: the column indices and bounds of every register,
+    // hoisted out of the block-row loop, would take more registers than there are)
+    asm volatile("" : "+v"(n_base), "+v"(m));
 #pragma unroll
-    for (int j = 0; j < JB; ++j)
+    for (int j = 0; j < Tile<TN>::JB; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int n = n_base + 32 * j + 8 * (v >> 2) + (v & 3);
@@ -437,16 +514,19 @@ __device__ __forceinline__ void export_c(const typename TileAcc<FP8>::type (&acc
         }
 }
 
-// Block row i of the wave's sub-tile, dequantized by the row scale (f): times
-// SCB/127 (/448), plus bias, rounded to 16-bit, staged in LDS as 8-byte pieces.
-// Register v of lane l of block (i, j) is row m = 32 i + l%32 and column
-// n = 32 j + 8 (v/4) + 4 (l/32) + v%4 of the wave's sub-tile.
-template <bool BF16>
-__device__ __forceinline__ void stage_y(int8_t* smem, const float* s_sb, const float* s_bias, const v16f (&f)[JB],
-                                        int row, int n_lane) {
+// The first nj of JC blocks of a block row of the wave's sub-tile, dequantized
+// by the row scale (f): times SCB/127 (/448), plus bias, rounded to 16-bit,
+// staged in LDS as 8-byte pieces.  Register v of lane l of block j is row
+// `row` and column n_lane + 32 j + 8 (v/4) + v%4 of the tile (n_lane holds
+// 4 (l/32) and the chunk's first column).
+template <bool BF16, int TN, int JC>
+__device__ __forceinline__ void stage_y(int8_t* smem, const float* s_sb, const float* s_bias, const v16f (&f)[JC],
+                                        int nj, int row, int n_lane) {
+    constexpr int kYStride = Tile<TN>::kYStride;
     uint16_t* ys = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-    for (int j = 0; j < JB; ++j)
+    for (int j = 0; j < JC; ++j)
+        if (j < nj)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
             const int nl = n_lane + 32 * j + 8 * a4;
@@ -461,8 +541,10 @@ __device__ __forceinline__ void stage_y(int8_t* smem, const float* s_sb, const f
 // The staged tile to Y (after a barrier): full 16-byte row-contiguous stores,
 // non-temporal (Y is not read again here; every tile of a round stores at
 // once, and the stream stays out of the way of the operand panels in L2).
+template <int TN>
 __device__ __forceinline__ void store_y(const int8_t* smem, uint16_t* __restrict__ Y, int M, int N, int m0, int n0,
                                         int tid_e) {
+    constexpr int BN = TN, kYStride = Tile<TN>::kYStride;
     const int rows = min(BM, M - m0), cols = min(BN, N - n0);
     if ((N & 7) == 0) {
         // 32 lanes per 512-byte row, 8 rows per pass of the workgroup
@@ -479,14 +561,6 @@ __device__ __forceinline__ void store_y(const int8_t* smem, uint16_t* __restrict
             if (c < cols) Y[(size_t)(m0 + r) * N + n0 + c] = ys[r * (kYStride / 2) + c];
         }
     }
-}
-
-// the lane index again, from v_mbcnt (opaque, so that it is not kept in a
-// register across the K loop)
-__device__ __forceinline__ int lane_again() {
-    int l;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-    return l;
 }
 
 }  // namespace
@@ -540,9 +614,9 @@ __global__ __launch_bounds__(kGatherThreads) void gemm_prep(
 // as 16-bit values, 0 past n_out: row r, column e at s_wo[r * kOutLds + e])
 // and s_xo (the tile's rows of XO at those columns: row r at
 // s_xo[r * kOutLds], 0 past n_out: XO's padding).
-template <bool BF16, bool FP8, bool SPLIT>
+template <bool BF16, bool FP8, bool SPLIT, int TN>
 __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_sb, float* s_bias, uint16_t* s_wo,
-                                           uint16_t* s_xo, int* s_last_p, int M, int N, int K, int tiles_m,
+                                           uint16_t* s_xo, int* s_xcol, int* s_last_p, int M, int N, int K, int tiles_m,
                                            int tiles_n, const int8_t* __restrict__ CA, const float* __restrict__ SCA,
                                            const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
                                            const uint16_t* __restrict__ XO, const int8_t* __restrict__ CB,
@@ -552,21 +626,29 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
                                            int wo_cap, int split, uint32_t* __restrict__ counters,
                                            int32_t* __restrict__ part) {
     typedef typename TileAcc<FP8>::type acc_t;
+    typedef Tile<TN> T;
+    constexpr int IB = T::IB, JB = T::JB, BN = T::BN, kWaveN = T::kWaveN;
+    // The weight codes at the first kOutLds outlier columns come from the B
+    // stages in the K loop (see k_loop) for the 224-column tile whose K is
+    // not split; the 256-column tile's epilogue spills with the loop's extra
+    // branch (measured slower), and a split tile sees only its part of K, so
+    // those gather the codes from memory ahead of the loop.
+    constexpr bool kExtract = TN == 224 && !SPLIT;
 
     const bool want_c = FP8 ? C_f32 != nullptr : C_i32 != nullptr;
     const int n_out = *n_out_ptr;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / kWavesN, wn = wave % kWavesN;
+    const int wm = wave / T::WN, wn = wave % T::WN;
     // SPLIT: workgroup b takes split ks = b % split of tile b / split
     if constexpr (!SPLIT) split = 1;
     const int tile = blockIdx.x / split, ks = blockIdx.x - tile * split;
-    const TileGeom g = tile_geom(tile, ks, split, M, N, K, tiles_m, tiles_n);
+    const TileGeom g = tile_geom<TN>(tile, ks, split, M, N, K, tiles_m, tiles_n);
     const int m0 = g.m0, n0 = g.n0;
 
-    acc_t acc[4][JB];
+    acc_t acc[IB][JB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int j = 0; j < JB; ++j) acc[i][j] = acc_t{};
 
@@ -582,33 +664,48 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
     const int n_sb = min(n0 + t8, N - 1);
     float sb_raw = SCB[n_sb];
     uint16_t bias_raw = *(bias ? bias + n_sb : XO);  // XO: any readable element
+    // The weight codes at the first kOutLds outlier columns: gathered here
+    // (lane column e = tid % 16, rows tid/16 + 16 q; lanes past n_out read
+    // column 0 and are masked), or, with kExtract, taken by the K loop into
+    // this thread's row of s_wo, zeroed first.
     const int e_out = tid & (kOutLds - 1);
     const bool e_valid = e_out < n_out;
-    int e_col = 0;
-#pragma unroll
-    for (int u = 0; u < kOutLds; ++u) {  // uniform reads; idx holds K >= 64 entries
-        int c = idx[u];
-        asm volatile("" : "+s"(c));  // all sixteen read, then selected without branches
-        e_col = u == e_out ? c : e_col;
-    }
-    if (!e_valid) e_col = 0;
-    constexpr int kWoPasses = BN * kOutLds / kThreads;  // rows tid/16 + (kThreads/16) q
+    constexpr int kWoPasses = !kExtract ? BN * kOutLds / kThreads : 1;  // rows tid/16 + (kThreads/16) q
     int32_t wo_raw[kWoPasses];
+    if constexpr (!kExtract) {
+        int e_col = 0;
 #pragma unroll
-    for (int q = 0; q < kWoPasses; ++q)
-        wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + (kThreads / 16) * q, N - 1) * K + e_col];
+        for (int u = 0; u < kOutLds; ++u) {  // uniform reads; idx holds K >= 64 entries
+            int c = idx[u];
+            asm volatile("" : "+s"(c));  // all sixteen read, then selected without branches
+            e_col = u == e_out ? c : e_col;
+        }
+        if (!e_valid) e_col = 0;
+#pragma unroll
+        for (int q = 0; q < kWoPasses; ++q)
+            wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + (kThreads / 16) * q, N - 1) * K + e_col];
+    } else {
+        if (tid < BN) {
+            *reinterpret_cast<v4i*>(s_wo + tid * kOutLds) = v4i{};
+            *reinterpret_cast<v4i*>(s_wo + tid * kOutLds + 8) = v4i{};
+        }
+        // the first min(n_out, kOutLds) columns, then the end (-BKS)
+        if (tid <= kOutLds) s_xcol[tid] = tid < min(n_out, kOutLds) ? idx[tid] : -BKS;
+    }
     // XO's first kOutLds columns of tile row t8 (in bounds for n_pad = 0 too:
     // XO holds M * K >= 64 elements)
     const int n_pad = (n_out + 31) & ~31;
     const v4i* xo_src = reinterpret_cast<const v4i*>(XO + (size_t)min(m0 + t8, M - 1) * n_pad);
     v4i xo_raw0 = xo_src[0], xo_raw1 = xo_src[1];
 
-    v8i ga[4], gb0[JB], gb1[JB];
-    k_loop<FP8>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane);
+    v8i ga[IB], gb0[JB], gb1[JB];
+    k_loop<BF16, FP8, kExtract, TN>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, s_wo, s_xcol);
 
     asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw), "+v"(xo_raw0), "+v"(xo_raw1));
+    if constexpr (!kExtract) {
 #pragma unroll
-    for (int q = 0; q < kWoPasses; ++q) asm volatile("" : "+v"(wo_raw[q]));
+        for (int q = 0; q < kWoPasses; ++q) asm volatile("" : "+v"(wo_raw[q]));
+    }
     if (kThreads == 256 || tid < 256) {
         s_sa[tid] = sa_raw;
         s_sb[tid] = sb_raw / code_max<FP8>();
@@ -616,7 +713,7 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
         *reinterpret_cast<v4i*>(s_xo + tid * kOutLds) = xo_raw0;
         *reinterpret_cast<v4i*>(s_xo + tid * kOutLds + 8) = xo_raw1;
     }
-    {
+    if constexpr (!kExtract) {
         const uint32_t e_mask = e_valid ? 0xFFFFu : 0u;  // a mask, not a select: no branches
 #pragma unroll
         for (int q = 0; q < kWoPasses; ++q)
@@ -625,34 +722,42 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
     }
 
     if constexpr (SPLIT) {
-        if (!split_sum<FP8>(acc, tile, ks, split, counters, part, wave, lane, tid, s_last_p)) return;
+        if (!split_sum<FP8, TN>(acc, tile, ks, split, counters, part, wave, lane, tid, s_last_p)) return;
     }
 
     // ---- epilogue, one 32-row block at a time -----------------------------------
     __syncthreads();  // every wave is done reading the stage buffers
     const int lane_e = lane_again();
     const int kh = lane_e >> 5, rr_e = lane_e & 31, tid_e = wave * 64 + lane_e;
-    const int m_lane = wm * 128 + rr_e;              // + 32 i
+    const int m_lane = wm * T::kWaveM + rr_e;        // + 32 i
     const int n_lane = wn * kWaveN + 4 * kh;       // + 32 j + 8 (v/4) + v%4
     typedef typename Vec16<BF16>::type vec_t;
+    // column blocks per step of the epilogue: at most 4 (64 fp32 values per
+    // lane), so the 7 blocks of a 224-column tile go in two steps
+    constexpr int JC = JB < 4 ? JB : 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < IB; ++i) {
         const int m = m0 + m_lane + 32 * i;
-        if (want_c) export_c<FP8>(acc, i, M, N, m, n0 + n_lane, C_i32, C_f32);
+        if (want_c) export_c<FP8, TN>(acc, i, M, N, m, n0 + n_lane, C_i32, C_f32);
         const float sa = s_sa[m_lane + 32 * i] / code_max<FP8>();
-        v16f f[JB];
 #pragma unroll
-        for (int j = 0; j < JB; ++j)
+        for (int jb0 = 0; jb0 < JB; jb0 += JC) {
+        const int nj = JB - jb0 < JC ? JB - jb0 : JC;
+        v16f f[JC];
 #pragma unroll
-            for (int v = 0; v < 16; ++v) f[j][v] = (float)acc[i][j][v] * sa;
+        for (int j = 0; j < JC; ++j)
+            if (j < nj)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) f[j][v] = (float)acc[i][jb0 + j][v] * sa;
         if (n_out > 0) {
             // the codes and XO of the first kOutLds columns, staged in LDS (XO
             // rows as the B operand: the transposed product)
             const v8u16 xraw = *reinterpret_cast<const v8u16*>(s_xo + (m_lane + 32 * i) * kOutLds + 8 * kh);
 #pragma unroll
-            for (int j = 0; j < JB; ++j) {
+            for (int j = 0; j < JC; ++j) {
+                if (j >= nj) continue;
                 const v8u16 raw =
-                    *reinterpret_cast<const v8u16*>(s_wo + (wn * kWaveN + 32 * j + rr_e) * kOutLds + 8 * kh);
+                    *reinterpret_cast<const v8u16*>(s_wo + (wn * kWaveN + 32 * (jb0 + j) + rr_e) * kOutLds + 8 * kh);
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), __builtin_bit_cast(vec_t, xraw), f[j]);
             }
         }
@@ -667,12 +772,12 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
             const vec_t xa = __builtin_bit_cast(
                 vec_t, *reinterpret_cast<const v8u16*>(XO + (size_t)min(m, M - 1) * n_pad + j0 + 8 * kh));
             const int first = idx[j0], last = idx[min(j0 + 15, n_out - 1)];
-            int b[JB][8];
+            int b[JC][8];
             uint32_t keep = 0xffu;
             if (j0 + 16 <= n_out && last - first == 15 && (first & 7) == 0) {
 #pragma unroll
-                for (int j = 0; j < JB; ++j) {
-                    const int8_t* cb = CB + (size_t)min(n0 + wn * kWaveN + 32 * j + rr_e, N - 1) * K;
+                for (int j = 0; j < JC; ++j) {
+                    const int8_t* cb = CB + (size_t)min(n0 + wn * kWaveN + 32 * (jb0 + j) + rr_e, N - 1) * K;
                     const uint2 w8 = *reinterpret_cast<const uint2*>(cb + first + 8 * kh);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) b[j][e] = (int)((e < 4 ? w8.x : w8.y) >> (8 * (e & 3)));
@@ -688,22 +793,21 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
                     keep |= (j0 + 8 * kh + e < n_out ? 1u : 0u) << e;
                 }
 #pragma unroll
-                for (int j = 0; j < JB; ++j) {
-                    const int8_t* cb = CB + (size_t)min(n0 + wn * kWaveN + 32 * j + rr_e, N - 1) * K;
+                for (int j = 0; j < JC; ++j) {
+                    const int8_t* cb = CB + (size_t)min(n0 + wn * kWaveN + 32 * (jb0 + j) + rr_e, N - 1) * K;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) b[j][e] = cb[kcol[e]];
                 }
                 // all the byte loads in flight before the first wait
 #pragma unroll
-                for (int j = 0; j < JB; j += 2)
+                for (int j = 0; j < JC; ++j)
                     asm volatile(""
                                  : "+v"(b[j][0]), "+v"(b[j][1]), "+v"(b[j][2]), "+v"(b[j][3]), "+v"(b[j][4]),
-                                   "+v"(b[j][5]), "+v"(b[j][6]), "+v"(b[j][7]), "+v"(b[j + 1][0]),
-                                   "+v"(b[j + 1][1]), "+v"(b[j + 1][2]), "+v"(b[j + 1][3]), "+v"(b[j + 1][4]),
-                                   "+v"(b[j + 1][5]), "+v"(b[j + 1][6]), "+v"(b[j + 1][7]));
+                                   "+v"(b[j][5]), "+v"(b[j][6]), "+v"(b[j][7]));
             }
 #pragma unroll
-            for (int j = 0; j < JB; ++j) {
+            for (int j = 0; j < JC; ++j) {
+                if (j >= nj) continue;
                 v8u16 raw;
 #pragma unroll
                 for (int e = 0; e < 8; ++e)  // exact in fp16 and bf16
@@ -711,16 +815,17 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
-        stage_y<BF16>(smem, s_sb, s_bias, f, m_lane + 32 * i, n_lane);
+        stage_y<BF16, TN, JC>(smem, s_sb, s_bias, f, nj, m_lane + 32 * i, n_lane + 32 * jb0);
+        }
     }
     __syncthreads();
-    store_y(smem, Y, M, N, m0, n0, tid_e);
+    store_y<TN>(smem, Y, M, N, m0, n0, tid_e);
 }
 
 // More than kOutLds outlier columns whose codes are CB's first columns or
 // gathered in the workspace.  Workgroup b takes tile b / split, split b % split
 // (one tile per workgroup: a loop over tiles spills the accumulators).
-template <bool BF16, bool FP8, bool SPLIT>
+template <bool BF16, bool FP8, bool SPLIT, int TN>
 __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s_sb, float* s_bias, int* s_last_p,
                                              int M, int N, int K, int tiles_m, int tiles_n,
                                              const int8_t* __restrict__ CA, const float* __restrict__ SCA,
@@ -732,6 +837,8 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
                                              int wo_cap, int split, uint32_t* __restrict__ counters,
                                              int32_t* __restrict__ part) {
     typedef typename TileAcc<FP8>::type acc_t;
+    typedef Tile<TN> T;
+    constexpr int IB = T::IB, JB = T::JB, kWaveN = T::kWaveN;
 
     const int n_out = *n_out_ptr;
     if constexpr (!SPLIT) split = 1;
@@ -746,14 +853,14 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
     {
         const int w = blockIdx.x;
         const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wm = wave / kWavesN, wn = wave % kWavesN;
+        const int wm = wave / T::WN, wn = wave % T::WN;
         const int tile = w / split, ks = w - tile * split;
-        const TileGeom g = tile_geom(tile, ks, split, M, N, K, tiles_m, tiles_n);
+        const TileGeom g = tile_geom<TN>(tile, ks, split, M, N, K, tiles_m, tiles_n);
         const int m0 = g.m0, n0 = g.n0;
 
-        acc_t acc[4][JB];
+        acc_t acc[IB][JB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < IB; ++i)
 #pragma unroll
             for (int j = 0; j < JB; ++j) acc[i][j] = acc_t{};
         const int t8 = kThreads > 256 ? (tid & 255) : tid;
@@ -762,8 +869,9 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
         float sb_raw = SCB[n_sb];
         uint16_t bias_raw = *(bias ? bias + n_sb : XO);
 
-        v8i ga[4], gb0[JB], gb1[JB];
-        if (int8_part) k_loop<FP8>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane);
+        v8i ga[IB], gb0[JB], gb1[JB];
+        if (int8_part)
+            k_loop<BF16, FP8, false, TN>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, nullptr, nullptr);
 
         asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw));
         if (kThreads == 256 || tid < 256) {
@@ -772,18 +880,18 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
             s_bias[tid] = bias ? widen16<BF16>(bias_raw) : 0.0f;
         }
         if constexpr (SPLIT) {
-            if (!split_sum<FP8>(acc, tile, ks, split, counters, part, wave, lane, tid, s_last_p)) return;
+            if (!split_sum<FP8, TN>(acc, tile, ks, split, counters, part, wave, lane, tid, s_last_p)) return;
         }
         __syncthreads();  // every wave is done reading the stage buffers; the scales are in LDS
 
         const int lane_e = lane_again();
         const int kh = lane_e >> 5, rr_e = lane_e & 31, tid_e = wave * 64 + lane_e;
-        const int m_lane = wm * 128 + rr_e;
+        const int m_lane = wm * T::kWaveM + rr_e;
         const int n_lane = wn * kWaveN + 4 * kh;
         // dequantize by the row scale in place: from here on the accumulators
         // hold fp32 values (the same AGPRs)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < IB; ++i) {
             const float sa = s_sa[m_lane + 32 * i] / code_max<FP8>();
 #pragma unroll
             for (int j = 0; j < JB; ++j) {
@@ -803,7 +911,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
         // half chunk) is conflict-free.  n_pad is a multiple of 32, so the
         // last stage may be half.
         constexpr int kBo = BM * BKS;
-        constexpr int kDmaC = BN / kWaves / 16;  // code-row instructions (16 rows x 64 bytes) per wave
+        constexpr int kDmaC = kRowsB / kWaves / 16;  // code-row instructions (16 rows x 64 bytes) per wave
         const int8_t* cbase = (prefix ? CB + (size_t)n0 * K : wo_all + (size_t)n0 * wo_cap);
         const v4i rsrc_x = buffer_rsrc(XO + (size_t)m0 * n_pad, (uint32_t)g.rows_a * 2u * (uint32_t)n_pad);
         const v4i rsrc_c = buffer_rsrc(cbase, (uint32_t)g.rows_b * cstride);
@@ -841,7 +949,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
             const v2u c1 = lds_load<v2u>(smem, row + (((2 * h + 1) ^ sw) * 16));
             return cat8(codes8_to16<BF16, FP8>(c0), codes8_to16<BF16, FP8>(c1));
         };
-        auto read_xo = [&](int u, int h, int i) -> v8i { return read_frag8(smem, u, h, i, wm, wn, lane_e); };
+        auto read_xo = [&](int u, int h, int i) -> v8i { return read_frag8<TN>(smem, u, h, i, wm, wn, lane_e); };
         constexpr int kNo = kDmaInst + kDmaC;
 #pragma unroll
         for (int d = 0; d < kNo; ++d) dma_o(d, 0, 0);
@@ -850,7 +958,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
         wait_vmcnt<kNo>();
         stage_barrier();
 #pragma unroll
-        for (int f = 0; f < 4; ++f) ga[f] = read_xo(0, 0, f);
+        for (int f = 0; f < IB; ++f) ga[f] = read_xo(0, 0, f);
 #pragma unroll
         for (int f = 0; f < JB; ++f) gb0[f] = read_codes(0, 0, f);
         // one stage, as the int8 loop's: unit 0 reads unit 1 of the same
@@ -858,7 +966,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
         // of the next stage is read and the stage after it loaded
         auto ostage = [&](int s, int u) {
 #pragma unroll
-            for (int q = 0; q < 4 * JB; ++q) {
+            for (int q = 0; q < IB * JB; ++q) {
                 const int i = q / JB, j = q % JB;
                 acc[i][j] = __builtin_bit_cast(acc_t, mfma16x2<BF16>(gb0[j], ga[i], __builtin_bit_cast(v16f, acc[i][j])));
                 if (q < JB) gb1[q] = read_codes(u, 1, q);
@@ -867,7 +975,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
             }
             const int sn = min(s + 2, no - 1);
 #pragma unroll
-            for (int q = 0; q < 4 * JB; ++q) {
+            for (int q = 0; q < IB * JB; ++q) {
                 const int i = q / JB, j = q % JB;
                 acc[i][j] = __builtin_bit_cast(acc_t, mfma16x2<BF16>(gb1[j], ga[i], __builtin_bit_cast(v16f, acc[i][j])));
                 if (q == kBarrierAt - 1) {
@@ -877,7 +985,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
                 if (q >= kBarrierAt) {
                     if (q - kBarrierAt < JB) gb0[q - kBarrierAt] = read_codes(1 - u, 0, q - kBarrierAt);
                     if (j == JB - 1) ga[i] = read_xo(1 - u, 0, i);
-                    constexpr int kSlots = 4 * JB - kBarrierAt;
+                    constexpr int kSlots = IB * JB - kBarrierAt;
                     const int d0 = (q - kBarrierAt) * kNo / kSlots, d1 = (q - kBarrierAt + 1) * kNo / kSlots;
 #pragma unroll
                     for (int d = d0; d < d1; ++d) dma_o(d, sn, u);
@@ -894,7 +1002,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
         if (so < nfo) ostage(so, 0);
         if (o_half) {
 #pragma unroll
-            for (int q = 0; q < 4 * JB; ++q) {
+            for (int q = 0; q < IB * JB; ++q) {
                 const int i = q / JB, j = q % JB;
                 acc[i][j] = __builtin_bit_cast(acc_t, mfma16x2<BF16>(gb0[j], ga[i], __builtin_bit_cast(v16f, acc[i][j])));
                 __builtin_amdgcn_sched_barrier(0);
@@ -903,21 +1011,27 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
         wait_vmcnt<0>();
         __syncthreads();  // the ring is read out before the Y staging
 
+        constexpr int JC = JB < 4 ? JB : 4;  // column blocks per step (registers)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v16f f[JB];
+        for (int i = 0; i < IB; ++i)
 #pragma unroll
-            for (int j = 0; j < JB; ++j) f[j] = __builtin_bit_cast(v16f, acc[i][j]);
-            stage_y<BF16>(smem, s_sb, s_bias, f, m_lane + 32 * i, n_lane);
-        }
+            for (int jb0 = 0; jb0 < JB; jb0 += JC) {
+                const int nj = JB - jb0 < JC ? JB - jb0 : JC;
+                v16f f[JC];
+#pragma unroll
+                for (int j = 0; j < JC; ++j)
+                    if (j < nj) f[j] = __builtin_bit_cast(v16f, acc[i][jb0 + j]);
+                stage_y<BF16, TN, JC>(smem, s_sb, s_bias, f, nj, m_lane + 32 * i, n_lane + 32 * jb0);
+            }
         __syncthreads();
-        store_y(smem, Y, M, N, m0, n0, tid_e);
+        store_y<TN>(smem, Y, M, N, m0, n0, tid_e);
     }
 }
 
 // The product's one kernel: workgroup b computes tile b / split (split b %
-// split of its K stages) on one of the two paths, chosen by n_out.
-template <bool BF16, bool FP8, bool SPLIT>
+// split of its K stages) on one of the two paths, chosen by n_out; TN is the
+// tile's columns (256 or 224).
+template <bool BF16, bool FP8, bool SPLIT, int TN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const int8_t* __restrict__ CA, const float* __restrict__ SCA,
@@ -928,19 +1042,20 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        float* __restrict__ C_f32, const int8_t* __restrict__ wo_all,
                        int wo_cap, int split, uint32_t* __restrict__ counters,
                        int32_t* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) int8_t smem[kSmemBytes];
-    __shared__ float s_sa[BM], s_sb[BN], s_bias[BN];
-    __shared__ __attribute__((aligned(16))) uint16_t s_wo[BN * kOutLds];
+    __shared__ __attribute__((aligned(16))) int8_t smem[Tile<TN>::kSmemBytes];
+    __shared__ float s_sa[BM], s_sb[kThreads], s_bias[kThreads];  // (entries past TN unused)
+    __shared__ __attribute__((aligned(16))) uint16_t s_wo[TN * kOutLds];
     __shared__ __attribute__((aligned(16))) uint16_t s_xo[BM * kOutLds];
+    __shared__ int s_xcol[kOutLds + 1];
     __shared__ int s_last;
     const int n_out = *n_out_ptr;
     if (outlier_path_takes(n_out, idx, wo_all, wo_cap, FP8 ? C_f32 != nullptr : C_i32 != nullptr)) {
-        outlier_body<BF16, FP8, SPLIT>(smem, s_sa, s_sb, s_bias, &s_last, M, N, K, tiles_m, tiles_n, CA, SCA,
+        outlier_body<BF16, FP8, SPLIT, TN>(smem, s_sa, s_sb, s_bias, &s_last, M, N, K, tiles_m, tiles_n, CA, SCA,
                                        idx, n_out_ptr, XO, CB, SCB, bias, Y, C_i32, C_f32, wo_all, wo_cap, split,
                                        counters, part);
         return;
     }
-    plain_body<BF16, FP8, SPLIT>(smem, s_sa, s_sb, s_bias, s_wo, s_xo, &s_last, M, N, K, tiles_m, tiles_n, CA, SCA,
+    plain_body<BF16, FP8, SPLIT, TN>(smem, s_sa, s_sb, s_bias, s_wo, s_xo, s_xcol, &s_last, M, N, K, tiles_m, tiles_n, CA, SCA,
                                  idx, n_out_ptr, XO, CB, SCB, bias, Y, C_i32, C_f32, wo_all, wo_cap, split,
                                  counters, part);
 }
@@ -949,11 +1064,13 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
 // columns (a multiple of 64): cap int8 codes per weight row.
 static size_t gathered_codes_bytes(int64_t N, int64_t cap) { return (size_t)N * (size_t)cap; }
 
+static int64_t tiles_of(int64_t M, int64_t N, int tn) { return ((M + BM - 1) / BM) * ((N + tn - 1) / tn); }
+
 // Workgroups per tile: split K when the tiles fill at most half the CUs, into
 // as many parts as keep one workgroup per CU, each at least kMinSplitStages
 // stages long.
-static int split_of(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+static int split_for(int64_t M, int64_t N, int64_t K, int tn) {
+    const int64_t tiles = tiles_of(M, N, tn);
     if (tiles == 0 || tiles * 2 > kCUs) return 1;  // (no tiles: an empty call)
     int64_t s = kCUs / tiles;
     if (s > K / BKS / kMinSplitStages) s = K / BKS / kMinSplitStages;
@@ -961,12 +1078,41 @@ static int split_of(int64_t M, int64_t N, int64_t K) {
     return s < 1 ? 1 : (int)s;
 }
 
+// The tile's columns: 224 where it takes fewer MFMA cycles per CU than 256
+// (rounds of kCUs workgroups, each of tn columns and its share of the K
+// stages), for instance N = 57344 or 14336 (a factor 7) at M = 512; 256
+// otherwise, ties included.  A function of the shape (and of the
+// environment variable LLMINT8_TILE_COLS, "256" or "224", which forces one),
+// so the workspace size and the launch agree.
+static int tile_cols(int64_t M, int64_t N, int64_t K) {
+    if (const char* force = std::getenv("LLMINT8_TILE_COLS")) {
+        if (std::strcmp(force, "256") == 0) return 256;
+        if (std::strcmp(force, "224") == 0) return 224;
+    }
+    const int64_t nk = (K + BKS - 1) / BKS;
+    int best = 256;
+    int64_t best_cost = 0;
+    for (int tn : {256, 224}) {
+        const int split = split_for(M, N, K, tn);
+        const int64_t rounds = (tiles_of(M, N, tn) * split + kCUs - 1) / kCUs;
+        const int64_t cost = rounds * tn * ((nk + split - 1) / split);
+        if (tn == 256 || cost < best_cost) {
+            best = tn;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+static int split_of(int64_t M, int64_t N, int64_t K) { return split_for(M, N, K, tile_cols(M, N, K)); }
+
 // arrival counters (padded to 256 bytes), then split x tiles partial tiles
 static size_t split_bytes(int64_t M, int64_t N, int64_t K) {
     const int split = split_of(M, N, K);
     if (split <= 1) return 0;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    return (((size_t)tiles * 4 + 255) & ~(size_t)255) + (size_t)split * tiles * BM * BN * 4;
+    const int tn = tile_cols(M, N, K);
+    const int64_t tiles = tiles_of(M, N, tn);
+    return (((size_t)tiles * 4 + 255) & ~(size_t)255) + (size_t)split * tiles * BM * tn * 4;
 }
 
 size_t gemm_tiled_workspace(int64_t M, int64_t N, int64_t K) {
@@ -983,7 +1129,7 @@ TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes) {
     char* p = static_cast<char*>(ws);
     const size_t sb = split_bytes(M, N, K);
     if (sb > 0 && ws_bytes >= sb) {
-        const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        const int tiles = (int)tiles_of(M, N, tile_cols(M, N, K));
         L.split = split_of(M, N, K);
         L.counters = reinterpret_cast<uint32_t*>(p);
         L.n_counters = tiles;
@@ -1001,7 +1147,8 @@ TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes) {
 
 hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                              hipEvent_t ev_stop) {
-    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+    const int tn = tile_cols(a.M, a.N, a.K);
+    const int tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + tn - 1) / tn;
     const TiledLayout L = tiled_layout(a.M, a.N, a.K, a.ws, a.ws_bytes);
     int8_t* gather_to = a.codes_gathered ? nullptr : L.codes;
     if (gather_to != nullptr || L.split > 1) {
@@ -1020,15 +1167,19 @@ hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t
                              const int32_t*, const uint16_t*, const int8_t*, const float*,
                              const uint16_t*, uint16_t*, int32_t*, float*, const int8_t*, int, int,
                              uint32_t*, int32_t*);
-    const bool sp = L.split > 1;
-    const kernel_t plain =
-        sp ? (a.bf16 ? (a.fp8 ? gemm_tiled_kernel<true, true, true> : gemm_tiled_kernel<true, false, true>)
-                     : (a.fp8 ? gemm_tiled_kernel<false, true, true> : gemm_tiled_kernel<false, false, true>))
-           : (a.bf16 ? (a.fp8 ? gemm_tiled_kernel<true, true, false> : gemm_tiled_kernel<true, false, false>)
-                     : (a.fp8 ? gemm_tiled_kernel<false, true, false> : gemm_tiled_kernel<false, false, false>));
+    // [columns 224?][split?][bf16?][fp8?]
+    static const kernel_t kernels[2][2][2][2] = {
+        {{{gemm_tiled_kernel<false, false, false, 256>, gemm_tiled_kernel<false, true, false, 256>},
+          {gemm_tiled_kernel<true, false, false, 256>, gemm_tiled_kernel<true, true, false, 256>}},
+         {{gemm_tiled_kernel<false, false, true, 256>, gemm_tiled_kernel<false, true, true, 256>},
+          {gemm_tiled_kernel<true, false, true, 256>, gemm_tiled_kernel<true, true, true, 256>}}},
+        {{{gemm_tiled_kernel<false, false, false, 224>, gemm_tiled_kernel<false, true, false, 224>},
+          {gemm_tiled_kernel<true, false, false, 224>, gemm_tiled_kernel<true, true, false, 224>}},
+         {{gemm_tiled_kernel<false, false, true, 224>, gemm_tiled_kernel<false, true, true, 224>},
+          {gemm_tiled_kernel<true, false, true, 224>, gemm_tiled_kernel<true, true, true, 224>}}}};
+    const kernel_t plain = kernels[tn == 224][L.split > 1][a.bf16][a.fp8];
     const int items = tiles_m * tiles_n * L.split;
-    // Both kernels go out; each reads n_out and one exits at once.  The events
-    // (when given) bracket the two dispatches.
+    // one dispatch; the events (when given) bracket it
     dim3 block(kThreads), grid(items);
 #define LLMINT8_GEMM_ARGS                                                                                     \
     a.M, a.N, a.K, tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32, \

@@ -73,30 +73,48 @@ def test_quantize_act_validation():
     assert qa(wsb=need - 1) == INVALID
 
 
+def test_tile_width_override(monkeypatch):
+    # LLMINT8_TILE_COLS forces the tiled product's tile width; the workspace
+    # size follows it (112 tiles of 256 columns, split in 2)
+    monkeypatch.setenv("LLMINT8_TILE_COLS", "256")
+    assert pkg.llmint8_matmul_workspace_size(512, 14336, 57344) == \
+        512 + 2 * 112 * (256 * 256 * 4) + 14336 * 1024
+    monkeypatch.setenv("LLMINT8_TILE_COLS", "224")
+    assert pkg.llmint8_matmul_workspace_size(2048, 16384, 4096) == 16 << 20  # no split either way
+    assert pkg.llmint8_matmul_workspace_size(17, 4096, 4096) == \
+        256 + 4 * 19 * (256 * 224 * 4) + 4096 * 1024
+    monkeypatch.setenv("LLMINT8_TILE_COLS", "other")  # ignored
+    assert pkg.llmint8_matmul_workspace_size(512, 14336, 57344) == \
+        512 + 2 * 128 * (256 * 224 * 4) + 14336 * 1024
+
+
 def test_workspace_sizes():
     assert pkg.llmint8_quantize_act_workspace_size(8, 4096) == 0      # one-launch path
     assert pkg.llmint8_quantize_act_workspace_size(2048, 4096) > 0
     assert pkg.llmint8_quantize_act_workspace_size(64, 100) == 0       # unsupported K
-    # the tiled product: split-K partial tiles when the 256 x 256 tiles fill
-    # under half of the 256 CUs (256 KiB each, per split, after 256 bytes of
-    # counters), then the gathered outlier codes (one byte per weight row and
-    # column, up to 1024 columns, fewer when K is smaller); nothing for the
-    # small-M kernel
+    # the tiled product: split-K partial tiles when the 256 x W tiles fill
+    # under half of the 256 CUs (256 * W * 4 bytes each, per split, after 256
+    # bytes of counters), then the gathered outlier codes (one byte per weight
+    # row and column, up to 1024 columns, fewer when K is smaller); nothing
+    # for the small-M kernel.  W = 224 where it takes fewer MFMA cycles per CU
+    # (one round of workgroups either way: 224 columns each), else 256.
+    P224, P256 = 256 * 224 * 4, 256 * 256 * 4
     assert pkg.llmint8_matmul_workspace_size(8, 4096, 4096) == 0
     assert pkg.llmint8_matmul_workspace_size(16, 4096, 4096) == 0
-    # 16 tiles, K = 64 stages split in 4
+    # W = 224: 19 tiles, K = 32 stages split in 4
     assert pkg.llmint8_matmul_workspace_size(17, 4096, 4096) == \
-        256 + 4 * 16 * (256 << 10) + 4096 * 1024
-    # 512 tiles: no split
+        256 + 4 * 19 * P224 + 4096 * 1024
+    # W = 256: 512 tiles (2 rounds; 592 tiles of 224 take 3): no split
     assert pkg.llmint8_matmul_workspace_size(2048, 16384, 4096) == 16 << 20
-    # 2 tiles, but K is 2 stages: no split
+    # 2 tiles, but K is 1 stage: no split
     assert pkg.llmint8_matmul_workspace_size(300, 33, 128) == 33 * 128
     # 1 tile, split in 8 (the most)
     assert pkg.llmint8_matmul_workspace_size(40, 64, 57344) == \
-        256 + 8 * (256 << 10) + 64 * 1024
-    # the BLOOM-shaped down projection: 112 tiles, split in 2
+        256 + 8 * P224 + 64 * 1024
+    # the BLOOM-shaped down projection: 128 tiles of 224 columns (112 of 256
+    # would leave 32 CUs idle), split in 2
     assert pkg.llmint8_matmul_workspace_size(512, 14336, 57344) == \
-        512 + 2 * 112 * (256 << 10) + 14336 * 1024
+        512 + 2 * 128 * P224 + 14336 * 1024
     assert pkg.llmint8_matmul_workspace_size(300, 33, 96) == 0           # unsupported K
     assert pkg.llmint8_matmul_workspace_size(300, 0, 4096) == 0          # empty: no tiles
     assert pkg.llmint8_linear_workspace_size(300, 0, 4096) == \

@@ -25,6 +25,14 @@ def gpu():
     pkg.lib()  # fails loudly when the library is missing
 
 
+@pytest.fixture(params=["256", "224"], ids=["w256", "w224"])
+def tile_cols(request, monkeypatch):
+    """The tiled product's tile width, forced (LLMINT8_TILE_COLS): both
+    kernels' ragged edges, splits and outlier paths get the small shapes."""
+    monkeypatch.setenv("LLMINT8_TILE_COLS", request.param)
+    return int(request.param)
+
+
 def full_check(orc, wl, threshold=None, label=None):
     t = wl.threshold if threshold is None else threshold
     label = label or f"{wl.name} t={t}"
@@ -70,7 +78,9 @@ RAGGED = [
 
 @pytest.mark.parametrize("M,N,K,dt,nout,bias", RAGGED,
                          ids=[f"{r[0]}x{r[1]}x{r[2]}-{synth.DTYPE_NAMES[r[3]]}" for r in RAGGED])
-def test_ragged_shapes(orc, M, N, K, dt, nout, bias):
+def test_ragged_shapes(orc, M, N, K, dt, nout, bias, tile_cols):
+    if M <= 16 and tile_cols == 224:
+        pytest.skip("M <= 16: the small-M kernels, no tiles")
     wl = synth.make_random(M, N, K, dt, seed=M + N + K, n_outlier_cols=nout,
                            bias_sigma=0.01 if bias else None)
     full_check(orc, wl)
@@ -79,7 +89,7 @@ def test_ragged_shapes(orc, M, N, K, dt, nout, bias):
 # ---- degenerate cases the method has ----------------------------------------
 @pytest.mark.parametrize("M,N,K", [(8, 100, 256), (64, 300, 512),
                                    (16, 130, 4096)])  # the small-M product over 4096 outlier columns
-def test_threshold_zero_every_column_outlier(orc, M, N, K):
+def test_threshold_zero_every_column_outlier(orc, M, N, K, tile_cols):
     wl = synth.make_random(M, N, K, F16, seed=21, n_outlier_cols=2, bias_sigma=0.01)
     g, ref = full_check(orc, wl, threshold=0.0)
     assert g["n_out"] == K and not g["CA"].any() and not g["SCA"].any()
@@ -87,7 +97,7 @@ def test_threshold_zero_every_column_outlier(orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 100, 256), (64, 300, 512)])
-def test_threshold_inf_no_outliers(orc, M, N, K):
+def test_threshold_inf_no_outliers(orc, M, N, K, tile_cols):
     wl = synth.make_random(M, N, K, BF16, seed=22, n_outlier_cols=3)
     g, _ = full_check(orc, wl, threshold=float("inf"))
     assert g["n_out"] == 0
@@ -105,7 +115,7 @@ MANY = [
 @pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
 @pytest.mark.parametrize("M,N,K,dt,nout,t", MANY,
                          ids=[f"{r[0]}x{r[1]}x{r[2]}-{r[4]}" for r in MANY])
-def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8):
+def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8, tile_cols):
     """The tiled product gives the same bits whether its outlier K loop reads
     the weight codes gathered into the workspace (default and full-capacity
     workspaces) or the plain kernel gathers them per tile (no workspace, one
@@ -127,7 +137,7 @@ def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8):
         q = pkg.quantize_act(X, t)
         mm = pkg.matmul
     n_out = int(q.n_out.item())
-    log(f"[parity] gathered outlier codes {M}x{N}x{K} fp8={fp8} n_out={n_out}")
+    log(f"[parity] gathered outlier codes {M}x{N}x{K} fp8={fp8} n_out={n_out} tile columns {tile_cols}")
     assert n_out > 16
     default_bytes = pkg.llmint8_matmul_workspace_size(M, N, K)
     full_bytes = N * K                # every column
@@ -171,8 +181,8 @@ def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8):
 
 # ---- K split over several workgroups per tile (few tiles, long K) -----------
 SPLIT = [
-    # M, N, K, dtype, planted outlier columns
-    (300, 700, 4096, F16, 40),    # 6 tiles, K split in 4; codes gathered too
+    # M, N, K, dtype, planted outlier columns (tiles of 256 / 224 columns)
+    (300, 700, 4096, F16, 40),    # 6 / 8 tiles, K split in 4; codes gathered too
     (40, 64, 57344, BF16, 3),     # 1 tile, split in 8
     (520, 300, 2048, BF16, 0),    # 6 tiles, split in 2; three tile rows
     (300, 700, 4160, F16, 20),    # split in 4; the last split ends in a half (64-byte) K stage
@@ -181,7 +191,7 @@ SPLIT = [
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
 @pytest.mark.parametrize("M,N,K,dt,nout", SPLIT, ids=[f"{r[0]}x{r[1]}x{r[2]}" for r in SPLIT])
-def test_split_k_matches_unsplit(M, N, K, dt, nout, fp8):
+def test_split_k_matches_unsplit(M, N, K, dt, nout, fp8, tile_cols):
     """The split product (default workspace) against the unsplit one (no
     workspace): int8 accumulators and Y bit for bit; FP8 accumulators within
     fp32 reassociation error, Y within one 16-bit step.  Two split runs give
@@ -199,7 +209,7 @@ def test_split_k_matches_unsplit(M, N, K, dt, nout, fp8):
     else:
         CB, SCB = pkg.quantize_weight(W)
         q = pkg.quantize_act(X, wl.threshold)
-    log(f"[parity] split K {M}x{N}x{K} fp8={fp8} n_out={int(q.n_out.item())}")
+    log(f"[parity] split K {M}x{N}x{K} fp8={fp8} n_out={int(q.n_out.item())} tile columns {tile_cols}")
     cdt = torch.float32 if fp8 else torch.int32
 
     def run(workspace):
