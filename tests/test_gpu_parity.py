@@ -240,6 +240,28 @@ def test_split_k_matches_unsplit(M, N, K, dt, nout, fp8, tile_cols):
         assert ((y1 - y0).abs() <= step * y0.abs() + 1e-6 * y0.abs().max()).all()
 
 
+# ---- outlier columns at the edges of the 128-byte K stages (the 224-column
+# tile takes their weight codes from the B stages in its K loop; the 256-column
+# tile gathers them from CB) --------------------------------------------------
+EDGE = [
+    # M, N, K, dtype, outlier columns
+    (300, 448, 4160, F16, [0, 127, 128, 4095, 4096, 4159]),    # two in the last, half (64-byte) stage
+    (300, 452, 4160, BF16, list(range(40, 56))),                # 16 adjacent columns in one stage; ragged N
+    (40, 230, 192, F16, [63, 64, 65, 127, 128, 191] + [10 * i + 1 for i in range(11)]),  # 17: one past the 16
+]
+
+
+@pytest.mark.parametrize("M,N,K,dt,cols", EDGE, ids=[f"{r[0]}x{r[1]}x{r[2]}-{len(r[4])}" for r in EDGE])
+def test_outlier_columns_at_stage_edges(orc, M, N, K, dt, cols, tile_cols):
+    wl = synth.make_random(M, N, K, dt, seed=M + K, bias_sigma=0.01)
+    x = synth.bits_to_f32(wl.X, dt)
+    for j, c in enumerate(cols):
+        x[(7 * j) % M, c] = 20.0 if j % 2 == 0 else -20.0
+    wl.X = synth.to_bits(x, dt)
+    g, ref = full_check(orc, wl, label=f"stage edges {M}x{N}x{K} tile columns {tile_cols}")
+    assert list(ref["idx"]) == sorted(cols)
+
+
 @pytest.mark.parametrize("M", [5, 48])
 def test_threshold_boundary_and_zero_rows(orc, M):
     wl = synth.make_random(M, 70, 128, F16, seed=23)
