@@ -110,8 +110,9 @@ struct Tile {
     static constexpr int JB = BN / 32 / WN;       // 32-column blocks per wave
     static constexpr int kWaveM = 32 * IB, kWaveN = 32 * JB;
     static constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
+    // the stage ring, then (after the K loop) two block rows of Y staging
     static constexpr int kSmemBytes =
-        kStages * kStageBytes > BM * kYStride ? kStages * kStageBytes : BM * kYStride;
+        kStages * kStageBytes > 2 * WM * 32 * kYStride ? kStages * kStageBytes : 2 * WM * 32 * kYStride;
 };
 
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -255,6 +256,45 @@ __device__ __forceinline__ v8i read_frag8(const int8_t* smem, int u, int h, int 
     const v4i lo = lds_load<v4i>(smem, (uint32_t)(base + (((4 * h + (lane >> 5)) ^ sw) * 16)));
     const v4i hi = lds_load<v4i>(smem, (uint32_t)(base + (((4 * h + 2 + (lane >> 5)) ^ sw) * 16)));
     return cat8(lo, hi);
+}
+
+// One block row of Y (block i of every wave: WM x 32 rows, staged row sr at
+// sr * kYStride holding tile row (sr / 32) * kWaveM + 32 i + sr % 32) from its
+// staging buffer to Y (after a barrier), rows past M and columns past N
+// skipped: full 16-byte row-contiguous stores, non-temporal (Y is not read
+// again here).  The block rows alternate between two staging buffers, so each
+// is stored while the next is computed, with one barrier per block row
+// (storing the whole tile after its last block row left every tile of a round
+// storing 33.5 MB at once at the end).
+template <int TN>
+__device__ __forceinline__ void store_block(const int8_t* buf, uint16_t* __restrict__ Y, int M, int N, int m0,
+                                            int n0, int i, int tid_e) {
+    typedef Tile<TN> T;
+    constexpr int BN = TN, kYStride = T::kYStride, kRows = T::WM * 32;
+    const int rows = min(BM, M - m0), cols = min(BN, N - n0);
+    auto tile_row = [&](int sr) { return (sr >> 5) * T::kWaveM + 32 * i + (sr & 31); };
+    if ((N & 7) == 0) {
+        const int c8 = (tid_e & 31) * 8;  // 32 lanes per staged row, 8 rows per pass
+#pragma unroll
+        for (int q = 0; q < kRows / (kThreads / 32); ++q) {
+            const int sr = (tid_e >> 5) + (kThreads / 32) * q, tr = tile_row(sr);
+            if (tr < rows && c8 < cols)
+                __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(buf + sr * kYStride + c8 * 2),
+                                            reinterpret_cast<v4i*>(Y + (size_t)(m0 + tr) * N + n0 + c8));
+        }
+    } else {
+        const uint16_t* ys = reinterpret_cast<const uint16_t*>(buf);
+        for (int e = tid_e; e < kRows * BN; e += kThreads) {
+            const int sr = e / BN, c = e - sr * BN, tr = tile_row(sr);
+            if (tr < rows && c < cols) Y[(size_t)(m0 + tr) * N + n0 + c] = ys[sr * (kYStride / 2) + c];
+        }
+    }
+}
+
+// bytes of one block row's staging buffer (two of them alternate)
+template <int TN>
+constexpr int y_block_bytes() {
+    return Tile<TN>::WM * 32 * Tile<TN>::kYStride;
 }
 
 // the lane index again, from v_mbcnt (opaque, so that it is not kept in a
@@ -538,31 +578,6 @@ __device__ __forceinline__ void stage_y(int8_t* smem, const float* s_sb, const f
         }
 }
 
-// The staged tile to Y (after a barrier): full 16-byte row-contiguous stores,
-// non-temporal (Y is not read again here; every tile of a round stores at
-// once, and the stream stays out of the way of the operand panels in L2).
-template <int TN>
-__device__ __forceinline__ void store_y(const int8_t* smem, uint16_t* __restrict__ Y, int M, int N, int m0, int n0,
-                                        int tid_e) {
-    constexpr int BN = TN, kYStride = Tile<TN>::kYStride;
-    const int rows = min(BM, M - m0), cols = min(BN, N - n0);
-    if ((N & 7) == 0) {
-        // 32 lanes per 512-byte row, 8 rows per pass of the workgroup
-        const int c8 = (tid_e & 31) * 8;
-        for (int r = tid_e >> 5; r < rows; r += kThreads / 32) {
-            if (c8 < cols)
-                __builtin_nontemporal_store(*reinterpret_cast<const v4i*>(smem + r * kYStride + c8 * 2),
-                                            reinterpret_cast<v4i*>(Y + (size_t)(m0 + r) * N + n0 + c8));
-        }
-    } else {
-        const uint16_t* ys = reinterpret_cast<const uint16_t*>(smem);
-        for (int e = tid_e; e < rows * BN; e += kThreads) {
-            const int r = e / BN, c = e - r * BN;
-            if (c < cols) Y[(size_t)(m0 + r) * N + n0 + c] = ys[r * (kYStride / 2) + c];
-        }
-    }
-}
-
 }  // namespace
 
 // Ahead of the GEMM: workgroup 0 zeroes the split-K arrival counters (if
@@ -815,11 +830,12 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
                 f[j] = mfma16<BF16>(__builtin_bit_cast(vec_t, raw), xa, f[j]);
             }
         }
-        stage_y<BF16, TN, JC>(smem, s_sb, s_bias, f, nj, m_lane + 32 * i, n_lane + 32 * jb0);
+        stage_y<BF16, TN, JC>(smem + (i & 1) * y_block_bytes<TN>(), s_sb, s_bias, f, nj, wm * 32 + rr_e,
+                              n_lane + 32 * jb0);
         }
+        __syncthreads();  // block row i staged; block row i-1's buffer read out
+        store_block<TN>(smem + (i & 1) * y_block_bytes<TN>(), Y, M, N, m0, n0, i, tid_e);
     }
-    __syncthreads();
-    store_y<TN>(smem, Y, M, N, m0, n0, tid_e);
 }
 
 // More than kOutLds outlier columns whose codes are CB's first columns or
@@ -1013,7 +1029,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
 
         constexpr int JC = JB < 4 ? JB : 4;  // column blocks per step (registers)
 #pragma unroll
-        for (int i = 0; i < IB; ++i)
+        for (int i = 0; i < IB; ++i) {
 #pragma unroll
             for (int jb0 = 0; jb0 < JB; jb0 += JC) {
                 const int nj = JB - jb0 < JC ? JB - jb0 : JC;
@@ -1021,10 +1037,12 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
 #pragma unroll
                 for (int j = 0; j < JC; ++j)
                     if (j < nj) f[j] = __builtin_bit_cast(v16f, acc[i][jb0 + j]);
-                stage_y<BF16, TN, JC>(smem, s_sb, s_bias, f, nj, m_lane + 32 * i, n_lane + 32 * jb0);
+                stage_y<BF16, TN, JC>(smem + (i & 1) * y_block_bytes<TN>(), s_sb, s_bias, f, nj, wm * 32 + rr_e,
+                                      n_lane + 32 * jb0);
             }
-        __syncthreads();
-        store_y<TN>(smem, Y, M, N, m0, n0, tid_e);
+            __syncthreads();  // block row i staged; block row i-1's buffer read out
+            store_block<TN>(smem + (i & 1) * y_block_bytes<TN>(), Y, M, N, m0, n0, i, tid_e);
+        }
     }
 }
 
