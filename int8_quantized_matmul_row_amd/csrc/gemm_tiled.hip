@@ -110,9 +110,12 @@ struct Tile {
     static constexpr int JB = BN / 32 / WN;       // 32-column blocks per wave
     static constexpr int kWaveM = 32 * IB, kWaveN = 32 * JB;
     static constexpr int kYStride = BN * 2 + 16;  // bytes per staged Y row (padding shifts banks)
-    // the stage ring, then (after the K loop) two block rows of Y staging
-    static constexpr int kSmemBytes =
-        kStages * kStageBytes > 2 * WM * 32 * kYStride ? kStages * kStageBytes : 2 * WM * 32 * kYStride;
+    // the stage ring (the 224-column tile: 2 A stages and 3 B stages of 224
+    // rows), then (after the K loop) two block rows of Y staging, and for the
+    // 224-column tile the tile rows of XO behind them
+    static constexpr int kRing = TN == 224 ? 2 * BM * BKS + 3 * 224 * BKS : kStages * kStageBytes;
+    static constexpr int kAfter = 2 * WM * 32 * kYStride + (TN == 224 ? BM * 16 * 2 : 0);
+    static constexpr int kSmemBytes = kRing > kAfter ? kRing : kAfter;
 };
 
 __device__ __forceinline__ void map_tile(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -468,6 +471,200 @@ __device__ __forceinline__ void k_loop(typename TileAcc<FP8>::type (&acc)[Tile<T
     wait_vmcnt<0>();  // the clamped loads past K have landed too
 }
 
+// ---- the 224-column tile's K loop: a deeper ring for the weights ---------------
+// With M = 512 each weight byte serves only 512 rows, so the loop streams its
+// weights from HBM, and one stage of lookahead leaves the MFMAs waiting.  The
+// 224-column tile's B stage is 28 KiB (224 rows), so LDS holds two A stages
+// (32 KiB each, at 0) and three B stages (at kDeepB), 148 KiB in all.  Stage
+// kt reads A buffer kt % 2 and B buffer kt % 3; after its barrier it loads A
+// stage kt + 2 and then B stage kt + 3 into the buffers it has just finished
+// with.  Loads complete in order, and the barrier of stage kt needs stage
+// kt + 1, whose A loads went out in stage kt - 1 just before the B loads of
+// stage kt + 2: only those 7 may still be in flight, so each barrier waits
+// for vmcnt <= kDmaB, and the weights get ~2.5 stages to land.  Stages run in
+// groups of six so that both ring slots are compile-time constants.  The
+// rest as in k_loop (the unit pipeline, the clamped loads past K, EXTRACT).
+constexpr int kDeepB = 2 * BM * BKS;         // B ring offset (after the two A stages)
+constexpr int kDeepBStage = 224 * BKS;       // 28 KiB
+constexpr int kDmaB = 224 / kWaves / 8;      // 7 B-row instructions per wave and stage
+
+template <bool BF16, bool FP8, bool EXTRACT>
+__device__ __forceinline__ void k_loop_deep(typename TileAcc<FP8>::type (&acc)[Tile<224>::IB][Tile<224>::JB],
+                                            v8i (&ga)[Tile<224>::IB], v8i (&gb0)[Tile<224>::JB],
+                                            v8i (&gb1)[Tile<224>::JB], int8_t* smem, const int8_t* __restrict__ CA,
+                                            const int8_t* __restrict__ CB, int K, const TileGeom& g, int wave,
+                                            int lane, uint16_t* s_wo, const int* s_xcol) {
+    typedef typename TileAcc<FP8>::type acc_t;
+    typedef Tile<224> T;
+    constexpr int IB = T::IB, JB = T::JB;
+    static_assert(T::WN == 1 && kDmaB * kWaves * 8 == 224, "4 x 1 waves, 224 weight rows");
+    const int wm = wave;
+    // A: wave w rows [64w, 64w + 64), instruction i rows 64w + 8i + lane/8; B:
+    // wave w rows [56w, 56w + 56), instruction i rows 56w + 8i + lane/8.  Lane p
+    // lands in slot p%8 of its row and fetches chunk (p%8) ^ ((row/2) % 8).
+    const v4i rsrc_a = buffer_rsrc(CA + (size_t)g.m0 * K, (uint32_t)g.rows_a * (uint32_t)K);
+    const v4i rsrc_b = buffer_rsrc(CB + (size_t)g.n0 * K, (uint32_t)g.rows_b * (uint32_t)K);
+    uint32_t voff_a[kDmaInst], voff_b[kDmaB];
+#pragma unroll
+    for (int i = 0; i < kDmaInst; ++i) {
+        const int r = 8 * kDmaInst * wave + 8 * i + (lane >> 3);
+        voff_a[i] = (uint32_t)min(r, g.rows_a - 1) * (uint32_t)K + (uint32_t)g.kt_begin * BKS +
+                    ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i) {
+        const int r = 8 * kDmaB * wave + 8 * i + (lane >> 3);
+        voff_b[i] = (uint32_t)min(r, g.rows_b - 1) * (uint32_t)K + (uint32_t)g.kt_begin * BKS +
+                    ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+    }
+    const uint32_t lds_a = __builtin_amdgcn_readfirstlane(lds_address(smem) + 8 * kDmaInst * wave * BKS);
+    const uint32_t lds_b = __builtin_amdgcn_readfirstlane(lds_address(smem) + kDeepB + 8 * kDmaB * wave * BKS);
+    const int nk = g.nk;
+    // load instruction d of stage kt: A rows into A buffer ua for d < kDmaInst,
+    // then B rows into B buffer ub
+    auto dma = [&](int d, int kt, int ua, int ub) {
+        const uint32_t kd = (uint32_t)kt * BKS;
+        if (d < kDmaInst)
+            dma_line(rsrc_a, voff_a[d] + kd, lds_a + ua * (BM * BKS) + 8 * d * BKS);
+        else
+            dma_line(rsrc_b, voff_b[d - kDmaInst] + kd, lds_b + ub * kDeepBStage + 8 * (d - kDmaInst) * BKS);
+    };
+    constexpr int kNd = kDmaInst + kDmaB;
+    // prologue: stages 0 and 1, then B of stage 2
+#pragma unroll
+    for (int d = 0; d < kNd; ++d) dma(d, 0, 0, 0);
+#pragma unroll
+    for (int d = 0; d < kNd; ++d) dma(d, min(1, nk - 1), 1, 1);
+#pragma unroll
+    for (int d = kDmaInst; d < kNd; ++d) dma(d, min(2, nk - 1), 0, 2);
+    wait_vmcnt<kNd + kDmaB>();  // stage 0 and everything issued before it
+    if constexpr (EXTRACT) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): s_xcol and s_wo written
+    stage_barrier();
+
+    auto mma = [&](const v8i& b, const v8i& a, acc_t c) -> acc_t {
+        if constexpr (FP8) {
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, 127, 0, 127);
+        } else {
+            c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_shufflevector(b, b, 0, 1, 2, 3),
+                                                       __builtin_shufflevector(a, a, 0, 1, 2, 3), c, 0, 0, 0);
+            return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_shufflevector(b, b, 4, 5, 6, 7),
+                                                          __builtin_shufflevector(a, a, 4, 5, 6, 7), c, 0, 0, 0);
+        }
+    };
+    // fragment f of unit h: A block f < IB of this wave's rows in A buffer ua,
+    // else B block f - IB in B buffer ub (the same chunks and swizzle as read_frag8)
+    auto rf = [&](int ua, int ub, int h, int f) -> v8i {
+        const int rr = lane & 31;
+        const int base = (f < IB ? ua * (BM * BKS) + (wm * T::kWaveM + 32 * f) * BKS
+                                 : kDeepB + ub * kDeepBStage + 32 * (f - IB) * BKS) +
+                         rr * BKS;
+        const int sw = (rr >> 1) & 7;
+        const v4i lo = lds_load<v4i>(smem, (uint32_t)(base + (((4 * h + (lane >> 5)) ^ sw) * 16)));
+        const v4i hi = lds_load<v4i>(smem, (uint32_t)(base + (((4 * h + 2 + (lane >> 5)) ^ sw) * 16)));
+        return cat8(lo, hi);
+    };
+    int x_p = 0, x_col = -BKS;
+    if constexpr (EXTRACT) x_col = __builtin_amdgcn_readfirstlane(s_xcol[0]);
+    auto extract = [&](int kt, int ub) {
+        if constexpr (EXTRACT) {
+            if (kt == (x_col >> 7)) {
+                const int t = wave * 64 + lane_again();  // (nothing held across the loop)
+                const int tr = min(t, 223);               // the B buffer holds 224 rows
+                const int row = kDeepB + ub * kDeepBStage + tr * BKS;
+                const int sw = (tr >> 1) & 7;
+                do {
+                    const int c = x_col & (BKS - 1);
+                    const int8_t v = smem[row + ((((c >> 4) ^ sw) << 4) | (c & 15))];
+                    if (t < 224) s_wo[t * kOutLds + x_p] = narrow16<BF16>(code_value<FP8>(v));
+                    ++x_p;
+                    x_col = __builtin_amdgcn_readfirstlane(s_xcol[x_p]);
+                } while ((x_col >> 7) == kt);
+            }
+        }
+    };
+#pragma unroll
+    for (int f = 0; f < IB; ++f) ga[f] = rf(0, 0, 0, f);
+#pragma unroll
+    for (int f = 0; f < JB; ++f) gb0[f] = rf(0, 0, 0, IB + f);
+    auto stage = [&](int kt, int ua, int ub) {
+        extract(kt, ub);  // stage kt is in buffers ua / ub until the barrier below
+#pragma unroll
+        for (int q = 0; q < IB * JB; ++q) {
+            const int i = q / JB, j = q % JB;
+            acc[i][j] = mma(gb0[j], ga[i], acc[i][j]);
+            if (q < JB) gb1[q] = rf(ua, ub, 1, IB + q);
+            if (j == JB - 1) ga[i] = rf(ua, ub, 1, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int ka = min(kt + 2, nk - 1), kb = min(kt + 3, nk - 1);
+        const int na = 1 - ua, nb = ub == 2 ? 0 : ub + 1;  // stage kt + 1's buffers
+#pragma unroll
+        for (int q = 0; q < IB * JB; ++q) {
+            const int i = q / JB, j = q % JB;
+            acc[i][j] = mma(gb1[j], ga[i], acc[i][j]);
+            if (q == kBarrierAt - 1) {
+                // stage kt + 1 has landed (only the B loads of stage kt + 2,
+                // issued after its A loads, may be in flight), and this wave's
+                // reads of buffers ua / ub are complete
+                __builtin_amdgcn_s_waitcnt(kDmaB);  // vmcnt(kDmaB), expcnt and lgkmcnt 0
+                stage_barrier();
+            }
+            if (q >= kBarrierAt) {
+                // (at the last stage these read stale buffers; unused)
+                if (q - kBarrierAt < JB) gb0[q - kBarrierAt] = rf(na, nb, 0, IB + q - kBarrierAt);
+                if (j == JB - 1) ga[i] = rf(na, nb, 0, i);
+                // loads d0 .. d1-1 (A of stage kt + 2 first, then B of stage
+                // kt + 3) go out with MFMA q
+                constexpr int kSlots = IB * JB - kBarrierAt;
+                const int d0 = (q - kBarrierAt) * kNd / kSlots;
+                const int d1 = (q - kBarrierAt + 1) * kNd / kSlots;
+#pragma unroll
+                for (int d = d0; d < d1; ++d) dma(d, d < kDmaInst ? ka : kb, ua, ub);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    const int nfull = g.half_last ? nk - 1 : nk;
+    int kt = 0;
+    for (; kt + 6 <= nfull; kt += 6) {
+        stage(kt, 0, 0);
+        stage(kt + 1, 1, 1);
+        stage(kt + 2, 0, 2);
+        stage(kt + 3, 1, 0);
+        stage(kt + 4, 0, 1);
+        stage(kt + 5, 1, 2);
+    }
+    if (kt < nfull) stage(kt, 0, 0);
+    if (kt + 1 < nfull) stage(kt + 1, 1, 1);
+    if (kt + 2 < nfull) stage(kt + 2, 0, 2);
+    if (kt + 3 < nfull) stage(kt + 3, 1, 0);
+    if (kt + 4 < nfull) stage(kt + 4, 0, 1);
+    if (g.half_last) {  // unit 0 of the last stage (its fragments are in registers)
+        extract(nfull, nfull % 3);
+#pragma unroll
+        for (int q = 0; q < IB * JB; ++q) {
+            const int i = q / JB, j = q % JB;
+            acc[i][j] = mma(gb0[j], ga[i], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    wait_vmcnt<0>();  // the clamped loads past K have landed too
+}
+
+// the K loop of the tile width (the FP8 variant keeps the two-stage ring at
+// 224 columns: with the deep ring its loop spilled ~100 registers)
+template <bool BF16, bool FP8, bool EXTRACT, int TN>
+__device__ __forceinline__ void k_loop_tile(typename TileAcc<FP8>::type (&acc)[Tile<TN>::IB][Tile<TN>::JB],
+                                            v8i (&ga)[Tile<TN>::IB], v8i (&gb0)[Tile<TN>::JB],
+                                            v8i (&gb1)[Tile<TN>::JB], int8_t* smem, const int8_t* __restrict__ CA,
+                                            const int8_t* __restrict__ CB, int K, const TileGeom& g, int wave,
+                                            int lane, uint16_t* s_wo, const int* s_xcol) {
+    if constexpr (TN == 224 && !FP8)
+        k_loop_deep<BF16, FP8, EXTRACT>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, s_wo, s_xcol);
+    else
+        k_loop<BF16, FP8, EXTRACT, TN>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, s_wo, s_xcol);
+}
+
 // ---- split K: the partial sums meet in the workspace --------------------------
 // Stored in register order: 16 bytes (registers 4c..4c+3 of a block) per lane,
 // a wave's 64 lanes contiguous, so every access is a full 1 KiB.  The stores
@@ -714,19 +911,25 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
     v4i xo_raw0 = xo_src[0], xo_raw1 = xo_src[1];
 
     v8i ga[IB], gb0[JB], gb1[JB];
-    k_loop<BF16, FP8, kExtract, TN>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, s_wo, s_xcol);
+    k_loop_tile<BF16, FP8, kExtract, TN>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, s_wo, s_xcol);
 
     asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw), "+v"(xo_raw0), "+v"(xo_raw1));
     if constexpr (!kExtract) {
 #pragma unroll
         for (int q = 0; q < kWoPasses; ++q) asm volatile("" : "+v"(wo_raw[q]));
     }
+    // the 224-column tile keeps XO's rows in the (then dead) stage ring,
+    // written after the barrier below
+    constexpr bool kXoInRing = TN == 224;
+    if constexpr (kXoInRing) s_xo = reinterpret_cast<uint16_t*>(smem + 2 * y_block_bytes<TN>());
     if (kThreads == 256 || tid < 256) {
         s_sa[tid] = sa_raw;
         s_sb[tid] = sb_raw / code_max<FP8>();
         s_bias[tid] = bias ? widen16<BF16>(bias_raw) : 0.0f;
-        *reinterpret_cast<v4i*>(s_xo + tid * kOutLds) = xo_raw0;
-        *reinterpret_cast<v4i*>(s_xo + tid * kOutLds + 8) = xo_raw1;
+        if constexpr (!kXoInRing) {
+            *reinterpret_cast<v4i*>(s_xo + tid * kOutLds) = xo_raw0;
+            *reinterpret_cast<v4i*>(s_xo + tid * kOutLds + 8) = xo_raw1;
+        }
     }
     if constexpr (!kExtract) {
         const uint32_t e_mask = e_valid ? 0xFFFFu : 0u;  // a mask, not a select: no branches
@@ -742,6 +945,13 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
 
     // ---- epilogue, one 32-row block at a time -----------------------------------
     __syncthreads();  // every wave is done reading the stage buffers
+    if constexpr (kXoInRing) {
+        if (kThreads == 256 || tid < 256) {
+            *reinterpret_cast<v4i*>(s_xo + tid * kOutLds) = xo_raw0;
+            *reinterpret_cast<v4i*>(s_xo + tid * kOutLds + 8) = xo_raw1;
+        }
+        __syncthreads();
+    }
     const int lane_e = lane_again();
     const int kh = lane_e >> 5, rr_e = lane_e & 31, tid_e = wave * 64 + lane_e;
     const int m_lane = wm * T::kWaveM + rr_e;        // + 32 i
@@ -887,7 +1097,7 @@ __device__ __forceinline__ void outlier_body(int8_t* smem, float* s_sa, float* s
 
         v8i ga[IB], gb0[JB], gb1[JB];
         if (int8_part)
-            k_loop<BF16, FP8, false, TN>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, nullptr, nullptr);
+            k_loop_tile<BF16, FP8, false, TN>(acc, ga, gb0, gb1, smem, CA, CB, K, g, wave, lane, nullptr, nullptr);
 
         asm volatile("" : "+v"(sa_raw), "+v"(sb_raw), "+v"(bias_raw));
         if (kThreads == 256 || tid < 256) {
@@ -1063,7 +1273,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
     __shared__ __attribute__((aligned(16))) int8_t smem[Tile<TN>::kSmemBytes];
     __shared__ float s_sa[BM], s_sb[kThreads], s_bias[kThreads];  // (entries past TN unused)
     __shared__ __attribute__((aligned(16))) uint16_t s_wo[TN * kOutLds];
-    __shared__ __attribute__((aligned(16))) uint16_t s_xo[BM * kOutLds];
+    __shared__ __attribute__((aligned(16))) uint16_t s_xo[TN == 224 ? 8 : BM * kOutLds];  // (224: in smem)
     __shared__ int s_xcol[kOutLds + 1];
     __shared__ int s_last;
     const int n_out = *n_out_ptr;
