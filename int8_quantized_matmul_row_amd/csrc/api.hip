@@ -202,6 +202,7 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
             gather.CB = CB;
             gather.N = (int)N;
             gather.cap = L.cap;
+            gather.min_cols = L.min_cols;
             gather.out = L.codes;
         }
     }

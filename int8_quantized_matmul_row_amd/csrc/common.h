@@ -174,7 +174,9 @@ __device__ __forceinline__ float code_value(int8_t b) {
 // once per call into a row-major buffer of `cap` bytes per weight row (cap a
 // multiple of 64, n_pad <= cap): byte c of row n is CB[n][col(c)] for
 // c < n_out and 0 for n_out <= c < n_pad (code 0 is +0 in both formats).
-// Outlier counts up to kOutLds are handled from LDS and need no gather.
+// The product stages the codes of the first kOutLds columns in LDS for its
+// epilogue, from this buffer when it holds them (any count up to cap; at
+// most kOutLds columns sit in rows of kOutLds bytes: gather_first_codes).
 constexpr int kOutLds = 16;
 
 // The gather runs over chunks of the outlier list, the same for every weight
@@ -240,6 +242,31 @@ __device__ __forceinline__ void build_gather_chunks(int K, int n_out, SegCount s
     }
     g.lo[n] = n_out;
     g.n = n;
+}
+
+// At most kOutLds outlier columns: their codes in rows of kOutLds bytes
+// instead (byte e of row n is CB[n][col(e)] for e < n_out, 0 after), which
+// the product reads 16 adjacent bytes per weight row.  One (row, column) item
+// per thread of the t0 / nt grid share, four items per thread in flight at
+// once; no barriers.
+template <typename Col>
+__device__ __forceinline__ void gather_first_codes(int N, int K, int n_out, Col col, const int8_t* __restrict__ CB,
+                                                   int8_t* __restrict__ out, int64_t t0, int64_t nt) {
+    const int64_t items = (int64_t)N * kOutLds;
+    for (int64_t base = t0; base < items; base += 4 * nt) {
+        int8_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = min(base + u * nt, items - 1);  // (past the end: re-read the last item)
+            const int e = (int)(i & (kOutLds - 1)), n = (int)(i / kOutLds);
+            v[u] = CB[(size_t)n * K + col(min(e, n_out - 1))];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = base + u * nt;
+            if (i < items) out[i] = (int)(i & (kOutLds - 1)) < n_out ? v[u] : (int8_t)0;
+        }
+    }
 }
 
 // Work items (weight row n, chunk i < nch; chunk(i) its columns and segment),
@@ -449,12 +476,13 @@ hipError_t launch_quantize_tensor(const void* A, bool bf16, int64_t rows, int64_
                                   float* scale, void* ws, hipStream_t stream);
 
 // Weight codes the activation kernel gathers (layout above) for the tiled
-// product that follows it, at most kActGatherCols columns; out == nullptr:
-// none.  The launcher clears out when it did not gather.
+// product that follows it, at most kActGatherCols columns, and only for more
+// than min_cols of them; out == nullptr: none.  The launcher clears out when
+// it did not gather.
 constexpr int kActGatherCols = 1024;
 struct CodeGather {
     const int8_t* CB = nullptr;
-    int N = 0, cap = 0;
+    int N = 0, cap = 0, min_cols = 0;
     int8_t* out = nullptr;
 };
 
@@ -488,7 +516,9 @@ struct MatmulArgs {
 size_t matmul_workspace(int64_t M, int64_t N, int64_t K);
 size_t gemm_tiled_workspace(int64_t M, int64_t N, int64_t K);
 // How the tiled product uses a workspace: split-K arrival counters and
-// partial tiles (split > 1), then the gathered outlier codes (cap columns).
+// partial tiles (split > 1), then the gathered outlier codes (cap columns),
+// gathered when there are more than min_cols outlier columns (kOutLds for the
+// tile that takes its first kOutLds codes from its own K loop, else 0).
 struct TiledLayout {
     int split = 1;
     uint32_t* counters = nullptr;
@@ -496,6 +526,7 @@ struct TiledLayout {
     int32_t* part = nullptr;
     int8_t* codes = nullptr;
     int cap = 0;
+    int min_cols = 0;
 };
 TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes);
 hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,

@@ -779,20 +779,26 @@ __device__ __forceinline__ void stage_y(int8_t* smem, const float* s_sb, const f
 
 // Ahead of the GEMM: workgroup 0 zeroes the split-K arrival counters (if
 // any), and the weight codes at the outlier columns are gathered (layout with
-// gather_codes) when the activation kernel has not done so (codes != nullptr)
-// and outlier_body reads them: more than kOutLds columns, at most cap,
-// and not simply columns 0 .. n_out-1 (whose codes it reads from CB).
+// gather_codes) when the activation kernel has not done so (codes != nullptr):
+// more than min_cols columns (TiledLayout), at most cap, and not simply
+// columns 0 .. n_out-1 (whose codes the product reads from CB).  plain_body
+// reads the first kOutLds of them, outlier_body all.
 __global__ __launch_bounds__(kGatherThreads) void gemm_prep(
-    int N, int K, int cap, const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
+    int N, int K, int cap, int min_cols, const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
     const int8_t* __restrict__ CB, int8_t* __restrict__ codes, uint32_t* __restrict__ counters,
     int n_counters) {
     if (blockIdx.x == 0)
         for (int t = threadIdx.x; t < n_counters; t += kGatherThreads) counters[t] = 0;
     if (codes == nullptr) return;
     const int n_out = *n_out_ptr;
-    if (n_out <= kOutLds || n_out > cap || idx[n_out - 1] == n_out - 1) return;
+    if (n_out <= min_cols || n_out == 0 || n_out > cap || idx[n_out - 1] == n_out - 1) return;
     __shared__ __attribute__((aligned(16))) int8_t buf[(kGatherThreads / 16) * kGatherSeg];
     auto col = [&](int c) { return idx[c]; };
+    if (n_out <= kOutLds) {
+        gather_first_codes(N, K, n_out, col, CB, codes, (int64_t)blockIdx.x * kGatherThreads + threadIdx.x,
+                           (int64_t)gridDim.x * kGatherThreads);
+        return;
+    }
     if (gather_all_sparse(K, n_out)) {
         gather_codes<kGatherThreads>(
             N, K, cap, n_out, col, (n_out + kGatherRun - 1) / kGatherRun,
@@ -876,10 +882,13 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
     const int n_sb = min(n0 + t8, N - 1);
     float sb_raw = SCB[n_sb];
     uint16_t bias_raw = *(bias ? bias + n_sb : XO);  // XO: any readable element
-    // The weight codes at the first kOutLds outlier columns: gathered here
-    // (lane column e = tid % 16, rows tid/16 + 16 q; lanes past n_out read
-    // column 0 and are masked), or, with kExtract, taken by the K loop into
-    // this thread's row of s_wo, zeroed first.
+    // The weight codes at the first kOutLds outlier columns (lane column
+    // e = tid % 16, rows tid/16 + 16 q; lanes past n_out read column 0 and are
+    // masked): from the codes gathered once per call into the workspace when
+    // it holds them (a row's 16 codes are adjacent there, and the rows too
+    // when there are at most 16 columns), else from CB (a 128-byte line per
+    // row and column, for every tile row of the grid again), or, with kExtract,
+    // taken by the K loop into this thread's row of s_wo, zeroed first.
     const int e_out = tid & (kOutLds - 1);
     const bool e_valid = e_out < n_out;
     constexpr int kWoPasses = !kExtract ? BN * kOutLds / kThreads : 1;  // rows tid/16 + (kThreads/16) q
@@ -893,9 +902,17 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
             e_col = u == e_out ? c : e_col;
         }
         if (!e_valid) e_col = 0;
+        // gathered for this call: the same condition as the gather's (more
+        // than TiledLayout::min_cols columns, which is 0 for every tile
+        // without kExtract; at most the workspace's columns; and not simply
+        // 0 .. n_out-1, whose codes are CB's own first columns)
+        const bool gathered = wo_all != nullptr && n_out > 0 && n_out <= wo_cap && idx[max(n_out, 1) - 1] != n_out - 1;
+        const int8_t* w_src = gathered ? wo_all : CB;
+        const size_t w_stride = gathered ? (size_t)(n_out <= kOutLds ? kOutLds : wo_cap) : (size_t)K;
+        const int w_col = gathered ? (e_valid ? e_out : 0) : e_col;
 #pragma unroll
         for (int q = 0; q < kWoPasses; ++q)
-            wo_raw[q] = CB[(size_t)min(n0 + (tid >> 4) + (kThreads / 16) * q, N - 1) * K + e_col];
+            wo_raw[q] = w_src[(size_t)min(n0 + (tid >> 4) + (kThreads / 16) * q, N - 1) * w_stride + w_col];
     } else {
         if (tid < BN) {
             *reinterpret_cast<v4i*>(s_wo + tid * kOutLds) = v4i{};
@@ -1370,6 +1387,10 @@ TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes) {
         L.cap = (int)(fit < k_blocks ? fit : k_blocks) * 64;
         if (L.cap > 0) L.codes = reinterpret_cast<int8_t*>(p);
     }
+    // the 224-column tile whose K is not split takes its first kOutLds codes
+    // from the B stages (plain_body, kExtract); every other tile reads them
+    // from the gather
+    L.min_cols = tile_cols(M, N, K) == 224 && L.split == 1 ? kOutLds : 0;
     return L;
 }
 
@@ -1386,7 +1407,7 @@ hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t
         const int64_t items = (int64_t)a.N * ((a.K + kGatherSeg - 1) / kGatherSeg);
         const int64_t want = (items + kGatherThreads / 16 - 1) / (kGatherThreads / 16);
         const int blocks = gather_to == nullptr ? 1 : (int)(want < 2048 ? (want < 1 ? 1 : want) : 2048);
-        gemm_prep<<<blocks, kGatherThreads, 0, stream>>>(a.N, a.K, L.cap, a.idx, a.n_out, a.CB, gather_to,
+        gemm_prep<<<blocks, kGatherThreads, 0, stream>>>(a.N, a.K, L.cap, L.min_cols, a.idx, a.n_out, a.CB, gather_to,
                                                          L.counters, L.split > 1 ? L.n_counters : 0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -409,9 +409,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
 
     // the weight codes at the outlier columns for the product that follows
     // (when asked for, and when the product reads them from the gather: more
-    // than kOutLds columns, not simply 0 .. total-1): this workgroup's share
+    // than min_cols columns, not simply 0 .. total-1): this workgroup's share
     // of the work items
-    if (gather.out != nullptr && total > kOutLds && total <= gather.cap) {
+    if (gather.out != nullptr && total > gather.min_cols && total <= gather.cap) {
         __shared__ int s_cols[kActGatherCols];
         for (int w = tid; w < nwords; w += kThreads) {
             uint32_t b = mw[w];
@@ -427,6 +427,9 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
         auto col = [&](int c) { return s_cols[c]; };
         if (s_cols[total - 1] == total - 1) {
             // columns 0 .. total-1: the product reads CB itself
+        } else if (total <= kOutLds) {
+            gather_first_codes(gather.N, K, total, col, gather.CB, gather.out, (int64_t)blockIdx.x * kThreads + tid,
+                               (int64_t)gridDim.x * kThreads);
         } else if (gather_all_sparse(K, total)) {
             gather_codes<kThreads>(
                 gather.N, K, gather.cap, total, col, (total + kGatherRun - 1) / kGatherRun,

@@ -179,6 +179,69 @@ def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8, 
         assert torch.equal(Y2.view(torch.int16).cpu(), Y2_none.view(torch.int16).cpu())
 
 
+# ---- at most 16 outlier columns: codes gathered once, in rows of 16 bytes ----
+FEW = [
+    # M, N, K, dtype, planted outlier columns, first columns (0 .. n-1) instead
+    (257, 769, 448, BF16, 5, False),
+    (64, 33, 576, F16, 16, False),
+    (300, 700, 4096, F16, 6, False),   # few tiles: K split (tiles of 256 and of 224 columns)
+    (96, 300, 512, F16, 4, True),      # columns 0 .. 3: the codes are CB's first columns
+]
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["int8", "fp8"])
+@pytest.mark.parametrize("M,N,K,dt,nout,prefix", FEW, ids=[f"{r[0]}x{r[1]}x{r[2]}-{r[4]}" for r in FEW])
+def test_few_outlier_codes_gathered_match_direct(orc, M, N, K, dt, nout, prefix, fp8, tile_cols):
+    """With at most 16 outlier columns the tiled product stages their weight
+    codes from the table gathered once per call (by the activation kernel or
+    by the product's own gather kernel) or, without a workspace, straight
+    from CB per tile: the same bits either way, also after a call with more
+    columns (a wider table) left the workspace stale, and against the oracle."""
+    import torch
+    import int8_quantized_matmul_row_amd as pkg
+    from gpu_helpers import to_torch
+    wl = synth.make_random(M, N, K, dt, seed=7 * M + N, n_outlier_cols=0 if prefix else nout, bias_sigma=0.01)
+    if prefix:
+        xb = synth.bits_to_f32(wl.X, dt)
+        xb[:, :nout] = 20.0
+        wl.X = synth.to_bits(xb, dt)
+    dev = torch.device("cuda:0")
+    X, W = to_torch(wl.X, dt, dev), to_torch(wl.W, dt, dev)
+    bias = to_torch(wl.bias, dt, dev)
+    qa, qw, mm, lin, lin_size = ((pkg.quantize_act_fp8, pkg.quantize_weight_fp8, pkg.matmul_fp8, pkg.linear_fp8,
+                                  pkg.llmint8_linear_fp8_workspace_size) if fp8 else
+                                 (pkg.quantize_act, pkg.quantize_weight, pkg.matmul, pkg.linear,
+                                  pkg.llmint8_linear_workspace_size))
+    CB, SCB = qw(W)
+    q = qa(X, wl.threshold)
+    n_out = int(q.n_out.item())
+    log(f"[parity] few outlier codes {M}x{N}x{K} fp8={fp8} n_out={n_out} prefix={prefix} tile columns {tile_cols}")
+    assert 1 <= n_out <= 16
+    assert (pkg.outlier_columns(q).tolist() == list(range(n_out))) == prefix
+    ref = mm(q, CB, SCB, bias=bias, workspace=(None, 0)).view(torch.int16).cpu()
+    mm_bytes = pkg.llmint8_matmul_workspace_size(M, N, K)
+    # a stale workspace: first a call with more than 16 columns (the wider layout)
+    X_many = X.clone()
+    X_many[:, 40:80] = 30.0
+    q_many = qa(X_many, wl.threshold)
+    assert int(q_many.n_out.item()) > 16
+    ws = torch.full((mm_bytes,), 0x5A, dtype=torch.uint8, device=dev)
+    mm(q_many, CB, SCB, bias=bias, workspace=(ws, mm_bytes))
+    got = mm(q, CB, SCB, bias=bias, workspace=(ws, mm_bytes)).view(torch.int16).cpu()
+    assert torch.equal(got, ref), "product's gather"
+    base = lin_size(M, N, K)
+    ws = torch.full((base,), 0x5A, dtype=torch.uint8, device=dev)
+    lin(X_many, CB, SCB, bias=bias, threshold=wl.threshold, workspace=(ws, base))
+    Y, q2 = lin(X, CB, SCB, bias=bias, threshold=wl.threshold, workspace=(ws, base))
+    assert int(q2.n_out.item()) == n_out
+    assert torch.equal(Y.view(torch.int16).cpu(), ref), "activation kernel's gather"
+    # and the product against the oracle (the 1e-2 gate; the integer stages
+    # are checked bit for bit by the other parity tests)
+    r = (orc.forward_fp8 if fp8 else orc.forward)(wl.X, wl.W, dt, wl.threshold, bias=wl.bias)
+    y = Y.float().cpu().numpy().astype(np.float64)
+    assert np.abs(y - r["Y"]).max() <= 1e-2 * np.abs(r["Y"]).max()
+
+
 # ---- K split over several workgroups per tile (few tiles, long K) -----------
 SPLIT = [
     # M, N, K, dtype, planted outlier columns (tiles of 256 / 224 columns)
