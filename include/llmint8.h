@@ -153,14 +153,16 @@ size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
  *          - the split-K region (sizes at llmint8_matmul_workspace_size),
  *            when the shape splits and the workspace holds it: the product
  *            then spreads K over several workgroups per tile;
- *          - the rest, R bytes, for the weight codes at the outlier columns
- *            when there are more than 16 of them, gathered once per call (by
- *            the activation kernel in llmint8_linear, else by a small kernel
- *            ahead of the GEMM) into N rows of C bytes, C a multiple of 64:
- *            C = 64 * floor(R / (64 N)), at most K (1024 at the default
- *            size, every column with N * K bytes).  The outlier part of the
- *            product then runs as a second pipelined K loop over those
- *            columns.  With more outlier columns than C (n_outliers is read
+ *          - the rest, R bytes, for the weight codes at the outlier columns,
+ *            gathered once per call (by the activation kernel in
+ *            llmint8_linear, else by a small kernel ahead of the GEMM) into N
+ *            rows of C bytes, C a multiple of 64: C = 64 * floor(R / (64 N)),
+ *            at most K (1024 at the default size, every column with N * K
+ *            bytes); at most 16 columns go in rows of 16 bytes instead.  The
+ *            product's tiles read their rows' codes there rather than from CB
+ *            (a 128-byte line per row and column, for every tile row), and
+ *            with more than 16 columns the outlier part runs as a second
+ *            pipelined K loop over them.  With more outlier columns than C (n_outliers is read
  *            on the device) the product gathers each tile's codes itself,
  *            several times slower, unless the outlier columns are exactly
  *            0 .. n_outliers-1 (every column at threshold 0), whose codes it

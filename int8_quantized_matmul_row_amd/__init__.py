@@ -421,8 +421,9 @@ def outlier_columns(q: QuantizedAct):
 
 
 def matmul_workspace(M, N, K, device, stream=None):
-    """(buffer, bytes) of the optional product workspace (the weight codes at
-    the outlier columns, gathered once per call when there are more than 16)."""
+    """(buffer, bytes) of the optional product workspace (split-K partial
+    tiles for shapes with few tiles, and the weight codes at the outlier
+    columns, gathered once per call)."""
     torch = _torch()
     n = llmint8_matmul_workspace_size(M, N, K)
     return _empty((max(n, 1),), torch.uint8, device, stream), n
