@@ -94,6 +94,7 @@ constexpr int kCUs = 256;             // compute units of the device (gfx950)
 constexpr int kMaxSplit = 8;          // workgroups per tile when K is split
 constexpr int kMinSplitStages = 8;    // K stages (128 bytes) per split, at least
 constexpr int kBarrierAt = 2;         // MFMA block of a stage's second unit at its barrier
+constexpr int kNoGatherRows = 128;    // token rows up to which the first outlier codes are not gathered
 
 // The tile's columns TN and the waves' grid: 256 columns as 2 x 2 waves of
 // 4 x 4 blocks (32 x 32), or 224 columns as 4 x 1 waves of 2 x 7 blocks (224
@@ -841,7 +842,7 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
                                            const float* __restrict__ SCB, const uint16_t* __restrict__ bias,
                                            uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32,
                                            float* __restrict__ C_f32, const int8_t* __restrict__ wo_all,
-                                           int wo_cap, int split, uint32_t* __restrict__ counters,
+                                           int wo_cap, int wo_min, int split, uint32_t* __restrict__ counters,
                                            int32_t* __restrict__ part) {
     typedef typename TileAcc<FP8>::type acc_t;
     typedef Tile<TN> T;
@@ -903,10 +904,11 @@ __device__ __forceinline__ void plain_body(int8_t* smem, float* s_sa, float* s_s
         }
         if (!e_valid) e_col = 0;
         // gathered for this call: the same condition as the gather's (more
-        // than TiledLayout::min_cols columns, which is 0 for every tile
-        // without kExtract; at most the workspace's columns; and not simply
-        // 0 .. n_out-1, whose codes are CB's own first columns)
-        const bool gathered = wo_all != nullptr && n_out > 0 && n_out <= wo_cap && idx[max(n_out, 1) - 1] != n_out - 1;
+        // than wo_min columns, TiledLayout::min_cols; at most the workspace's
+        // columns; and not simply 0 .. n_out-1, whose codes are CB's own
+        // first columns)
+        const bool gathered = wo_all != nullptr && n_out > wo_min && n_out > 0 && n_out <= wo_cap &&
+                              idx[max(n_out, 1) - 1] != n_out - 1;
         const int8_t* w_src = gathered ? wo_all : CB;
         const size_t w_stride = gathered ? (size_t)(n_out <= kOutLds ? kOutLds : wo_cap) : (size_t)K;
         const int w_col = gathered ? (e_valid ? e_out : 0) : e_col;
@@ -1285,7 +1287,7 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
                        const float* __restrict__ SCB, const uint16_t* __restrict__ bias,
                        uint16_t* __restrict__ Y, int32_t* __restrict__ C_i32,
                        float* __restrict__ C_f32, const int8_t* __restrict__ wo_all,
-                       int wo_cap, int split, uint32_t* __restrict__ counters,
+                       int wo_cap, int wo_min, int split, uint32_t* __restrict__ counters,
                        int32_t* __restrict__ part) {
     __shared__ __attribute__((aligned(16))) int8_t smem[Tile<TN>::kSmemBytes];
     __shared__ float s_sa[BM], s_sb[kThreads], s_bias[kThreads];  // (entries past TN unused)
@@ -1301,8 +1303,8 @@ void gemm_tiled_kernel(int M, int N, int K, int tiles_m, int tiles_n,
         return;
     }
     plain_body<BF16, FP8, SPLIT, TN>(smem, s_sa, s_sb, s_bias, s_wo, s_xo, s_xcol, &s_last, M, N, K, tiles_m, tiles_n, CA, SCA,
-                                 idx, n_out_ptr, XO, CB, SCB, bias, Y, C_i32, C_f32, wo_all, wo_cap, split,
-                                 counters, part);
+                                 idx, n_out_ptr, XO, CB, SCB, bias, Y, C_i32, C_f32, wo_all, wo_cap, wo_min,
+                                 split, counters, part);
 }
 
 // Bytes of gathered outlier codes for an N x K weight holding `cap` outlier
@@ -1388,9 +1390,10 @@ TiledLayout tiled_layout(int M, int N, int K, void* ws, size_t ws_bytes) {
         if (L.cap > 0) L.codes = reinterpret_cast<int8_t*>(p);
     }
     // the 224-column tile whose K is not split takes its first kOutLds codes
-    // from the B stages (plain_body, kExtract); every other tile reads them
-    // from the gather
-    L.min_cols = tile_cols(M, N, K) == 224 && L.split == 1 ? kOutLds : 0;
+    // from the B stages (plain_body, kExtract), and at most 128 token rows
+    // (one row of tiles, each reading its rows' codes from CB once) skip the
+    // gather pass; every other tile reads them from the gather
+    L.min_cols = (tile_cols(M, N, K) == 224 && L.split == 1) || M <= kNoGatherRows ? kOutLds : 0;
     return L;
 }
 
@@ -1414,7 +1417,7 @@ hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t
     }
     typedef void (*kernel_t)(int, int, int, int, int, const int8_t*, const float*, const int32_t*,
                              const int32_t*, const uint16_t*, const int8_t*, const float*,
-                             const uint16_t*, uint16_t*, int32_t*, float*, const int8_t*, int, int,
+                             const uint16_t*, uint16_t*, int32_t*, float*, const int8_t*, int, int, int,
                              uint32_t*, int32_t*);
     // [columns 224?][split?][bf16?][fp8?]
     static const kernel_t kernels[2][2][2][2] = {
@@ -1432,7 +1435,7 @@ hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t
     dim3 block(kThreads), grid(items);
 #define LLMINT8_GEMM_ARGS                                                                                     \
     a.M, a.N, a.K, tiles_m, tiles_n, a.CA, a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32, \
-        a.C_f32, L.codes, L.cap, L.split, L.counters, L.part
+        a.C_f32, L.codes, L.cap, L.min_cols, L.split, L.counters, L.part
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(plain, grid, block, 0, stream, ev_start, ev_stop, 0, LLMINT8_GEMM_ARGS);
     } else {

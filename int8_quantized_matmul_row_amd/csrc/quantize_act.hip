@@ -454,6 +454,10 @@ __global__ __launch_bounds__(kThreads) void act_quant_rows(
 
 __global__ void write_zero_count(int32_t* n_out) { *n_out = 0; }
 
+// workgroups of the row kernel below which it leaves the weight codes'
+// gather to the product
+constexpr int kActGatherMinBlocks = 64;
+
 struct ActPlan {
     bool small;
     int slabs;            // K/64: 64-column slabs of kernel A
@@ -530,6 +534,10 @@ hipError_t launch_quantize_act(const void* Xv, bool bf16, bool fp8, int M, int K
     // 33.6 and 512 took 34.9)
     int blocks = (M + rows_wg - 1) / rows_wg;
     if (blocks > 1024) blocks = 1024;
+    // the weight codes' gather (N rows of work) only with enough workgroups:
+    // a grid sized for a few token rows would take it in many dependent
+    // passes, and the product's own gather kernel does it instead
+    if (blocks < kActGatherMinBlocks) g.out = nullptr;
     void (*fn)(const uint16_t*, int, int, const uint32_t*, int, int8_t*, float*, int32_t*, int32_t*,
                uint16_t*, int, CodeGather) =
         bf16 ? (fp8 ? act_quant_rows<true, true> : act_quant_rows<true, false>)
