@@ -57,17 +57,23 @@ KERNEL_NAMES = {"decode": "linear_decode_kernel", "fused": "linear_small_m_kerne
                 "tiled": "gemm_tiled_kernel"}
 
 
-def kernel_family(M, K, variant="int8"):
+def small_m_product(M, N, K):
+    """Whether the product takes the weight-streaming kernel: up to 16 token
+    rows always, up to 64 when M * N * K is at most 6e9 (the library's rule)."""
+    return M <= 16 or (M <= 64 and N is not None and M * N * K <= 6_000_000_000)
+
+
+def kernel_family(M, K, variant="int8", N=None):
     """The kernel that carries the product in llmint8_linear (or
     llmint8_linear_fp8, which has the fused decode kernel but not the other
     fused small-M one) for this shape."""
     if 1 <= M <= 8 and M * K <= 32768 and K <= 8192:
         return "decode"
     if variant == "fp8":
-        return "small_m" if M <= 16 else "tiled"
+        return "small_m" if small_m_product(M, N, K) else "tiled"
     if 1 <= M <= 16 and M * K <= 65536 and K <= 8192:
         return "fused"
-    return "small_m" if M <= 16 else "tiled"
+    return "small_m" if small_m_product(M, N, K) else "tiled"
 
 
 def source_hash(files):
@@ -388,7 +394,7 @@ def main():
     # the GEMM, and a start event bound to the GEMM would also take in the gap
     # after the kernel before it; the GEMM then runs back to back on the
     # activations of the last step (the same kernel on the same inputs).
-    fam = kernel_family(M, K, args.variant)
+    fam = kernel_family(M, K, args.variant, N)
     n_kt = min(steps, 512)
     evs = [(hip.event(), hip.event()) for _ in range(n_kt)]
     mm_prof = pkg.llmint8_matmul_fp8_profiled if fp8 else pkg.llmint8_matmul_profiled

@@ -119,7 +119,8 @@ llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of optional device workspace llmint8_matmul can use for M x N x K
- * (0 for M <= 16 and for invalid sizes).  For M > 16 the product works on
+ * (0 for the weight-streaming product and for invalid sizes: M <= 16, or
+ * M <= 64 with M * N * K <= 6e9).  Otherwise the product works on
  * tiles of 256 rows by W columns, W = 256 or 224: for each W, T(W) =
  * ceil(M/256) * ceil(N/W) tiles, S(W) workgroups per tile (below), and the
  * W with the fewer MFMA cycles per CU, ceil(T*S/256) * W * ceil(ceil(K/128)/S),
@@ -149,7 +150,7 @@ size_t llmint8_matmul_workspace_size(int64_t M, int64_t N, int64_t K);
  *   C_i32  [M,N] int32 out or NULL: when given, the same kernels also store the
  *          exact int8 accumulators (for parity checks).
  *   workspace  optional scratch, 16-byte aligned; NULL / 0 bytes is always
- *          valid.  For M > 16 it is used in this order:
+ *          valid.  Past the weight-streaming shapes it is used in this order:
  *          - the split-K region (sizes at llmint8_matmul_workspace_size),
  *            when the shape splits and the workspace holds it: the product
  *            then spreads K over several workgroups per tile;

@@ -196,7 +196,7 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
     // codes at the outlier columns when the workspace holds no more columns
     // than it can list (it knows the columns first); no extra launch.
     llmint8::CodeGather gather;
-    if (M > llmint8::kSmallM && N > 0 && mm_ws) {
+    if (!llmint8::small_m_product(M, N, K) && N > 0 && mm_ws) {
         const llmint8::TiledLayout L = llmint8::tiled_layout((int)M, (int)N, (int)K, mm_ws, mm_bytes);
         if (L.codes != nullptr && L.cap <= llmint8::kActGatherCols) {
             gather.CB = CB;
@@ -239,12 +239,12 @@ llmint8_status linear_impl(const void* X, int dtype, bool fp8, int64_t M, int64_
 namespace llmint8 {
 
 size_t matmul_workspace(int64_t M, int64_t N, int64_t K) {
-    return M <= kSmallM ? 0 : gemm_tiled_workspace(M, N, K);
+    return small_m_product(M, N, K) ? 0 : gemm_tiled_workspace(M, N, K);
 }
 
 hipError_t launch_matmul(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                          hipEvent_t ev_stop) {
-    if (a.M <= kSmallM) return launch_gemm_small_m(a, stream, ev_start, ev_stop);
+    if (small_m_product(a.M, a.N, a.K)) return launch_gemm_small_m(a, stream, ev_start, ev_stop);
     return launch_gemm_tiled(a, stream, ev_start, ev_stop);
 }
 

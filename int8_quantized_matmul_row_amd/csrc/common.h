@@ -552,6 +552,17 @@ hipError_t launch_linear_decode(const void* X, bool bf16, bool fp8, int M, int N
 
 // Kernel families used by launch_matmul.
 constexpr int kSmallM = 16;  // M <= kSmallM takes the streaming kernel
+// up to 64 rows the streaming kernel (1, 2 or 4 groups of 16 rows) also takes
+// shapes whose M * N * K is at most this: its weight stream, with every
+// workgroup re-reading the M x K activations, is then cheaper than one row of
+// 256-row tiles (measured: 17 x 28672 x 8192 80 against 96 us, 64 x 16384 x
+// 4096 65 against 82 us, 32 x 4096 x 4096 21 against 65 us; above it,
+// 32 x 28672 x 8192 106 against 96 us)
+constexpr int64_t kSmallMMaxRows = 64;
+constexpr int64_t kSmallMWork = 6000000000LL;
+inline bool small_m_product(int64_t M, int64_t N, int64_t K) {
+    return M <= kSmallM || (M <= kSmallMMaxRows && M * N * K <= kSmallMWork);
+}
 hipError_t launch_gemm_small_m(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                                hipEvent_t ev_stop);
 hipError_t launch_gemm_tiled(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,

@@ -15,6 +15,11 @@ def test_kernel_family():
     assert bench.kernel_family(16, 4096) == "fused"
     assert bench.kernel_family(16, 8192) == "small_m"
     assert bench.kernel_family(2048, 4096) == "tiled"
+    # up to 64 rows, the weight-streaming kernel while M * N * K <= 6e9
+    assert bench.kernel_family(17, 8192, N=28672) == "small_m"
+    assert bench.kernel_family(32, 8192, N=28672) == "tiled"
+    assert bench.kernel_family(64, 4096, N=16384) == "small_m"
+    assert bench.kernel_family(65, 4096, N=1024) == "tiled"
     # the FP8 forward has the fused decode kernel, not the other fused one
     assert bench.kernel_family(8, 4096, "fp8") == "decode"
     assert bench.kernel_family(16, 4096, "fp8") == "small_m"

@@ -81,7 +81,7 @@ def test_tile_width_override(monkeypatch):
         512 + 2 * 112 * (256 * 256 * 4) + 14336 * 1024
     monkeypatch.setenv("LLMINT8_TILE_COLS", "224")
     assert pkg.llmint8_matmul_workspace_size(2048, 16384, 4096) == 16 << 20  # no split either way
-    assert pkg.llmint8_matmul_workspace_size(17, 4096, 4096) == \
+    assert pkg.llmint8_matmul_workspace_size(65, 4096, 4096) == \
         256 + 4 * 19 * (256 * 224 * 4) + 4096 * 1024
     monkeypatch.setenv("LLMINT8_TILE_COLS", "other")  # ignored
     assert pkg.llmint8_matmul_workspace_size(512, 14336, 57344) == \
@@ -101,15 +101,16 @@ def test_workspace_sizes():
     P224, P256 = 256 * 224 * 4, 256 * 256 * 4
     assert pkg.llmint8_matmul_workspace_size(8, 4096, 4096) == 0
     assert pkg.llmint8_matmul_workspace_size(16, 4096, 4096) == 0
+    assert pkg.llmint8_matmul_workspace_size(64, 4096, 4096) == 0   # up to 64 rows: the streaming kernel
     # W = 224: 19 tiles, K = 32 stages split in 4
-    assert pkg.llmint8_matmul_workspace_size(17, 4096, 4096) == \
+    assert pkg.llmint8_matmul_workspace_size(65, 4096, 4096) == \
         256 + 4 * 19 * P224 + 4096 * 1024
     # W = 256: 512 tiles (2 rounds; 592 tiles of 224 take 3): no split
     assert pkg.llmint8_matmul_workspace_size(2048, 16384, 4096) == 16 << 20
     # 2 tiles, but K is 1 stage: no split
     assert pkg.llmint8_matmul_workspace_size(300, 33, 128) == 33 * 128
     # 1 tile, split in 8 (the most)
-    assert pkg.llmint8_matmul_workspace_size(40, 64, 57344) == \
+    assert pkg.llmint8_matmul_workspace_size(80, 64, 57344) == \
         256 + 8 * P224 + 64 * 1024
     # the BLOOM-shaped down projection: 128 tiles of 224 columns (112 of 256
     # would leave 32 CUs idle), split in 2

@@ -136,8 +136,9 @@ RAGGED = [
     (3, 17, 128, BF16, 1, True),
     (8, 200, 4160, F16, 4, True),
     (16, 33, 192, F16, 2, True),
-    (17, 40, 64, F16, 1, False),       # tiled, one stage
-    (64, 64, 128, BF16, 2, True),      # tiled, two stages
+    (65, 40, 64, F16, 1, False),       # tiled, one stage
+    (80, 64, 128, BF16, 2, True),      # tiled, two stages
+    (40, 64, 128, BF16, 2, True),      # the streaming kernel, four groups of 16 rows
     (65, 300, 192, F16, 2, True),      # tiled, three stages
     (300, 520, 320, F16, 3, True),
     (300, 520, 320, BF16, 3, True),

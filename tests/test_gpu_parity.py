@@ -61,11 +61,17 @@ RAGGED = [
     (8, 4100, 256, F16, 2, True),
     (16, 33, 192, F16, 2, True),
     (17, 40, 64, F16, 1, False),
+    (65, 40, 64, F16, 1, False),
+    # the streaming kernel's two and four groups of 16 token rows, with more
+    # than 32 outlier columns (their product as 16-bit MFMAs) and without
+    (30, 130, 512, F16, 36, False),
+    (48, 200, 1024, BF16, 40, True),
+    (64, 96, 2048, F16, 3, True),
     (300, 520, 320, F16, 3, True),
     (300, 520, 320, BF16, 3, True),
     (513, 257, 1024, F16, 5, False),
     (257, 769, 448, BF16, 40, True),
-    (40, 64, 57344, BF16, 2, False),
+    (80, 64, 57344, BF16, 2, False),
     (8, 96, 133120, F16, 1, False),
     # few long rows: the activation kernel shares each row among 2 or 4 waves
     (37, 100, 8192, BF16, 3, True),     # 2 waves per row, odd M (a half-empty row group)
@@ -79,8 +85,8 @@ RAGGED = [
 @pytest.mark.parametrize("M,N,K,dt,nout,bias", RAGGED,
                          ids=[f"{r[0]}x{r[1]}x{r[2]}-{synth.DTYPE_NAMES[r[3]]}" for r in RAGGED])
 def test_ragged_shapes(orc, M, N, K, dt, nout, bias, tile_cols):
-    if M <= 16 and tile_cols == 224:
-        pytest.skip("M <= 16: the small-M kernels, no tiles")
+    if M <= 64 and tile_cols == 224:
+        pytest.skip("M <= 64: the small-M kernels, no tiles")
     wl = synth.make_random(M, N, K, dt, seed=M + N + K, n_outlier_cols=nout,
                            bias_sigma=0.01 if bias else None)
     full_check(orc, wl)
@@ -107,7 +113,7 @@ def test_threshold_inf_no_outliers(orc, M, N, K, tile_cols):
 MANY = [
     # M, N, K, dtype, planted outlier columns, threshold (None: the default)
     (257, 769, 448, BF16, 40, None),
-    (64, 33, 576, F16, 150, None),
+    (72, 33, 576, F16, 150, None),
     (300, 100, 1024, F16, 0, 0.0),   # every column: 1024 > the default capacity
 ]
 
@@ -183,7 +189,7 @@ def test_gathered_outlier_codes_match_direct_gathers(M, N, K, dt, nout, t, fp8, 
 FEW = [
     # M, N, K, dtype, planted outlier columns, first columns (0 .. n-1) instead
     (257, 769, 448, BF16, 5, False),
-    (64, 33, 576, F16, 16, False),
+    (72, 33, 576, F16, 16, False),
     (300, 700, 4096, F16, 6, False),   # few tiles: K split (tiles of 256 and of 224 columns)
     (96, 300, 512, F16, 4, True),      # columns 0 .. 3: the codes are CB's first columns
 ]
@@ -246,7 +252,7 @@ def test_few_outlier_codes_gathered_match_direct(orc, M, N, K, dt, nout, prefix,
 SPLIT = [
     # M, N, K, dtype, planted outlier columns (tiles of 256 / 224 columns)
     (300, 700, 4096, F16, 40),    # 6 / 8 tiles, K split in 4; codes gathered too
-    (40, 64, 57344, BF16, 3),     # 1 tile, split in 8
+    (80, 64, 57344, BF16, 3),     # 1 tile, split in 8
     (520, 300, 2048, BF16, 0),    # 6 tiles, split in 2; three tile rows
     (300, 700, 4160, F16, 20),    # split in 4; the last split ends in a half (64-byte) K stage
 ]
@@ -310,7 +316,7 @@ EDGE = [
     # M, N, K, dtype, outlier columns
     (300, 448, 4160, F16, [0, 127, 128, 4095, 4096, 4159]),    # two in the last, half (64-byte) stage
     (300, 452, 4160, BF16, list(range(40, 56))),                # 16 adjacent columns in one stage; ragged N
-    (40, 230, 192, F16, [63, 64, 65, 127, 128, 191] + [10 * i + 1 for i in range(11)]),  # 17: one past the 16
+    (80, 230, 192, F16, [63, 64, 65, 127, 128, 191] + [10 * i + 1 for i in range(11)]),  # 17: one past the 16
 ]
 
 
@@ -448,13 +454,14 @@ LINEAR = [
     (12, 260, 2048, F16, 12, True, 0.0),      # every column an outlier
     (7, 96, 512, F16, 2, True, float("inf")),
     (16, 64, 8192, F16, 2, False, 6.0),       # M*K beyond the fused bound
-    (33, 300, 640, BF16, 3, True, 6.0),       # tiled path through llmint8_linear
+    (65, 300, 640, BF16, 3, True, 6.0),       # tiled path through llmint8_linear
+    (33, 300, 640, BF16, 3, True, 6.0),       # the streaming kernel through llmint8_linear
     (8, 200, 4160, F16, 3, True, 6.0),        # last K slice one step deep
     (3, 64, 192, BF16, 1, False, 6.0),        # one slice, a wave with no step
     (16, 77, 2112, BF16, 2, True, 2.5),       # ~90 outlier columns per slice
     (8, 4096, 1024, F16, 1, True, 6.0),       # four slices of 256 columns
     (257, 769, 448, BF16, 40, True, 6.0),     # tiled; the activation kernel gathers codes
-    (64, 33, 576, F16, 150, True, 6.0),
+    (72, 33, 576, F16, 150, True, 6.0),
     (300, 100, 1024, F16, 2, True, 0.0),      # more outlier columns than the workspace holds
     # the fused decode kernel with more than 8 outlier columns: the 16-bit
     # product as MFMAs over all of K against X masked to the outlier columns
