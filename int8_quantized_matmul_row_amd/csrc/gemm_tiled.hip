@@ -19,7 +19,7 @@
 //    2-deep ring of LDS buffers (A 256 x 128 + B 256 x 128 bytes, 64 KiB
 //    each).  Stages are filled by buffer_load_dwordx4 ... lds: each wave
 //    instruction moves 8 rows x 128 bytes straight from memory into LDS, no
-//    registers involved.  One barrier per stage, two MFMA blocks into the
+//    registers involved.  One barrier per stage, one MFMA block into the
 //    stage's second 64-byte unit; after it the next stage's first unit is read
 //    and the stage after that is loaded into the buffer just finished, so
 //    every load has a whole stage to land.
@@ -93,7 +93,7 @@ constexpr int kGatherThreads = 256;
 constexpr int kCUs = 256;             // compute units of the device (gfx950)
 constexpr int kMaxSplit = 8;          // workgroups per tile when K is split
 constexpr int kMinSplitStages = 8;    // K stages (128 bytes) per split, at least
-constexpr int kBarrierAt = 2;         // MFMA block of a stage's second unit at its barrier
+constexpr int kBarrierAt = 1;         // MFMA block of a stage's second unit at its barrier
 constexpr int kNoGatherRows = 128;    // token rows up to which the first outlier codes are not gathered
 
 // The tile's columns TN and the waves' grid: 256 columns as 2 x 2 waves of
