@@ -47,3 +47,13 @@ def test_profile_digests_name_their_kernel_sources():
                 t = json.load(f)
             assert t["kernel"] in bench.KERNEL_NAMES.values(), name
             assert t["hbm_bytes_per_launch"] > 0 and t["algorithmic_bytes_per_launch"] > 0
+
+
+def test_small_m_rule_matches_library():
+    """bench.py's kernel family follows the library's choice of the streaming
+    product: its workspace size is 0 exactly for those shapes (M > 16)."""
+    import int8_quantized_matmul_row_amd as pkg
+    for M in (17, 32, 48, 64, 65, 100):
+        for N, K in ((4096, 4096), (16384, 4096), (28672, 8192), (57344, 14336), (700, 2048)):
+            streaming = pkg.llmint8_matmul_workspace_size(M, N, K) == 0
+            assert streaming == bench.small_m_product(M, N, K), (M, N, K)
