@@ -552,16 +552,31 @@ hipError_t launch_linear_decode(const void* X, bool bf16, bool fp8, int M, int N
 
 // Kernel families used by launch_matmul.
 constexpr int kSmallM = 16;  // M <= kSmallM takes the streaming kernel
-// up to 64 rows the streaming kernel (1, 2 or 4 groups of 16 rows) also takes
-// shapes whose M * N * K is at most this: its weight stream, with every
-// workgroup re-reading the M x K activations, is then cheaper than one row of
-// 256-row tiles (measured: 17 x 28672 x 8192 80 against 96 us, 64 x 16384 x
-// 4096 65 against 82 us, 32 x 4096 x 4096 21 against 65 us; above it,
-// 32 x 28672 x 8192 106 against 96 us)
+// More than 16 rows with at least 256 x 64 output channels: workgroups of 64
+// channels (four groups of 16), each reading the M x K activations once for
+// 64 weight rows instead of 16.
+inline bool small_m_wide(int64_t M, int64_t N) { return M > kSmallM && N >= 64 * 256; }
+// Whether the streaming kernel's grid is one round of the chip: at most 256
+// workgroups of 64 channels (one per CU), or, up to 32 rows, 512 of 16 (two
+// per CU; with four groups of 16 rows these lost to the tiled product,
+// 64 x 8192 x 28672 150 against 140 us).
+inline bool small_m_one_round(int64_t M, int64_t N) {
+    return small_m_wide(M, N) ? (N + 63) / 64 <= 256 : M <= 32 && (N + 15) / 16 <= 512;
+}
+// Up to 64 rows the streaming kernel (1, 2 or 4 groups of 16 rows) also takes
+// shapes whose M * N * K is at most kSmallMWork, and any whose grid is one
+// round: each workgroup's time grows with K and every further round adds one,
+// while the tiled product runs one row of 256-row tiles over the whole weight
+// (measured, against the tiled product: 17 x 28672 x 8192 68 against 76 us,
+// 64 x 16384 x 4096 49 against 66, 64 x 16384 x 16384 100 against 126,
+// 32 x 16384 x 8192 46 against 63, 32 x 8192 x 28672 95 against 136; above
+// both, 64 x 20480 x 8192 113 against 90 and 32 x 57344 x 8192 183 against
+// 121)
 constexpr int64_t kSmallMMaxRows = 64;
 constexpr int64_t kSmallMWork = 6000000000LL;
 inline bool small_m_product(int64_t M, int64_t N, int64_t K) {
-    return M <= kSmallM || (M <= kSmallMMaxRows && M * N * K <= kSmallMWork);
+    return M <= kSmallM ||
+           (M <= kSmallMMaxRows && (M * N * K <= kSmallMWork || small_m_one_round(M, N)));
 }
 hipError_t launch_gemm_small_m(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                                hipEvent_t ev_stop);

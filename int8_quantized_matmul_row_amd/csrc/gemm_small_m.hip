@@ -37,45 +37,51 @@ namespace {
 constexpr int kBatch = 8;       // K steps in flight per wave for one group of 16 token rows
 constexpr int kDenseOut = 32;  // more outlier columns than this: the outlier product as MFMAs
 
-// steps s0 + i*WAVES (i < kBatch / MT) of the weight rows and of every group's
-// activation rows (steps past K, rows past M or N load zeros)
-template <int WAVES, int MT>
-__device__ __forceinline__ void load_steps(const int8_t* const (&pa)[MT], const int8_t* __restrict__ pb,
-                                           const bool (&a_ok)[MT], bool b_ok, int s0, int nsteps,
-                                           v4i (&a)[MT][kBatch / MT], v4i (&b)[kBatch / MT]) {
+// steps s0 + i*WAVES (i < KB) of the weight rows of every channel group and
+// of the activation rows of every token group (steps past K, rows past M or
+// N load zeros)
+template <int WAVES, int MT, int NC, int KB>
+__device__ __forceinline__ void load_steps(const int8_t* const (&pa)[MT], const int8_t* const (&pb)[NC],
+                                           const bool (&a_ok)[MT], const bool (&b_ok)[NC], int s0, int nsteps,
+                                           v4i (&a)[MT][KB], v4i (&b)[NC][KB]) {
 #pragma unroll
-    for (int i = 0; i < kBatch / MT; ++i) {
+    for (int i = 0; i < KB; ++i) {
         const int s = s0 + i * WAVES;
         const bool in = s < nsteps;
-        b[i] = (in && b_ok) ? *reinterpret_cast<const v4i*>(pb + (size_t)s * 64) : v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            b[c][i] = (in && b_ok[c]) ? *reinterpret_cast<const v4i*>(pb[c] + (size_t)s * 64) : v4i{0, 0, 0, 0};
 #pragma unroll
         for (int t = 0; t < MT; ++t)
             a[t][i] = (in && a_ok[t]) ? *reinterpret_cast<const v4i*>(pa[t] + (size_t)s * 64) : v4i{0, 0, 0, 0};
     }
 }
 
-template <int MT>
-__device__ __forceinline__ void mfma_steps(const v4i (&a)[MT][kBatch / MT], const v4i (&b)[kBatch / MT],
-                                           v4i (&acc)[MT]) {
+template <int MT, int NC, int KB>
+__device__ __forceinline__ void mfma_steps(const v4i (&a)[MT][KB], const v4i (&b)[NC][KB], v4i (&acc)[NC][MT]) {
 #pragma unroll
-    for (int i = 0; i < kBatch / MT; ++i)
+    for (int i = 0; i < KB; ++i)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][i], b[i], acc[t], 0, 0, 0);
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                acc[c][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][i], b[c][i], acc[c][t], 0, 0, 0);
 }
 
-template <int MT>
-__device__ __forceinline__ void mfma_steps(const v4i (&a)[MT][kBatch / MT], const v4i (&b)[kBatch / MT],
-                                           v4f (&acc)[MT]) {
+template <int MT, int NC, int KB>
+__device__ __forceinline__ void mfma_steps(const v4i (&a)[MT][KB], const v4i (&b)[NC][KB], v4f (&acc)[NC][MT]) {
 #pragma unroll
-    for (int i = 0; i < kBatch / MT; ++i) {
-        const v2l b2 = __builtin_bit_cast(v2l, b[i]);
+    for (int i = 0; i < KB; ++i)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const v2l a2 = __builtin_bit_cast(v2l, a[t][i]);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc[t], 0, 0, 0);
+        for (int c = 0; c < NC; ++c) {
+            const v2l b2 = __builtin_bit_cast(v2l, b[c][i]);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const v2l a2 = __builtin_bit_cast(v2l, a[t][i]);
+                acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[0], b2[0], acc[c][t], 0, 0, 0);
+                acc[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a2[1], b2[1], acc[c][t], 0, 0, 0);
+            }
         }
-    }
 }
 
 template <bool FP8>
@@ -89,7 +95,7 @@ struct SmallAcc<true> {
     typedef float elem;
 };
 
-template <bool BF16, bool FP8, int WAVES, int MT>
+template <bool BF16, bool FP8, int WAVES, int MT, int NC>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     int M, int N, int K, const int8_t* __restrict__ CA, const float* __restrict__ SCA,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
@@ -98,119 +104,141 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     float* __restrict__ C_f32) {
     typedef typename SmallAcc<FP8>::vec acc_t;
     typedef typename SmallAcc<FP8>::elem elem_t;
-    constexpr int kB = kBatch / MT;
+    // K steps in flight per wave: fewer for more token groups, and two with
+    // four channel groups, so that the registers in flight stay about the same
+    constexpr int kB = NC == 1 ? kBatch / MT : 2;
     __shared__ elem_t red[WAVES][MT][4][64];
     __shared__ float red_o[WAVES][MT][4][64];  // the 16-bit outlier product's partial tiles (many columns)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = blockIdx.x * 16 * NC;
     const int r16 = lane & 15, kg = lane >> 4;
     const int nsteps = K >> 6;
-    bool a_ok[MT];
+    bool a_ok[MT], b_ok[NC];
     const int8_t* pa[MT];
+    const int8_t* pb[NC];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         const int r = 16 * t + r16;
         a_ok[t] = r < M;
         pa[t] = CA + (size_t)(a_ok[t] ? r : 0) * K + kg * 16;
     }
-    const bool b_ok = n0 + r16 < N;
-    const int8_t* pb = CB + (size_t)(b_ok ? n0 + r16 : 0) * K + kg * 16;
-
-    acc_t acc[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = acc_t{0, 0, 0, 0};
-    v4i a0[MT][kB], b0[kB], a1[MT][kB], b1[kB];
-    load_steps<WAVES, MT>(pa, pb, a_ok, b_ok, wave, nsteps, a0, b0);
-    for (int s = wave; s < nsteps; s += 2 * kB * WAVES) {
-        load_steps<WAVES, MT>(pa, pb, a_ok, b_ok, s + kB * WAVES, nsteps, a1, b1);
-        mfma_steps<MT>(a0, b0, acc);
-        load_steps<WAVES, MT>(pa, pb, a_ok, b_ok, s + 2 * kB * WAVES, nsteps, a0, b0);
-        mfma_steps<MT>(a1, b1, acc);
+    for (int c = 0; c < NC; ++c) {
+        const int n = n0 + 16 * c + r16;
+        b_ok[c] = n < N;
+        pb[c] = CB + (size_t)(b_ok[c] ? n : 0) * K + kg * 16;
     }
+
+    acc_t acc[NC][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][t][v][lane] = acc[t][v];
+        for (int t = 0; t < MT; ++t) acc[c][t] = acc_t{0, 0, 0, 0};
+    v4i a0[MT][kB], b0[NC][kB], a1[MT][kB], b1[NC][kB];
+    load_steps<WAVES, MT, NC, kB>(pa, pb, a_ok, b_ok, wave, nsteps, a0, b0);
+    for (int s = wave; s < nsteps; s += 2 * kB * WAVES) {
+        load_steps<WAVES, MT, NC, kB>(pa, pb, a_ok, b_ok, s + kB * WAVES, nsteps, a1, b1);
+        mfma_steps<MT, NC, kB>(a0, b0, acc);
+        load_steps<WAVES, MT, NC, kB>(pa, pb, a_ok, b_ok, s + 2 * kB * WAVES, nsteps, a0, b0);
+        mfma_steps<MT, NC, kB>(a1, b1, acc);
+    }
     // Many outlier columns: the 16-bit outlier product as v_mfma_f32_16x16x32
     // over blocks of 32 outlier ranks (block q to wave q % WAVES): A = XO rows
     // (lane: token 16t + r16, ranks 32q + 8kg .. +8, contiguous; XO is 0 past
     // n_out), B = the weight codes at those ranks' columns as 16-bit values
-    // (exact; ranks past n_out read the last outlier column, against XO's 0),
-    // the same for every group of token rows.  A loop over the columns per
-    // output would take one dependent load each.
+    // (exact; ranks past n_out read the last outlier column, against XO's 0).
+    // A loop over the columns per output would take one dependent load each.
     const int n_out = *n_out_ptr;
     const bool dense_out = n_out > kDenseOut;
+    v4f acc_o[NC][MT];
     if (dense_out) {
         const int n_pad = (n_out + 31) & ~31;
-        const int8_t* cbr = CB + (size_t)min(n0 + r16, N - 1) * K;
-        v4f acc_o[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc_o[t] = v4f{0, 0, 0, 0};
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc_o[c][t] = v4f{0, 0, 0, 0};
         for (int q = wave; q * 32 < n_out; q += WAVES) {
             const int j0 = q * 32 + kg * 8;
             const v4i i0 = *reinterpret_cast<const v4i*>(idx + j0);
             const v4i i1 = *reinterpret_cast<const v4i*>(idx + j0 + 4);
             const int last = idx[n_out - 1];
-            v8u16 b;
+            int col[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int col = j0 + e < n_out ? (e < 4 ? i0[e] : i1[e - 4]) : last;
-                b[e] = narrow16<BF16>(code_value<FP8>(cbr[col]));
-            }
+            for (int e = 0; e < 8; ++e) col[e] = j0 + e < n_out ? (e < 4 ? i0[e] : i1[e - 4]) : last;
+            v8u16 a[MT];
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const v8u16 a = *reinterpret_cast<const v8u16*>(XO + (size_t)min(16 * t + r16, M - 1) * n_pad +
-                                                                 kg * 8 + q * 32);
-                if constexpr (BF16)
-                    acc_o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
-                                                                       __builtin_bit_cast(v8bf, b), acc_o[t], 0, 0, 0);
-                else
-                    acc_o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a),
-                                                                      __builtin_bit_cast(v8h, b), acc_o[t], 0, 0, 0);
+            for (int t = 0; t < MT; ++t)
+                a[t] = *reinterpret_cast<const v8u16*>(XO + (size_t)min(16 * t + r16, M - 1) * n_pad + kg * 8 + q * 32);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int8_t* cbr = CB + (size_t)min(n0 + 16 * c + r16, N - 1) * K;
+                v8u16 b;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) b[e] = narrow16<BF16>(code_value<FP8>(cbr[col[e]]));
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    if constexpr (BF16)
+                        acc_o[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(v8bf, a[t]), __builtin_bit_cast(v8bf, b), acc_o[c][t], 0, 0, 0);
+                    else
+                        acc_o[c][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(v8h, a[t]), __builtin_bit_cast(v8h, b), acc_o[c][t], 0, 0, 0);
+                }
             }
         }
+    }
+
+    // one channel group at a time through LDS: element e is accumulator
+    // register v of lane l of token group t -> row 16t + 4*(l/16) + v, column
+    // n0 + 16c + l%16
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (c > 0) __syncthreads();  // the previous group's partial tiles are read out
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float f = acc_o[t][v];  // by value: bit_cast of a vector element reads element 0
-                red_o[wave][t][v][lane] = f;
-            }
-    }
-    __syncthreads();
-
-    // element e: accumulator register v of lane l of group t -> row
-    // 16t + 4*(l/16) + v, column l%16
-    for (int e = tid; e < MT * 256; e += WAVES * 64) {
-        const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
-        elem_t c = 0;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) c += red[w][t][v][l];
-        const int m = 16 * t + 4 * (l >> 4) + v;
-        const int n = n0 + (l & 15);
-        if (m >= M || n >= N) continue;
-        if constexpr (FP8) {
-            if (C_f32) C_f32[(size_t)m * N + n] = c;
-        } else {
-            if (C_i32) C_i32[(size_t)m * N + n] = c;
-        }
-
-        float y = (float)c * (SCA[m] / code_max<FP8>());
+            for (int v = 0; v < 4; ++v) red[wave][t][v][lane] = acc[c][t][v];
         if (dense_out) {
-            float o = 0.0f;  // the waves' partial sums, in a fixed order
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) o += red_o[w][t][v][l];
-            y += o;
-        } else if (n_out > 0) {
-            const int n_pad = (n_out + 31) & ~31;
-            const uint16_t* xo = XO + (size_t)m * n_pad;
-            const int8_t* cb = CB + (size_t)n * K;
-#pragma unroll 4
-            for (int j = 0; j < n_out; ++j) y += widen16<BF16>(xo[j]) * code_value<FP8>(cb[idx[j]]);
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float f = acc_o[c][t][v];  // by value: bit_cast of a vector element reads element 0
+                    red_o[wave][t][v][lane] = f;
+                }
         }
-        y *= SCB[n] / code_max<FP8>();
-        if (bias) y += widen16<BF16>(bias[n]);
-        Y[(size_t)m * N + n] = narrow16<BF16>(y);
+        __syncthreads();
+        for (int e = tid; e < MT * 256; e += WAVES * 64) {
+            const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
+            elem_t cs = 0;
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) cs += red[w][t][v][l];
+            const int m = 16 * t + 4 * (l >> 4) + v;
+            const int n = n0 + 16 * c + (l & 15);
+            if (m >= M || n >= N) continue;
+            if constexpr (FP8) {
+                if (C_f32) C_f32[(size_t)m * N + n] = cs;
+            } else {
+                if (C_i32) C_i32[(size_t)m * N + n] = cs;
+            }
+
+            float y = (float)cs * (SCA[m] / code_max<FP8>());
+            if (dense_out) {
+                float o = 0.0f;  // the waves' partial sums, in a fixed order
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) o += red_o[w][t][v][l];
+                y += o;
+            } else if (n_out > 0) {
+                const int n_pad = (n_out + 31) & ~31;
+                const uint16_t* xo = XO + (size_t)m * n_pad;
+                const int8_t* cb = CB + (size_t)n * K;
+#pragma unroll 4
+                for (int j = 0; j < n_out; ++j) y += widen16<BF16>(xo[j]) * code_value<FP8>(cb[idx[j]]);
+            }
+            y *= SCB[n] / code_max<FP8>();
+            if (bias) y += widen16<BF16>(bias[n]);
+            Y[(size_t)m * N + n] = narrow16<BF16>(y);
+        }
     }
 }
 
@@ -223,15 +251,25 @@ hipError_t launch_gemm_small_m(const MatmulArgs& a, hipStream_t stream, hipEvent
     typedef void (*kernel_t)(int, int, int, const int8_t*, const float*, const int32_t*, const int32_t*,
                              const uint16_t*, const int8_t*, const float*, const uint16_t*, uint16_t*, int32_t*,
                              float*);
-    // [groups of 16 token rows: 1, 2, 4][bf16?][fp8?]
-    static const kernel_t kernels[3][2][2] = {
-        {{gemm_small_m_kernel<false, false, W, 1>, gemm_small_m_kernel<false, true, W, 1>},
-         {gemm_small_m_kernel<true, false, W, 1>, gemm_small_m_kernel<true, true, W, 1>}},
-        {{gemm_small_m_kernel<false, false, W, 2>, gemm_small_m_kernel<false, true, W, 2>},
-         {gemm_small_m_kernel<true, false, W, 2>, gemm_small_m_kernel<true, true, W, 2>}},
-        {{gemm_small_m_kernel<false, false, W, 4>, gemm_small_m_kernel<false, true, W, 4>},
-         {gemm_small_m_kernel<true, false, W, 4>, gemm_small_m_kernel<true, true, W, 4>}}};
-    const kernel_t fn = kernels[a.M <= 16 ? 0 : a.M <= 32 ? 1 : 2][a.bf16][a.fp8];
+    // [token groups of 16: 1, 2, 4, and 2, 4 with four channel groups][bf16?][fp8?]
+    static const kernel_t kernels[5][2][2] = {
+        {{gemm_small_m_kernel<false, false, W, 1, 1>, gemm_small_m_kernel<false, true, W, 1, 1>},
+         {gemm_small_m_kernel<true, false, W, 1, 1>, gemm_small_m_kernel<true, true, W, 1, 1>}},
+        {{gemm_small_m_kernel<false, false, W, 2, 1>, gemm_small_m_kernel<false, true, W, 2, 1>},
+         {gemm_small_m_kernel<true, false, W, 2, 1>, gemm_small_m_kernel<true, true, W, 2, 1>}},
+        {{gemm_small_m_kernel<false, false, W, 4, 1>, gemm_small_m_kernel<false, true, W, 4, 1>},
+         {gemm_small_m_kernel<true, false, W, 4, 1>, gemm_small_m_kernel<true, true, W, 4, 1>}},
+        {{gemm_small_m_kernel<false, false, W, 2, 4>, gemm_small_m_kernel<false, true, W, 2, 4>},
+         {gemm_small_m_kernel<true, false, W, 2, 4>, gemm_small_m_kernel<true, true, W, 2, 4>}},
+        {{gemm_small_m_kernel<false, false, W, 4, 4>, gemm_small_m_kernel<false, true, W, 4, 4>},
+         {gemm_small_m_kernel<true, false, W, 4, 4>, gemm_small_m_kernel<true, true, W, 4, 4>}}};
+    // more than one group of token rows with at least a round of 64-channel
+    // workgroups: four channel groups per workgroup, each reading CA once for
+    // 64 weight rows
+    const int mt = a.M <= 16 ? 0 : a.M <= 32 ? 1 : 2;
+    const bool wide = small_m_wide(a.M, a.N);
+    const kernel_t fn = kernels[wide ? mt + 2 : mt][a.bf16][a.fp8];
+    if (wide) grid = dim3((a.N + 63) / 64);
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(fn, grid, block, 0, stream, ev_start, ev_stop, 0, a.M, a.N, a.K, a.CA,
                               a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32,

@@ -139,6 +139,8 @@ RAGGED = [
     (65, 40, 64, F16, 1, False),       # tiled, one stage
     (80, 64, 128, BF16, 2, True),      # tiled, two stages
     (40, 64, 128, BF16, 2, True),      # the streaming kernel, four groups of 16 rows
+    (40, 16400, 128, F16, 36, True),   # ... in workgroups of 64 channels, many outlier columns
+    (24, 16448, 192, BF16, 3, False),  # ... two groups of 16 rows, 64 channels
     (65, 300, 192, F16, 2, True),      # tiled, three stages
     (300, 520, 320, F16, 3, True),
     (300, 520, 320, BF16, 3, True),

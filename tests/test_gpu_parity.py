@@ -67,6 +67,11 @@ RAGGED = [
     (30, 130, 512, F16, 36, False),
     (48, 200, 1024, BF16, 40, True),
     (64, 96, 2048, F16, 3, True),
+    # workgroups of 64 channels (N >= 16384), two and four groups of 16 token
+    # rows, a ragged last workgroup, with and without many outlier columns
+    (40, 16400, 128, F16, 36, True),
+    (20, 16448, 192, BF16, 3, False),
+    (64, 16384, 256, F16, 0, True),
     (300, 520, 320, F16, 3, True),
     (300, 520, 320, BF16, 3, True),
     (513, 257, 1024, F16, 5, False),
