@@ -445,6 +445,17 @@ def test_bloom_ffn_full_size(orc, name):
     sampled_check(orc, wl, 48)
 
 
+# batched decode at real layer sizes through the weight-streaming product:
+# workgroups of 64 channels in one round (64 x 16384 x 16384) and in 1.75
+# rounds (24 x 28672 x 8192), workgroups of 16 channels in one round
+# (32 x 8192 x 28672); every row
+@pytest.mark.parametrize("M,N,K,dt,nout", [(64, 16384, 16384, F16, 6), (24, 28672, 8192, F16, 40),
+                                           (32, 8192, 28672, BF16, 3)])
+def test_batched_decode_streaming_full_size(orc, M, N, K, dt, nout):
+    wl = synth.make_random(M, N, K, dt, seed=M + 7, n_outlier_cols=nout, bias_sigma=0.01)
+    sampled_check(orc, wl, M)
+
+
 # ---- the one-call forward (llmint8_linear): fused small-M kernel and the
 # ---- quantize_act + matmul sequence, every stage against the oracle ----------
 from gpu_helpers import run_gpu_linear  # noqa: E402
