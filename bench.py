@@ -60,15 +60,18 @@ KERNEL_NAMES = {"decode": "linear_decode_kernel", "fused": "linear_small_m_kerne
 def small_m_product(M, N, K):
     """Whether the product takes the weight-streaming kernel (the library's
     rule): up to 16 token rows always; up to 64 when M * N * K is at most 6e9
-    or the streaming grid is one round of the chip (at most 256 workgroups of
-    64 channels when M > 16 and N >= 16384, else, up to 32 rows, at most 512
-    of 16)."""
+    or the streaming grid is one round of the chip: up to 32 rows at most 512
+    workgroups (of 64 channels when N >= 16384, else of 16), above that at
+    most 256 workgroups of 64 channels."""
     if M <= 16:
         return True
     if M > 64 or N is None:
         return False
     wide = N >= 64 * 256
-    one_round = -(-N // 64) <= 256 if wide else M <= 32 and -(-N // 16) <= 512
+    if M <= 32:
+        one_round = -(-N // (64 if wide else 16)) <= 512
+    else:
+        one_round = wide and -(-N // 64) <= 256
     return M * N * K <= 6_000_000_000 or one_round
 
 

@@ -120,9 +120,10 @@ llmint8_status llmint8_quantize_act(const void* X, int dtype, int64_t M, int64_t
 
 /* Bytes of optional device workspace llmint8_matmul can use for M x N x K
  * (0 for the weight-streaming product and for invalid sizes: M <= 16, or
- * M <= 64 with M * N * K <= 6e9 or with a streaming grid of one round,
- * that is ceil(N/64) <= 256 when M > 16 and N >= 16384, else M <= 32
- * with ceil(N/16) <= 512).  Otherwise the product works on
+ * M <= 64 with M * N * K <= 6e9 or with a streaming grid of one round:
+ * for M <= 32 at most 512 workgroups, ceil(N/64) when N >= 16384, else
+ * ceil(N/16); for M > 32, N >= 16384 and ceil(N/64) <= 256).  Otherwise
+ * the product works on
  * tiles of 256 rows by W columns, W = 256 or 224: for each W, T(W) =
  * ceil(M/256) * ceil(N/W) tiles, S(W) workgroups per tile (below), and the
  * W with the fewer MFMA cycles per CU, ceil(T*S/256) * W * ceil(ceil(K/128)/S),

@@ -552,16 +552,20 @@ hipError_t launch_linear_decode(const void* X, bool bf16, bool fp8, int M, int N
 
 // Kernel families used by launch_matmul.
 constexpr int kSmallM = 16;  // M <= kSmallM takes the streaming kernel
-// More than 16 rows with at least 256 x 64 output channels: workgroups of 64
+// More than 8 rows with at least 256 x 64 output channels: workgroups of 64
 // channels (four groups of 16), each reading the M x K activations once for
-// 64 weight rows instead of 16.
-inline bool small_m_wide(int64_t M, int64_t N) { return M > kSmallM && N >= 64 * 256; }
-// Whether the streaming kernel's grid is one round of the chip: at most 256
-// workgroups of 64 channels (one per CU), or, up to 32 rows, 512 of 16 (two
-// per CU; with four groups of 16 rows these lost to the tiled product,
-// 64 x 8192 x 28672 150 against 140 us).
+// 64 weight rows instead of 16. Up to 8 rows those re-reads are small and
+// the finer grid of 16-channel workgroups balances better (4 x 28672 x 16384:
+// 135 us in workgroups of 64 channels, 123 in workgroups of 16).
+inline bool small_m_wide(int64_t M, int64_t N) { return M > 8 && N >= 64 * 256; }
+// Whether the streaming kernel's grid is one round of the chip: up to 32
+// rows, 512 workgroups of 64 or of 16 channels (two per CU); above, 256 of
+// 64 (one per CU). Workgroups of 16 channels with four groups of 16 rows lost
+// to the tiled product even in one round (64 x 8192 x 28672 150 against
+// 140 us).
 inline bool small_m_one_round(int64_t M, int64_t N) {
-    return small_m_wide(M, N) ? (N + 63) / 64 <= 256 : M <= 32 && (N + 15) / 16 <= 512;
+    if (M <= 32) return (N + (small_m_wide(M, N) ? 63 : 15)) / (small_m_wide(M, N) ? 64 : 16) <= 512;
+    return small_m_wide(M, N) && (N + 63) / 64 <= 256;
 }
 // Up to 64 rows the streaming kernel (1, 2 or 4 groups of 16 rows) also takes
 // shapes whose M * N * K is at most kSmallMWork, and any whose grid is one

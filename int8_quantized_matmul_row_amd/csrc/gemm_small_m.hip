@@ -34,7 +34,13 @@ namespace llmint8 {
 
 namespace {
 
-constexpr int kBatch = 8;       // K steps in flight per wave for one group of 16 token rows
+// K steps in flight per wave, by token groups MT and channel groups NC: the
+// deepest batch that keeps the kernel within 128 VGPRs (two workgroups per
+// CU, which measured faster than deeper batches in one), four groups of 16
+// rows and 64 channels aside (238 VGPRs at any depth)
+constexpr int steps_in_flight(int MT, int NC) {
+    return NC == 1 ? (MT == 4 ? 2 : 4) : MT == 2 ? 1 : 2;
+}
 constexpr int kDenseOut = 32;  // more outlier columns than this: the outlier product as MFMAs
 
 // steps s0 + i*WAVES (i < KB) of the weight rows of every channel group and
@@ -104,9 +110,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     float* __restrict__ C_f32) {
     typedef typename SmallAcc<FP8>::vec acc_t;
     typedef typename SmallAcc<FP8>::elem elem_t;
-    // K steps in flight per wave: fewer for more token groups, and two with
-    // four channel groups, so that the registers in flight stay about the same
-    constexpr int kB = NC == 1 ? kBatch / MT : 2;
+    constexpr int kB = steps_in_flight(MT, NC);
     __shared__ elem_t red[WAVES][MT][4][64];
     __shared__ float red_o[WAVES][MT][4][64];  // the 16-bit outlier product's partial tiles (many columns)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -251,24 +255,26 @@ hipError_t launch_gemm_small_m(const MatmulArgs& a, hipStream_t stream, hipEvent
     typedef void (*kernel_t)(int, int, int, const int8_t*, const float*, const int32_t*, const int32_t*,
                              const uint16_t*, const int8_t*, const float*, const uint16_t*, uint16_t*, int32_t*,
                              float*);
-    // [token groups of 16: 1, 2, 4, and 2, 4 with four channel groups][bf16?][fp8?]
-    static const kernel_t kernels[5][2][2] = {
-        {{gemm_small_m_kernel<false, false, W, 1, 1>, gemm_small_m_kernel<false, true, W, 1, 1>},
-         {gemm_small_m_kernel<true, false, W, 1, 1>, gemm_small_m_kernel<true, true, W, 1, 1>}},
-        {{gemm_small_m_kernel<false, false, W, 2, 1>, gemm_small_m_kernel<false, true, W, 2, 1>},
-         {gemm_small_m_kernel<true, false, W, 2, 1>, gemm_small_m_kernel<true, true, W, 2, 1>}},
-        {{gemm_small_m_kernel<false, false, W, 4, 1>, gemm_small_m_kernel<false, true, W, 4, 1>},
-         {gemm_small_m_kernel<true, false, W, 4, 1>, gemm_small_m_kernel<true, true, W, 4, 1>}},
-        {{gemm_small_m_kernel<false, false, W, 2, 4>, gemm_small_m_kernel<false, true, W, 2, 4>},
-         {gemm_small_m_kernel<true, false, W, 2, 4>, gemm_small_m_kernel<true, true, W, 2, 4>}},
-        {{gemm_small_m_kernel<false, false, W, 4, 4>, gemm_small_m_kernel<false, true, W, 4, 4>},
-         {gemm_small_m_kernel<true, false, W, 4, 4>, gemm_small_m_kernel<true, true, W, 4, 4>}}};
-    // more than one group of token rows with at least a round of 64-channel
-    // workgroups: four channel groups per workgroup, each reading CA once for
-    // 64 weight rows
+    // [channel groups: 1, 4][token groups of 16: 1, 2, 4][bf16?][fp8?]
+    static const kernel_t kernels[2][3][2][2] = {
+        {{{gemm_small_m_kernel<false, false, W, 1, 1>, gemm_small_m_kernel<false, true, W, 1, 1>},
+          {gemm_small_m_kernel<true, false, W, 1, 1>, gemm_small_m_kernel<true, true, W, 1, 1>}},
+         {{gemm_small_m_kernel<false, false, W, 2, 1>, gemm_small_m_kernel<false, true, W, 2, 1>},
+          {gemm_small_m_kernel<true, false, W, 2, 1>, gemm_small_m_kernel<true, true, W, 2, 1>}},
+         {{gemm_small_m_kernel<false, false, W, 4, 1>, gemm_small_m_kernel<false, true, W, 4, 1>},
+          {gemm_small_m_kernel<true, false, W, 4, 1>, gemm_small_m_kernel<true, true, W, 4, 1>}}},
+        {{{gemm_small_m_kernel<false, false, W, 1, 4>, gemm_small_m_kernel<false, true, W, 1, 4>},
+          {gemm_small_m_kernel<true, false, W, 1, 4>, gemm_small_m_kernel<true, true, W, 1, 4>}},
+         {{gemm_small_m_kernel<false, false, W, 2, 4>, gemm_small_m_kernel<false, true, W, 2, 4>},
+          {gemm_small_m_kernel<true, false, W, 2, 4>, gemm_small_m_kernel<true, true, W, 2, 4>}},
+         {{gemm_small_m_kernel<false, false, W, 4, 4>, gemm_small_m_kernel<false, true, W, 4, 4>},
+          {gemm_small_m_kernel<true, false, W, 4, 4>, gemm_small_m_kernel<true, true, W, 4, 4>}}}};
+    // more than 8 rows and at least a round of 64-channel workgroups: four
+    // channel groups per workgroup, each wave reading its CA rows once for 64
+    // weight rows
     const int mt = a.M <= 16 ? 0 : a.M <= 32 ? 1 : 2;
     const bool wide = small_m_wide(a.M, a.N);
-    const kernel_t fn = kernels[wide ? mt + 2 : mt][a.bf16][a.fp8];
+    const kernel_t fn = kernels[wide][mt][a.bf16][a.fp8];
     if (wide) grid = dim3((a.N + 63) / 64);
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(fn, grid, block, 0, stream, ev_start, ev_stop, 0, a.M, a.N, a.K, a.CA,

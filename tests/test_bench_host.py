@@ -18,7 +18,9 @@ def test_kernel_family():
     # up to 64 rows, the weight-streaming kernel while M * N * K <= 6e9 or
     # its grid is one round of the chip
     assert bench.kernel_family(17, 8192, N=28672) == "small_m"
-    assert bench.kernel_family(32, 8192, N=28672) == "tiled"
+    assert bench.kernel_family(32, 8192, N=28672) == "small_m"
+    assert bench.kernel_family(32, 8192, N=57344) == "tiled"
+    assert bench.kernel_family(48, 8192, N=28672) == "tiled"
     assert bench.kernel_family(64, 4096, N=16384) == "small_m"
     assert bench.kernel_family(64, 16384, N=16384) == "small_m"
     assert bench.kernel_family(32, 28672, N=8192) == "small_m"

@@ -141,6 +141,7 @@ RAGGED = [
     (40, 64, 128, BF16, 2, True),      # the streaming kernel, four groups of 16 rows
     (40, 16400, 128, F16, 36, True),   # ... in workgroups of 64 channels, many outlier columns
     (24, 16448, 192, BF16, 3, False),  # ... two groups of 16 rows, 64 channels
+    (16, 16400, 128, F16, 2, True),    # ... one group of 16 rows, 64 channels
     (65, 300, 192, F16, 2, True),      # tiled, three stages
     (300, 520, 320, F16, 3, True),
     (300, 520, 320, BF16, 3, True),

@@ -72,6 +72,9 @@ RAGGED = [
     (40, 16400, 128, F16, 36, True),
     (20, 16448, 192, BF16, 3, False),
     (64, 16384, 256, F16, 0, True),
+    (12, 16400, 256, F16, 36, True),    # one group of 16 rows, 64 channels
+    (9, 16448, 128, BF16, 2, False),
+    (5, 16448, 128, BF16, 2, False),    # up to 8 rows: 16 channels
     (300, 520, 320, F16, 3, True),
     (300, 520, 320, BF16, 3, True),
     (513, 257, 1024, F16, 5, False),
@@ -446,11 +449,11 @@ def test_bloom_ffn_full_size(orc, name):
 
 
 # batched decode at real layer sizes through the weight-streaming product:
-# workgroups of 64 channels in one round (64 x 16384 x 16384) and in 1.75
-# rounds (24 x 28672 x 8192), workgroups of 16 channels in one round
-# (32 x 8192 x 28672); every row
+# workgroups of 64 channels with four, two and one groups of 16 rows
+# (64 x 16384 x 16384, 24 x 28672 x 8192, 16 x 28672 x 8192), workgroups of
+# 16 channels (32 x 8192 x 28672); every row
 @pytest.mark.parametrize("M,N,K,dt,nout", [(64, 16384, 16384, F16, 6), (24, 28672, 8192, F16, 40),
-                                           (32, 8192, 28672, BF16, 3)])
+                                           (32, 8192, 28672, BF16, 3), (16, 28672, 8192, BF16, 4)])
 def test_batched_decode_streaming_full_size(orc, M, N, K, dt, nout):
     wl = synth.make_random(M, N, K, dt, seed=M + 7, n_outlier_cols=nout, bias_sigma=0.01)
     sampled_check(orc, wl, M)
