@@ -34,13 +34,6 @@ namespace llmint8 {
 
 namespace {
 
-// K steps in flight per wave, by token groups MT and channel groups NC: the
-// deepest batch that keeps the kernel within 128 VGPRs (two workgroups per
-// CU, which measured faster than deeper batches in one), four groups of 16
-// rows and 64 channels aside (238 VGPRs at any depth)
-constexpr int steps_in_flight(int MT, int NC) {
-    return NC == 1 ? (MT == 4 ? 2 : 4) : MT == 2 ? 1 : 2;
-}
 constexpr int kDenseOut = 32;  // more outlier columns than this: the outlier product as MFMAs
 
 // steps s0 + i*WAVES (i < KB) of the weight rows of every channel group and
@@ -101,7 +94,7 @@ struct SmallAcc<true> {
     typedef float elem;
 };
 
-template <bool BF16, bool FP8, int WAVES, int MT, int NC>
+template <bool BF16, bool FP8, int WAVES, int MT, int NC, int KB>
 __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     int M, int N, int K, const int8_t* __restrict__ CA, const float* __restrict__ SCA,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_out_ptr,
@@ -110,7 +103,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     float* __restrict__ C_f32) {
     typedef typename SmallAcc<FP8>::vec acc_t;
     typedef typename SmallAcc<FP8>::elem elem_t;
-    constexpr int kB = steps_in_flight(MT, NC);
+    constexpr int kB = KB;  // K steps in flight per wave
     __shared__ elem_t red[WAVES][MT][4][64];
     __shared__ float red_o[WAVES][MT][4][64];  // the 16-bit outlier product's partial tiles (many columns)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -246,36 +239,47 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_small_m_kernel(
     }
 }
 
+constexpr int kWaves = 8;
+typedef void (*small_m_kernel_t)(int, int, int, const int8_t*, const float*, const int32_t*, const int32_t*,
+                                 const uint16_t*, const int8_t*, const float*, const uint16_t*, uint16_t*,
+                                 int32_t*, float*);
+
+template <int MT, int NC, int KB>
+small_m_kernel_t small_m_variant(bool bf16, bool fp8) {
+    if (bf16)
+        return fp8 ? gemm_small_m_kernel<true, true, kWaves, MT, NC, KB>
+                   : gemm_small_m_kernel<true, false, kWaves, MT, NC, KB>;
+    return fp8 ? gemm_small_m_kernel<false, true, kWaves, MT, NC, KB>
+               : gemm_small_m_kernel<false, false, kWaves, MT, NC, KB>;
+}
+
 }  // namespace
 
 hipError_t launch_gemm_small_m(const MatmulArgs& a, hipStream_t stream, hipEvent_t ev_start,
                                hipEvent_t ev_stop) {
-    constexpr int W = 8;
+    constexpr int W = kWaves;
     dim3 grid((a.N + 15) / 16), block(W * 64);
-    typedef void (*kernel_t)(int, int, int, const int8_t*, const float*, const int32_t*, const int32_t*,
-                             const uint16_t*, const int8_t*, const float*, const uint16_t*, uint16_t*, int32_t*,
-                             float*);
-    // [channel groups: 1, 4][token groups of 16: 1, 2, 4][bf16?][fp8?]
-    static const kernel_t kernels[2][3][2][2] = {
-        {{{gemm_small_m_kernel<false, false, W, 1, 1>, gemm_small_m_kernel<false, true, W, 1, 1>},
-          {gemm_small_m_kernel<true, false, W, 1, 1>, gemm_small_m_kernel<true, true, W, 1, 1>}},
-         {{gemm_small_m_kernel<false, false, W, 2, 1>, gemm_small_m_kernel<false, true, W, 2, 1>},
-          {gemm_small_m_kernel<true, false, W, 2, 1>, gemm_small_m_kernel<true, true, W, 2, 1>}},
-         {{gemm_small_m_kernel<false, false, W, 4, 1>, gemm_small_m_kernel<false, true, W, 4, 1>},
-          {gemm_small_m_kernel<true, false, W, 4, 1>, gemm_small_m_kernel<true, true, W, 4, 1>}}},
-        {{{gemm_small_m_kernel<false, false, W, 1, 4>, gemm_small_m_kernel<false, true, W, 1, 4>},
-          {gemm_small_m_kernel<true, false, W, 1, 4>, gemm_small_m_kernel<true, true, W, 1, 4>}},
-         {{gemm_small_m_kernel<false, false, W, 2, 4>, gemm_small_m_kernel<false, true, W, 2, 4>},
-          {gemm_small_m_kernel<true, false, W, 2, 4>, gemm_small_m_kernel<true, true, W, 2, 4>}},
-         {{gemm_small_m_kernel<false, false, W, 4, 4>, gemm_small_m_kernel<false, true, W, 4, 4>},
-          {gemm_small_m_kernel<true, false, W, 4, 4>, gemm_small_m_kernel<true, true, W, 4, 4>}}}};
-    // more than 8 rows and at least a round of 64-channel workgroups: four
-    // channel groups per workgroup, each wave reading its CA rows once for 64
-    // weight rows
-    const int mt = a.M <= 16 ? 0 : a.M <= 32 ? 1 : 2;
+    // Token groups of 16 (1, 2, 4) by M; more than 8 rows and at least a
+    // round of 64-channel workgroups: four channel groups per workgroup, each
+    // wave reading its CA rows once for 64 weight rows. K steps in flight per
+    // wave: the deepest batch within 128 VGPRs (two workgroups per CU, which
+    // measured faster than deeper batches in one), except four groups of 16
+    // rows in 64 channels (238 VGPRs at any depth) and up to 8 rows, which
+    // stream faster with 8 steps in flight in one workgroup per CU (151
+    // VGPRs; 2 x 28672 x 16384: 113 against 120 us).
     const bool wide = small_m_wide(a.M, a.N);
-    const kernel_t fn = kernels[wide][mt][a.bf16][a.fp8];
-    if (wide) grid = dim3((a.N + 63) / 64);
+    small_m_kernel_t fn;
+    if (wide) {
+        fn = a.M <= 16   ? small_m_variant<1, 4, 2>(a.bf16, a.fp8)
+             : a.M <= 32 ? small_m_variant<2, 4, 1>(a.bf16, a.fp8)
+                         : small_m_variant<4, 4, 2>(a.bf16, a.fp8);
+        grid = dim3((a.N + 63) / 64);
+    } else {
+        fn = a.M <= 8    ? small_m_variant<1, 1, 8>(a.bf16, a.fp8)
+             : a.M <= 16 ? small_m_variant<1, 1, 4>(a.bf16, a.fp8)
+             : a.M <= 32 ? small_m_variant<2, 1, 4>(a.bf16, a.fp8)
+                         : small_m_variant<4, 1, 2>(a.bf16, a.fp8);
+    }
     if (ev_start || ev_stop) {
         hipExtLaunchKernelGGL(fn, grid, block, 0, stream, ev_start, ev_stop, 0, a.M, a.N, a.K, a.CA,
                               a.SCA, a.idx, a.n_out, a.XO, a.CB, a.SCB, a.bias, a.Y, a.C_i32,
