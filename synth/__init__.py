@@ -135,6 +135,9 @@ _SPECS = {
     "sweep_0.1": (F16, 4096, 28672, 8192, 8, 8.0, 60.0, 0.02, None, 0, 1),
     "sweep_1": (F16, 4096, 28672, 8192, 82, 8.0, 60.0, 0.02, None, 0, 1),
     "sweep_5": (F16, 4096, 28672, 8192, 410, 8.0, 60.0, 0.02, None, 0, 1),
+    # batched decode: 32 tokens through the sweep's layer (the weight-streaming
+    # product)
+    "batch_32": (F16, 32, 28672, 8192, 4, 8.0, 60.0, 0.02, None, 0, 1),
 }
 
 WORKLOADS = tuple(_SPECS)

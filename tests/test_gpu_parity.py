@@ -44,8 +44,8 @@ def full_check(orc, wl, threshold=None, label=None):
     return g, ref
 
 
-# ---- the two small named workloads, every row ------------------------------
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+# ---- the small named workloads, every row ----------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode", "batch_32"])
 def test_named_workload_full(orc, name):
     wl = synth.make_workload(name)
     g, ref = full_check(orc, wl)
